@@ -1,0 +1,184 @@
+"""Python binding of the glass_amd C ABI (include/glass_amd.h).
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream, ctypes passes raw pointers, and every step runs in the HIP kernels of
+``libglass_amd.so``.  There is no CPU or PyTorch fallback -- if the library is
+missing, every call raises.
+
+Because the C ABI takes raw pointers, this layer checks each tensor's device,
+dtype, contiguity and element count against the sizes implied by
+``state_size`` / ``knot_points`` before anything is launched.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "GlassError", "load", "library_path", "bdmv_batched", "pcg_batched",
+    "pcg_grid", "pcg_grid_workspace_bytes", "CONVERGED", "MAX_ITERS",
+    "BREAKDOWN", "GRID_TIMEOUT",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libglass_amd.so")
+_lib = None
+_lock = threading.Lock()
+
+GLASS_F32, GLASS_F64 = 0, 1
+CONVERGED, MAX_ITERS, BREAKDOWN, GRID_TIMEOUT = 0, 1, 2, 3
+
+
+class GlassError(RuntimeError):
+    def __init__(self, code: int, where: str, detail: str):
+        super().__init__("%s failed with %d: %s" % (where, code, detail))
+        self.code = code
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load ``libglass_amd.so`` (built by ``build.py``); raises if absent."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                "libglass_amd.so is not built (run __graft_entry__.build() or "
+                "python block_tridiagonal_pcg_bdmv_amd/build.py)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P, I, D, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+        sigs = {
+            "glass_bdmv_batched": ([P, P, P, I, I, I, I, P], I),
+            "glass_pcg_batched": ([P, P, P, P, I, I, I, I, D, D, P, I, P], I),
+            "glass_pcg_batched_ex": ([P, P, P, P, I, I, I, I, D, D, P, P, P, I, P], I),
+            "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
+            "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
+            "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, P], I),
+            "glass_status_string": ([I], ctypes.c_char_p),
+            "glass_last_error": ([], ctypes.c_char_p),
+            "glass_version": ([], I),
+        }
+        for name, (args, res) in sigs.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = lib
+        return lib
+
+
+def _check(rc: int, where: str):
+    if rc != 0:
+        lib = load()
+        raise GlassError(rc, where, "%s (%s)" % (
+            lib.glass_status_string(rc).decode(), lib.glass_last_error().decode()))
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return GLASS_F32
+    if t.dtype == torch.float64:
+        return GLASS_F64
+    raise TypeError("tensors must be float32 or float64, got %s" % t.dtype)
+
+
+def _dev(t, name, numel, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
+    if t.numel() != numel:
+        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _problems(S, ss, kp):
+    per = kp * ss * 3 * ss
+    if ss < 1 or kp < 1 or S.numel() % per != 0:
+        raise ValueError("S size is not a multiple of knot_points*state_size*3*state_size")
+    return S.numel() // per
+
+
+def bdmv_batched(y, S, v, state_size: int, knot_points: int, stream=None):
+    """y = A_bd v for every problem (page "Block-tridiagonal Solves", section
+    "Matvec -- glass::bdmv").  y, v: padded [B, (kp+2)*ss]; only the interior
+    of y is written."""
+    ss, kp = int(state_size), int(knot_points)
+    B = _problems(S, ss, kp)
+    dt = S.dtype
+    vec = (kp + 2) * ss * B
+    args = (_dev(y, "y", vec, dt), _dev(S, "S", S.numel(), dt), _dev(v, "v", vec, dt))
+    rc = load().glass_bdmv_batched(*args, ss, kp, B, _dtype_code(S), _stream(stream))
+    _check(rc, "glass_bdmv_batched")
+
+
+def pcg_batched(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
+                rel_tol: float, abs_tol: float, iters_out, status_out=None,
+                rho_out=None, stream=None):
+    """Batched PCG (page "Block-tridiagonal Solves", section "Solve --
+    glass::pcg").  x: [B, kp*ss] initial guess in, solution out; iters_out
+    (and status_out) int32 [B]; rho_out dtype [B, 2]."""
+    import torch
+    ss, kp = int(state_size), int(knot_points)
+    B = _problems(S, ss, kp)
+    dt = S.dtype
+    n = kp * ss
+    a = (_dev(x, "x", B * n, dt), _dev(S, "S", S.numel(), dt),
+         _dev(Pinv, "Pinv", S.numel(), dt), _dev(b, "b", B * n, dt))
+    it = _dev(iters_out, "iters_out", B, torch.int32)
+    st = _dev(status_out, "status_out", B, torch.int32) if status_out is not None else None
+    rh = _dev(rho_out, "rho_out", 2 * B, dt) if rho_out is not None else None
+    rc = load().glass_pcg_batched_ex(*a, ss, kp, B, int(max_iters), float(rel_tol),
+                                     float(abs_tol), it, st, rh, _dtype_code(S),
+                                     _stream(stream))
+    _check(rc, "glass_pcg_batched_ex")
+
+
+def pcg_grid_workspace_bytes(state_size: int, knot_points: int, dtype) -> int:
+    import torch
+    code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
+    return int(load().glass_pcg_grid_workspace_bytes(int(state_size), int(knot_points), code))
+
+
+def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
+             rel_tol: float, abs_tol: float, iters_out, workspace,
+             status_out=None, rho_out=None, stream=None):
+    """One PCG solve over a cooperative grid.  Same arguments as
+    ``pcg_batched`` with one problem, plus a device ``workspace`` tensor of at
+    least ``pcg_grid_workspace_bytes`` bytes (any dtype, 256-byte aligned)."""
+    import torch
+    ss, kp = int(state_size), int(knot_points)
+    if _problems(S, ss, kp) != 1:
+        raise ValueError("pcg_grid solves exactly one problem")
+    dt = S.dtype
+    n = kp * ss
+    a = (_dev(x, "x", n, dt), _dev(S, "S", S.numel(), dt),
+         _dev(Pinv, "Pinv", S.numel(), dt), _dev(b, "b", n, dt))
+    it = _dev(iters_out, "iters_out", 1, torch.int32)
+    st = _dev(status_out, "status_out", 1, torch.int32) if status_out is not None else None
+    rh = _dev(rho_out, "rho_out", 2, dt) if rho_out is not None else None
+    if not (workspace.is_cuda and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous device tensor")
+    wbytes = workspace.numel() * workspace.element_size()
+    rc = load().glass_pcg_grid_ex(*a, ss, kp, int(max_iters), float(rel_tol),
+                                  float(abs_tol), it, st, rh,
+                                  ctypes.c_void_p(workspace.data_ptr()), wbytes,
+                                  _dtype_code(S), _stream(stream))
+    _check(rc, "glass_pcg_grid_ex")

@@ -1,0 +1,156 @@
+// Device building blocks shared by the bdmv and PCG kernels (gfx950, wave64).
+//
+// * wave_sum: a 64-lane all-reduce built from DPP lane moves (quad_perm,
+//   row_half_mirror, row_mirror), one ds_swizzle (xor 16 inside 32 lanes) and
+//   two readlanes.  Each step adds a value to its mirror image, and IEEE
+//   addition is commutative, so every lane ends with the same bits and the
+//   summation tree is fixed: results are run-to-run deterministic.
+// * block_sum: wave_sum, one LDS slot per wave, one barrier, then every thread
+//   adds the slots in wave order -- again the same bits in every thread, so
+//   scalars such as alpha, beta and the convergence test need no broadcast.
+// * copy_to_lds: coalesced HBM -> LDS staging of a contiguous range with
+//   16-byte loads when the caller vouches for alignment.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace glass {
+
+constexpr int kWave = 64;
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// DPP control words (GCN/CDNA encoding).
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kRowMirror = 0x140;      // lane i <- lane 15-i within 16
+constexpr int kSwizzleXor16 = 0x401F;  // ds_swizzle bitmask: and 0x1f, xor 0x10
+
+template <int CTRL>
+__device__ __forceinline__ float lane_move(float v) {
+  return __int_as_float(dpp_move<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double lane_move(double v) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = dpp_move<CTRL>((int)(bits & 0xffffffffLL));
+  const int hi = dpp_move<CTRL>((int)(bits >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ float swizzle_xor16(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), kSwizzleXor16));
+}
+__device__ __forceinline__ double swizzle_xor16(double v) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_ds_swizzle((int)(bits & 0xffffffffLL), kSwizzleXor16);
+  const int hi = __builtin_amdgcn_ds_swizzle((int)(bits >> 32), kSwizzleXor16);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ double read_lane(double v, int lane) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(bits & 0xffffffffLL), lane);
+  const int hi = __builtin_amdgcn_readlane((int)(bits >> 32), lane);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// Sum over the 64 lanes of a wave; all 64 lanes must be active.  Returns the
+// same value (same bits) in every lane.
+template <typename T>
+__device__ __forceinline__ T wave_sum(T v) {
+  v = v + lane_move<kQuadXor1>(v);
+  v = v + lane_move<kQuadXor2>(v);
+  v = v + lane_move<kRowHalfMirror>(v);
+  v = v + lane_move<kRowMirror>(v);
+  v = v + swizzle_xor16(v);
+  return read_lane(v, 0) + read_lane(v, 32);
+}
+
+// Workgroup-wide sum; every thread of the block must call it.  `slots` is an
+// LDS array of one entry per wave that no other live block_sum is using (the
+// callers alternate two arrays; a barrier separates reads of one use from
+// writes of the next).  Contains exactly one __syncthreads().
+template <typename T>
+__device__ __forceinline__ T block_sum(T v, T* slots, int n_waves) {
+  v = wave_sum(v);
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) slots[wave] = v;
+  __syncthreads();
+  T s = slots[0];
+  for (int w = 1; w < n_waves; ++w) s = s + slots[w];
+  return s;
+}
+
+// Orders LDS accesses of one wave around a hand-off between its own lanes
+// (DS operations of one wave execute in order; this only stops the compiler
+// from moving accesses across the point).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Copy `count` contiguous elements global -> LDS using `nthreads` threads
+// (thread index `tid`).  With `vec`, src and dst must be 16-byte aligned; the
+// bulk moves as 16-byte vectors, issued in groups so several loads are in
+// flight per thread, and the tail moves element-wise.  STREAM marks data read
+// once (non-temporal loads); data re-read later is loaded normally so it can
+// stay in L2 / Infinity Cache.
+typedef float vec16_t __attribute__((ext_vector_type(4)));  // 16-byte bit copy
+
+template <bool STREAM>
+__device__ __forceinline__ vec16_t load16(const vec16_t* p) {
+  if constexpr (STREAM) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <bool STREAM, typename T>
+__device__ __forceinline__ void copy_to_lds(T* __restrict__ dst,
+                                            const T* __restrict__ src,
+                                            int count, int tid, int nthreads,
+                                            bool vec) {
+  if (vec) {
+    constexpr int E = 16 / sizeof(T);
+    constexpr int U = 4;
+    const int nv = count / E;
+    const vec16_t* __restrict__ s4 = reinterpret_cast<const vec16_t*>(src);
+    vec16_t* __restrict__ d4 = reinterpret_cast<vec16_t*>(dst);
+    int q = tid;
+    for (; q + (U - 1) * nthreads < nv; q += U * nthreads) {
+      vec16_t t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = load16<STREAM>(s4 + q + u * nthreads);
+#pragma unroll
+      for (int u = 0; u < U; ++u) d4[q + u * nthreads] = t[u];
+    }
+    for (; q < nv; q += nthreads) d4[q] = load16<STREAM>(s4 + q);
+    for (int e = nv * E + tid; e < count; e += nthreads) dst[e] = src[e];
+  } else {
+    for (int e = tid; e < count; e += nthreads) dst[e] = src[e];
+  }
+}
+
+// Round-to-nearest a*b + c with two roundings (no contraction), for the few
+// scalar decisions that must match a reference that never fuses.
+template <typename T>
+__device__ __forceinline__ T mul_add_unfused(T a, T b, T c) {
+#pragma clang fp contract(off)
+  const T m = a * b;
+  return m + c;
+}
+
+template <typename T>
+__device__ __forceinline__ bool is_finite_val(T v) {
+  return v - v == T(0);  // false for inf and NaN
+}
+
+}  // namespace glass

@@ -1,0 +1,52 @@
+// Host-side plumbing shared by the C ABI (capi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <string>
+
+#include "glass_amd.h"
+
+namespace glass {
+
+// Record a failure for glass_last_error() and return `code`.
+int fail(int code, const std::string& msg);
+int fail_hip(hipError_t e, const char* what);
+const char* last_error_text();
+
+struct DeviceInfo {
+  int device = -1;
+  int cu_count = 0;
+  size_t max_lds_per_block = 0;  // bytes of LDS one workgroup may allocate
+  int cooperative = 0;
+};
+// Properties of the current HIP device (queried once per device).
+int current_device_info(DeviceInfo* out);
+
+// Optional launch-shape override from the environment (tests and tuning
+// sweeps): returns `fallback` when `name` is unset or not a positive integer.
+int env_int(const char* name, int fallback);
+
+// Kernel launchers.  Arguments are already validated by the C ABI.
+int launch_bdmv(glass_dtype dt, void* y, const void* S, const void* v, int ss,
+                int kp, int n_problems, hipStream_t stream);
+
+int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
+                       const void* Pinv, const void* b, int ss, int kp,
+                       int n_problems, int max_iters, double rel_tol,
+                       double abs_tol, int* iters, int* status, void* rho,
+                       hipStream_t stream);
+
+size_t grid_workspace_bytes(int ss, int kp, glass_dtype dt);
+int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
+                    const void* b, int ss, int kp, int max_iters,
+                    double rel_tol, double abs_tol, int* iters, int* status,
+                    void* rho, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+}  // namespace glass

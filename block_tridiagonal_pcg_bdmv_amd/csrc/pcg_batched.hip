@@ -1,0 +1,425 @@
+// Batched preconditioned conjugate gradient, one problem per workgroup
+// (GLASS user guide, page "Block-tridiagonal Solves", section
+// "Solve -- glass::pcg"; the matvec windows follow sections "The [L|D|R]
+// block-tridiagonal layout" and "The padded vector layout").
+//
+// Steps per problem (standard PCG; the page fixes the z = p = Pinv r start,
+// rho = r^T z and the stopping rule |rho| < abs_tol + rel_tol |rho_init|):
+//   r = b - S x; z = Pinv r; p = z; rho = r^T z; rho_init = |rho|
+//   loop: Sp = S p; alpha = rho / p^T Sp; x += alpha p; r -= alpha Sp;
+//         z = Pinv r; rho' = r^T z; stop if |rho'| < thresh;
+//         p = z + (rho'/rho) p; rho = rho'
+//
+// Mapping on gfx950 (wave64):
+// * rows are dealt to waves in 64-row chunks: chunk c goes to wave c % NW and
+//   lane l of that wave owns row 64c + l; a lane owns RPT rows.  Its entries of
+//   x, r, p (and the transient z, S p) live in registers.
+// * only p and r must be seen by other lanes (the 3*ss matvec window), so
+//   they are the two padded vectors kept in LDS; the page's other work
+//   vectors stay in registers.
+// * dots: per-lane partial -> wave64 DPP tree -> one LDS slot per wave ->
+//   every thread adds the slots in wave order, so alpha, beta and the stopping
+//   decision are computed identically (same bits) by every thread and need no
+//   broadcast.  Two slot arrays alternate so one barrier per dot suffices.
+// * matrices: RESIDENT -- each lane holds its S row and Pinv row in VGPRs,
+//   loaded once through a small per-wave LDS stage with coalesced 16-byte
+//   loads; STREAMED -- every matvec re-stages the wave's 64-row chunk of S or
+//   Pinv HBM/L2 -> LDS (coalesced) and each lane multiplies its row from there.
+// Barriers per iteration: 4 (p^T Sp, r publish, r^T z, p publish).
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace glass {
+namespace {
+
+template <typename T>
+struct PcgArgs {
+  T* x;
+  const T* S;
+  const T* P;
+  const T* b;
+  int* iters;
+  int* status;
+  T* rho;
+  int ss;
+  int kp;
+  int max_iters;
+  T rel_tol;
+  T abs_tol;
+  int vec;          // 16-byte staging allowed (alignment checked on the host)
+  int stage_elems;  // per-wave LDS stage, elements
+};
+
+constexpr int kStageRowsResident = 16;
+
+// Load the W-wide rows of chunk `chunk` (rows 64*chunk + lane) of a problem's
+// matrix into per-lane registers, 16 rows at a time through the wave's stage.
+template <typename T, int W>
+__device__ __forceinline__ void load_rows_to_regs(T (&reg)[W],
+                                                  const T* __restrict__ gM,
+                                                  int chunk, int n,
+                                                  T* __restrict__ stage,
+                                                  int lane, bool vec) {
+#pragma unroll
+  for (int c = 0; c < W; ++c) reg[c] = T(0);
+  for (int j = 0; j < 64 / kStageRowsResident; ++j) {
+    const int r0 = chunk * 64 + j * kStageRowsResident;
+    const int nrows = min(kStageRowsResident, n - r0);
+    if (nrows <= 0) break;  // wave-uniform
+    copy_to_lds<true>(stage, gM + (long long)r0 * W, nrows * W, lane, kWave, vec);
+    wave_lds_sync();
+    const int local = lane - j * kStageRowsResident;
+    if (local >= 0 && local < nrows) {
+#pragma unroll
+      for (int c = 0; c < W; ++c) reg[c] = stage[local * W + c];
+    }
+    wave_lds_sync();
+  }
+}
+
+template <typename T, int SS, int RPT, bool RES>
+__global__ void __launch_bounds__(1024)
+pcg_batched_kernel(PcgArgs<T> a) {
+  constexpr int WC = SS > 0 ? 3 * SS : 1;  // compile-time width (RES only)
+  const int ss = SS > 0 ? SS : a.ss;
+  const int W = 3 * ss;
+  const int kp = a.kp;
+  const int n = kp * ss;
+  const int pad_len = (kp + 2) * ss;
+  const int NT = blockDim.x;
+  const int NW = NT >> 6;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const long long prob = blockIdx.x;
+  const long long mstride = (long long)n * W;
+  const T* __restrict__ gS = a.S + prob * mstride;
+  const T* __restrict__ gP = a.P + prob * mstride;
+  const bool vec = a.vec != 0;
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* p_pad = reinterpret_cast<T*>(smem_raw);
+  T* r_pad = p_pad + pad_len;
+  T* slotA = r_pad + pad_len;
+  T* slotB = slotA + NW;
+  const size_t head = ((size_t)(2 * pad_len + 2 * NW) * sizeof(T) + 15) & ~(size_t)15;
+  T* stage = reinterpret_cast<T*>(smem_raw + head) + (size_t)wave * a.stage_elems;
+
+  // Row bookkeeping.
+  int row[RPT], wstart[RPT];
+  bool valid[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    row[k] = (wave + k * NW) * 64 + lane;
+    valid[k] = row[k] < n;
+    const int br = valid[k] ? row[k] / ss : 0;
+    wstart[k] = br * ss;  // window start in a padded vector
+  }
+
+  // Matrix rows in registers (RESIDENT only).
+  T mS[RES ? RPT : 1][WC], mP[RES ? RPT : 1][WC];
+  if constexpr (RES) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      load_rows_to_regs<T, WC>(mS[k], gS, wave + k * NW, n, stage, lane, vec);
+      load_rows_to_regs<T, WC>(mP[k], gP, wave + k * NW, n, stage, lane, vec);
+    }
+  }
+
+  // out[k] = (M * vpad)[row k]: one lane, one row, serial 3*ss contraction.
+  auto matvec = [&](T (&out)[RPT], const T* __restrict__ gM,
+                    T (&mreg)[RES ? RPT : 1][WC], const T* __restrict__ vpad) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      T acc = T(0);
+      if constexpr (RES) {
+        if (valid[k]) {
+          const T* __restrict__ w = vpad + wstart[k];
+#pragma unroll
+          for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], w[c], acc);
+        }
+      } else {
+        const int chunk = wave + k * NW;
+        const int r0 = chunk * 64;
+        if (r0 < n) {  // wave-uniform
+          const int nrows = min(64, n - r0);
+          copy_to_lds<false>(stage, gM + (long long)r0 * W, nrows * W, lane, kWave, vec);
+          wave_lds_sync();
+          if (valid[k]) {
+            const T* __restrict__ m = stage + lane * W;
+            const T* __restrict__ w = vpad + wstart[k];
+            if constexpr (SS > 0) {
+#pragma unroll
+              for (int c = 0; c < 3 * SS; ++c) acc = fma(m[c], w[c], acc);
+            } else {
+              for (int c = 0; c < W; ++c) acc = fma(m[c], w[c], acc);
+            }
+          }
+          wave_lds_sync();
+        }
+      }
+      out[k] = acc;
+    }
+  };
+
+  // Initial state: p_pad temporarily holds x0 (the vector S multiplies).
+  T xr[RPT], rr[RPT], pr[RPT], tmp[RPT];
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    xr[k] = T(0);
+    tmp[k] = T(0);
+    if (valid[k]) {
+      xr[k] = a.x[prob * n + row[k]];
+      tmp[k] = a.b[prob * n + row[k]];
+      p_pad[ss + row[k]] = xr[k];
+    }
+  }
+  for (int e = tid; e < ss; e += NT) {
+    p_pad[e] = T(0);
+    p_pad[(kp + 1) * ss + e] = T(0);
+    r_pad[e] = T(0);
+    r_pad[(kp + 1) * ss + e] = T(0);
+  }
+  __syncthreads();
+
+  T sv[RPT];
+  matvec(sv, gS, mS, p_pad);  // S x0
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    rr[k] = valid[k] ? tmp[k] - sv[k] : T(0);
+    if (valid[k]) r_pad[ss + row[k]] = rr[k];
+  }
+  __syncthreads();
+  matvec(sv, gP, mP, r_pad);  // z = Pinv r
+  T part = T(0);
+#pragma unroll
+  for (int k = 0; k < RPT; ++k) {
+    pr[k] = sv[k];
+    if (valid[k]) p_pad[ss + row[k]] = pr[k];  // p = z (x0 reads are done)
+    part = fma(rr[k], sv[k], part);
+  }
+  T rho = block_sum(part, slotA, NW);  // also publishes p_pad
+  const T rho0 = rho;
+  const T rho_init = fabs(rho);
+  const T thresh = mul_add_unfused(a.rel_tol, rho_init, a.abs_tol);
+  T rho_last = rho;
+  int iters = 0;
+  int status = GLASS_PCG_MAX_ITERS;
+  if (rho_init == T(0) || rho_init < thresh) {
+    status = GLASS_PCG_CONVERGED;
+  } else {
+    for (int it = 0; it < a.max_iters; ++it) {
+      matvec(sv, gS, mS, p_pad);  // Sp
+      part = T(0);
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) part = fma(pr[k], sv[k], part);
+      const T pSp = block_sum(part, slotB, NW);
+      if (!(pSp > T(0)) || !is_finite_val(pSp)) {
+        status = GLASS_PCG_BREAKDOWN;
+        break;
+      }
+      const T alpha = rho / pSp;
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        xr[k] = fma(alpha, pr[k], xr[k]);
+        rr[k] = fma(-alpha, sv[k], rr[k]);
+        if (valid[k]) r_pad[ss + row[k]] = rr[k];
+      }
+      iters = it + 1;
+      __syncthreads();
+      matvec(sv, gP, mP, r_pad);  // z = Pinv r
+      part = T(0);
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) part = fma(rr[k], sv[k], part);
+      const T rz = block_sum(part, slotA, NW);
+      rho_last = rz;
+      if (fabs(rz) < thresh) {
+        status = GLASS_PCG_CONVERGED;
+        break;
+      }
+      const T beta = rz / rho;
+#pragma unroll
+      for (int k = 0; k < RPT; ++k) {
+        pr[k] = fma(beta, pr[k], sv[k]);
+        if (valid[k]) p_pad[ss + row[k]] = pr[k];
+      }
+      rho = rz;
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int k = 0; k < RPT; ++k)
+    if (valid[k]) a.x[prob * n + row[k]] = xr[k];
+  if (tid == 0) {
+    if (a.iters) a.iters[prob] = iters;
+    if (a.status) a.status[prob] = status;
+    if (a.rho) {
+      a.rho[2 * prob] = rho0;
+      a.rho[2 * prob + 1] = rho_last;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+struct Plan {
+  int NW = 0;
+  int RPT = 0;
+  bool res = false;
+  int stage_elems = 0;
+  size_t lds = 0;
+};
+
+template <typename T>
+size_t lds_bytes(int ss, int kp, int NW, int stage_elems) {
+  const size_t head = ((size_t)(2 * (kp + 2) * ss + 2 * NW) * sizeof(T) + 15) & ~(size_t)15;
+  return head + (size_t)NW * stage_elems * sizeof(T);
+}
+
+constexpr int kRptChoices[] = {1, 2, 3, 4, 8};
+
+// Register-resident rows (S and Pinv, 3*ss each) fit in the 128-VGPR budget
+// of a 1024-thread workgroup with room for the solver state.
+template <typename T>
+constexpr bool kResidentFits(int ss) {
+  return 6 * ss * (int)sizeof(T) / 4 <= 96;
+}
+
+template <typename T>
+bool make_plan(int ss, int kp, bool res_available, size_t lds_max, Plan* plan) {
+  const int n = kp * ss;
+  const int W = 3 * ss;
+  const int nchunks = (n + 63) / 64;
+  // Register-resident rows when they fit comfortably in 128 VGPRs per lane.
+  const bool res_fits = res_available && kResidentFits<T>(ss) && nchunks <= 16;
+  if (res_fits) {
+    Plan p;
+    p.NW = nchunks;
+    p.RPT = 1;
+    p.res = true;
+    p.stage_elems = kStageRowsResident * W;
+    p.lds = lds_bytes<T>(ss, kp, p.NW, p.stage_elems);
+    if (p.lds <= lds_max) {
+      *plan = p;
+      return true;
+    }
+  }
+  // Streamed: the fewest idle chunk slots, then the most waves.
+  bool found = false;
+  Plan best;
+  int best_waste = 1 << 30;
+  for (int rpt : kRptChoices) {
+    const int NW = (nchunks + rpt - 1) / rpt;
+    if (NW > 16) continue;
+    const int stage = 64 * W;
+    const size_t lds = lds_bytes<T>(ss, kp, NW, stage);
+    if (lds > lds_max) continue;
+    const int waste = NW * rpt - nchunks;
+    if (!found || waste < best_waste || (waste == best_waste && NW > best.NW)) {
+      found = true;
+      best_waste = waste;
+      best.NW = NW;
+      best.RPT = rpt;
+      best.res = false;
+      best.stage_elems = stage;
+      best.lds = lds;
+    }
+  }
+  if (found) *plan = best;
+  return found;
+}
+
+template <typename T, int SS, int RPT, bool RES>
+int launch_one(const PcgArgs<T>& a, int n_problems, const Plan& pl,
+               hipStream_t stream) {
+  auto kern = pcg_batched_kernel<T, SS, RPT, RES>;
+  if (pl.lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)pl.lds);
+    if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(pcg)");
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)n_problems), dim3(pl.NW * 64), pl.lds,
+                     stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "pcg launch");
+  return GLASS_OK;
+}
+
+template <typename T, int SS>
+int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
+              hipStream_t st) {
+  if constexpr (SS > 0 && kResidentFits<T>(SS)) {
+    if (pl.res) return launch_one<T, SS, 1, true>(a, n_problems, pl, st);
+  }
+  switch (pl.RPT) {
+    case 1: return launch_one<T, SS, 1, false>(a, n_problems, pl, st);
+    case 2: return launch_one<T, SS, 2, false>(a, n_problems, pl, st);
+    case 3: return launch_one<T, SS, 3, false>(a, n_problems, pl, st);
+    case 4: return launch_one<T, SS, 4, false>(a, n_problems, pl, st);
+    default: return launch_one<T, SS, 8, false>(a, n_problems, pl, st);
+  }
+}
+
+template <typename T>
+int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
+                 int n_problems, int max_iters, double rel_tol, double abs_tol,
+                 int* iters, int* status, T* rho, hipStream_t st) {
+  DeviceInfo dev;
+  if (int rc = current_device_info(&dev)) return rc;
+  const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
+  Plan pl;
+  if (!make_plan<T>(ss, kp, specialised, dev.max_lds_per_block, &pl))
+    return fail(GLASS_EUNSUPPORTED,
+                "pcg: problem too large for one workgroup (rows or LDS)");
+  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl.res) {
+    Plan alt;
+    if (make_plan<T>(ss, kp, false, dev.max_lds_per_block, &alt)) pl = alt;
+  }
+  const long long n = (long long)kp * ss;
+  PcgArgs<T> a;
+  a.x = x;
+  a.S = S;
+  a.P = P;
+  a.b = b;
+  a.iters = iters;
+  a.status = status;
+  a.rho = rho;
+  a.ss = ss;
+  a.kp = kp;
+  a.max_iters = max_iters;
+  a.rel_tol = (T)rel_tol;
+  a.abs_tol = (T)abs_tol;
+  a.vec = aligned(S, 16) && aligned(P, 16) &&
+          ((n * 3 * ss * (long long)sizeof(T)) % 16 == 0);
+  a.stage_elems = pl.stage_elems;
+  switch (ss) {
+    case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
+    case 12: return launch_ss<T, 12>(a, n_problems, pl, st);
+    case 14: return launch_ss<T, 14>(a, n_problems, pl, st);
+    case 21: return launch_ss<T, 21>(a, n_problems, pl, st);
+    default: return launch_ss<T, 0>(a, n_problems, pl, st);
+  }
+}
+
+}  // namespace
+
+int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
+                       const void* Pinv, const void* b, int ss, int kp,
+                       int n_problems, int max_iters, double rel_tol,
+                       double abs_tol, int* iters, int* status, void* rho,
+                       hipStream_t stream) {
+  if (dt == GLASS_F32)
+    return launch_typed<float>((float*)x, (const float*)S, (const float*)Pinv,
+                               (const float*)b, ss, kp, n_problems, max_iters,
+                               rel_tol, abs_tol, iters, status, (float*)rho,
+                               stream);
+  return launch_typed<double>((double*)x, (const double*)S,
+                              (const double*)Pinv, (const double*)b, ss, kp,
+                              n_problems, max_iters, rel_tol, abs_tol, iters,
+                              status, (double*)rho, stream);
+}
+
+}  // namespace glass

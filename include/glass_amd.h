@@ -1,0 +1,158 @@
+/*
+ * glass_amd.h -- C ABI of the MI355X (gfx950) batched block-tridiagonal
+ * matvec and preconditioned conjugate-gradient library.
+ *
+ * Operations (GLASS user guide, page "Block-tridiagonal Solves"):
+ *   - section "The [L|D|R] block-tridiagonal layout": a block-tridiagonal
+ *     matrix with knot_points block-rows of size state_size is stored as
+ *     knot_points contiguous row-major strips, each state_size x 3*state_size,
+ *     holding [L_br | D_br | R_br]; L of the first and R of the last block-row
+ *     are stored but multiply zero pads.
+ *   - section "The padded vector layout": vectors of (knot_points+2)*state_size
+ *     with one zero pad block at each end; block-row br reads the window
+ *     v[br*ss, br*ss + 3*ss) and writes y[(br+1)*ss + row].
+ *   - section "Matvec -- glass::bdmv": y = A_bd * v.
+ *   - section "Solve -- glass::pcg": preconditioned CG on S x = b with a
+ *     block-tridiagonal preconditioner Pinv (also in [L|D|R] form); stop when
+ *     |rho| < abs_tol + rel_tol * |rho_init| with rho = r^T z the
+ *     preconditioned residual; x carries the initial guess in and the
+ *     solution out; the iteration count is returned.
+ *   - the same page names a cooperative grid-wide PCG (one solve spanning the
+ *     whole grid) as future work; glass_pcg_grid is that solve.
+ *
+ * Conventions shared by every entry point:
+ *   - All array arguments are DEVICE pointers owned by the caller (e.g. torch
+ *     tensors).  Nothing is allocated or freed by the library.
+ *   - Work is enqueued asynchronously on hip_stream (a hipStream_t; NULL is
+ *     the null stream).  No entry point synchronises the host.
+ *   - dtype selects float (GLASS_F32) or double (GLASS_F64) for every
+ *     floating-point array of the call.
+ *   - Layouts are problem-major and contiguous:
+ *       S, Pinv   [n_problems][knot_points][state_size][3*state_size]
+ *       bdmv v, y [n_problems][(knot_points+2)*state_size]   (padded)
+ *       PCG x, b  [n_problems][knot_points*state_size]        (unpadded)
+ *       iters_out, status_out   int32 [n_problems]
+ *       rho_out   dtype [n_problems][2] = (signed initial r^T z, last r^T z)
+ *   - Base pointers must be aligned to the element size; 16-byte alignment
+ *     enables the vectorised loads (otherwise a scalar path is used).
+ *   - Return value: GLASS_OK, or a negative GLASS_E* code; on error nothing
+ *     has been enqueued (except GLASS_EHIP, which reports a failed launch).
+ *     glass_last_error() then describes the failure (per host thread).
+ *   - Calls on one stream run in order; calls on different streams that write
+ *     the same memory race, as with any HIP kernel.
+ */
+#ifndef GLASS_AMD_H
+#define GLASS_AMD_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { GLASS_F32 = 0, GLASS_F64 = 1 } glass_dtype;
+
+enum {
+  GLASS_OK = 0,
+  GLASS_EINVAL = -1,       /* null pointer, size <= 0, bad dtype, misaligned,
+                              max_iters < 0, tolerance negative or NaN */
+  GLASS_EUNSUPPORTED = -2, /* valid, but beyond this build's size limits */
+  GLASS_EHIP = -3,         /* a HIP runtime call or launch failed */
+  GLASS_ECOOP = -4         /* the grid solve cannot be made co-resident */
+};
+
+/* Per-problem PCG outcome written to status_out. */
+enum {
+  GLASS_PCG_CONVERGED = 0, /* |rho| < abs_tol + rel_tol*|rho_init| was met
+                              (also when rho_init == 0: nothing to do)   */
+  GLASS_PCG_MAX_ITERS = 1, /* max_iters iterations ran without meeting it   */
+  GLASS_PCG_BREAKDOWN = 2  /* p^T S p <= 0 or not finite (S not SPD, NaN);
+                              x keeps the last completed update           */
+};
+
+/* Largest state_size accepted by any entry point. */
+#define GLASS_MAX_STATE_SIZE 64
+
+/*
+ * y = A_bd * v for n_problems independent matrices (page "Block-tridiagonal
+ * Solves", sections "The padded vector layout" and "Matvec -- glass::bdmv"):
+ *   y[q][(br+1)*ss + i] = sum_{c < 3ss} S[q][br][i][c] * v[q][br*ss + c]
+ * for br < knot_points, i < state_size.  The caller zeroes the pad blocks of
+ * v; the pad blocks of y are not written.  y must not overlap S or v.
+ * Each output row is summed by one thread in a fixed order, so the result does
+ * not depend on the launch shape.
+ * Limits: 1 <= state_size <= GLASS_MAX_STATE_SIZE, knot_points >= 1,
+ * n_problems >= 0 (0 enqueues nothing).
+ */
+int glass_bdmv_batched(void* y, const void* S, const void* v, int state_size,
+                       int knot_points, int n_problems, glass_dtype dtype,
+                       void* hip_stream);
+
+/*
+ * Preconditioned conjugate gradient on S x = b, one independent problem per
+ * workgroup (page "Block-tridiagonal Solves", section "Solve -- glass::pcg").
+ * On entry x holds the initial guess; on exit the solution.  Steps:
+ *   r = b - S x; z = Pinv r; p = z; rho = r^T z; rho_init = |rho|;
+ *   thresh = abs_tol + rel_tol * rho_init (both rounded to dtype);
+ *   converged at once if rho_init == 0 or rho_init < thresh; otherwise per
+ *   iteration: Sp = S p; alpha = rho / (p^T Sp); x += alpha p;
+ *   r -= alpha Sp; z = Pinv r; rho' = r^T z; stop if |rho'| < thresh;
+ *   p = z + (rho'/rho) p; rho = rho'.
+ * iters_out[q] = number of completed x updates (<= max_iters).  S and Pinv
+ * must be symmetric positive definite for the result to be meaningful; a
+ * non-positive p^T S p stops that problem with GLASS_PCG_BREAKDOWN.
+ * Limits: state_size <= GLASS_MAX_STATE_SIZE; knot_points*state_size <= 8192
+ * (further limited by LDS for large state_size: GLASS_EUNSUPPORTED).
+ */
+int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
+                      int state_size, int knot_points, int n_problems,
+                      int max_iters, double rel_tol, double abs_tol,
+                      int* iters_out, glass_dtype dtype, void* hip_stream);
+
+/* As glass_pcg_batched, plus optional per-problem outputs (either may be
+ * NULL): status_out (GLASS_PCG_*) and rho_out (see conventions). */
+int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
+                         const void* b, int state_size, int knot_points,
+                         int n_problems, int max_iters, double rel_tol,
+                         double abs_tol, int* iters_out, int* status_out,
+                         void* rho_out, glass_dtype dtype, void* hip_stream);
+
+/*
+ * One PCG solve (same steps and outputs as glass_pcg_batched with
+ * n_problems = 1) spread over a cooperative grid of workgroups that stay
+ * co-resident on the device; each workgroup owns a contiguous range of
+ * block-rows, and the dot products are reduced across the grid in a fixed
+ * order, so every workgroup takes identical decisions.
+ * workspace: caller-owned device memory of at least
+ * glass_pcg_grid_workspace_bytes(...) bytes, 256-byte aligned; its contents on
+ * entry do not matter and it must not be used by another call on another
+ * stream at the same time.
+ * Limits: knot_points >= 4; state_size <= GLASS_MAX_STATE_SIZE.
+ * Returns GLASS_ECOOP if the device cannot hold a large enough grid.
+ */
+size_t glass_pcg_grid_workspace_bytes(int state_size, int knot_points,
+                                      glass_dtype dtype);
+int glass_pcg_grid(void* x, const void* S, const void* Pinv, const void* b,
+                   int state_size, int knot_points, int max_iters,
+                   double rel_tol, double abs_tol, int* iters_out,
+                   void* workspace, size_t workspace_bytes, glass_dtype dtype,
+                   void* hip_stream);
+int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
+                      int state_size, int knot_points, int max_iters,
+                      double rel_tol, double abs_tol, int* iters_out,
+                      int* status_out, void* rho_out, void* workspace,
+                      size_t workspace_bytes, glass_dtype dtype,
+                      void* hip_stream);
+
+/* Static text for a GLASS_* return code. */
+const char* glass_status_string(int status);
+/* Text describing the last failing call on this host thread ("" if none). */
+const char* glass_last_error(void);
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int glass_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLASS_AMD_H */

@@ -1,0 +1,104 @@
+"""The C ABI library on the host: it loads, exports every declared symbol, and
+rejects invalid arguments before touching a device (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "glass_amd.h")
+LIB = os.path.join(ROOT, "block_tridiagonal_pcg_bdmv_amd", "libglass_amd.so")
+
+EINVAL, EUNSUPPORTED = -1, -2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(glass_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from block_tridiagonal_pcg_bdmv_amd import build
+        build.build(verbose=False)
+    import block_tridiagonal_pcg_bdmv_amd as glass
+    return glass.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("glass_bdmv_batched", "glass_pcg_batched", "glass_pcg_grid",
+                 "glass_pcg_batched_ex", "glass_pcg_grid_ex",
+                 "glass_pcg_grid_workspace_bytes", "glass_status_string",
+                 "glass_last_error", "glass_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version(lib):
+    assert lib.glass_status_string(0) == b"ok"
+    assert lib.glass_status_string(-4).startswith(b"cooperative")
+    assert lib.glass_version() >= 100
+
+
+FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: checks fail first
+
+
+def _bdmv(lib, y=FAKE, S=FAKE, v=FAKE, ss=14, kp=64, B=1, dt=0):
+    return lib.glass_bdmv_batched(y, S, v, ss, kp, B, dt, None)
+
+
+def test_bdmv_argument_errors(lib):
+    assert _bdmv(lib, y=None) == EINVAL
+    assert _bdmv(lib, S=None) == EINVAL
+    assert _bdmv(lib, v=ctypes.c_void_p(0x100002)) == EINVAL  # misaligned
+    assert _bdmv(lib, ss=0) == EINVAL
+    assert _bdmv(lib, kp=0) == EINVAL
+    assert _bdmv(lib, B=-1) == EINVAL
+    assert _bdmv(lib, dt=7) == EINVAL
+    assert _bdmv(lib, ss=65) == EUNSUPPORTED
+    assert b"state_size" in lib.glass_last_error()
+    assert _bdmv(lib, B=0) == 0  # nothing to do, nothing launched
+
+
+def _pcg(lib, x=FAKE, S=FAKE, P=FAKE, b=FAKE, ss=6, kp=32, B=1, it=20,
+         rel=1e-6, ab=0.0, iters=FAKE, dt=0):
+    return lib.glass_pcg_batched(x, S, P, b, ss, kp, B, it, rel, ab, iters, dt, None)
+
+
+def test_pcg_argument_errors(lib):
+    assert _pcg(lib, x=None) == EINVAL
+    assert _pcg(lib, P=None) == EINVAL
+    assert _pcg(lib, iters=None) == EINVAL
+    assert _pcg(lib, it=-1) == EINVAL
+    assert _pcg(lib, rel=-1.0) == EINVAL
+    assert _pcg(lib, rel=float("nan")) == EINVAL
+    assert _pcg(lib, ab=float("inf")) == EINVAL
+    assert _pcg(lib, dt=2) == EINVAL
+    assert _pcg(lib, ss=64, kp=200) == EUNSUPPORTED  # 12800 rows > 8192
+    assert _pcg(lib, B=0) == 0
+
+
+def test_grid_argument_errors_and_workspace_size(lib):
+    ws = lib.glass_pcg_grid_workspace_bytes(12, 8192, 1)
+    assert ws >= 256 + 2 * 2048 * 8 + 2048 * 4 * 12 * 8
+    assert lib.glass_pcg_grid_workspace_bytes(12, 3, 1) == 0
+    assert lib.glass_pcg_grid_workspace_bytes(0, 100, 1) == 0
+
+    def grid(kp=8192, ws_ptr=ctypes.c_void_p(0x100000), ws_bytes=ws, it=10):
+        return lib.glass_pcg_grid(FAKE, FAKE, FAKE, FAKE, 12, kp, it, 1e-10, 0.0,
+                                  FAKE, ws_ptr, ws_bytes, 1, None)
+    assert grid(kp=3) == EINVAL
+    assert grid(ws_ptr=None) == EINVAL
+    assert grid(ws_ptr=ctypes.c_void_p(0x100080)) == EINVAL  # not 256-aligned
+    assert grid(ws_bytes=ws - 1) == EINVAL
+    assert grid(it=-3) == EINVAL

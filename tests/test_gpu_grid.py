@@ -1,0 +1,105 @@
+"""GPU parity of glass_pcg_grid (one chain over a cooperative grid) against
+the CPU oracle through the C ABI: iterations within +-2, x within 1e-10
+(fp64) / 1e-4 (fp32) relative L2 of the float64 oracle at the same
+iteration count, final criterion met."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_common import X_REL, assert_pcg_parity, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol):
+    t = {k: to_dev(v) for k, v in inp.items()}
+    x = t["x0"].clone()
+    iters = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    rho = torch.zeros(2, dtype=x.dtype, device="cuda")
+    nbytes = glass.pcg_grid_workspace_bytes(ss, kp, x.dtype)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    glass.pcg_grid(x, t["S"], t["Pinv"], t["b"], ss, kp, max_iters, rel_tol, abs_tol,
+                   iters, ws, status, rho)
+    torch.cuda.synchronize()
+    return (x.cpu().numpy(), iters.cpu().numpy(), status.cpu().numpy(),
+            rho.cpu().numpy().reshape(1, 2))
+
+
+def test_grid_full_chain_fp64(gpu):
+    """The kp=8192, ss=12 fp64 chain, every entry of x checked."""
+    w = workloads.CONFIGS[4]
+    inp = workloads.generate(w)
+    say("grid ss=12 kp=8192 fp64")
+    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    assert res[2][0] == gpu.CONVERGED, res[2]
+    its = assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float64)
+    say("  iterations: %d" % its[0])
+
+
+@pytest.mark.parametrize("ss,kp,dtype", [(12, 64, np.float64), (6, 300, np.float32),
+                                         (14, 97, np.float32), (21, 40, np.float32),
+                                         (5, 33, np.float64), (3, 4, np.float64),
+                                         (12, 5000, np.float32)])
+def test_grid_matches_oracle_and_batched(gpu, ss, kp, dtype):
+    """Specialised and runtime state sizes, partitions of uneven length, the
+    minimum chain (kp = 4).  Also cross-checked with the batched solve of the
+    same single problem."""
+    rng = np.random.default_rng(ss * 7 + kp)
+    S, D = workloads.random_spd_strips(rng, 1, ss, kp, 0.1, dtype)
+    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
+           "b": rng.standard_normal((1, kp * ss)).astype(dtype),
+           "x0": np.zeros((1, kp * ss), dtype)}
+    rel = 1e-10 if dtype == np.float64 else 1e-7
+    say("grid ss=%d kp=%d %s" % (ss, kp, np.dtype(dtype).name))
+    res = grid_gpu(gpu, inp, ss, kp, 500, rel, 0.0)
+    assert res[2][0] == gpu.CONVERGED
+    assert_pcg_parity(inp, ss, kp, 500, rel, 0.0, res, dtype)
+    if kp * ss <= 8192:
+        from gpu_common import pcg_gpu
+        bat = pcg_gpu(gpu, inp, ss, kp, 500, rel, 0.0)
+        assert abs(int(bat[1][0]) - int(res[1][0])) <= 2
+        num = np.linalg.norm(bat[0][0].astype(np.float64) - res[0][0])
+        den = np.linalg.norm(bat[0][0].astype(np.float64))
+        if bat[1][0] == res[1][0]:
+            assert num / den <= X_REL[dtype]
+
+
+@pytest.mark.parametrize("wgs", [2, 8, 24, 64, 512])
+def test_grid_partition_count_does_not_change_the_answer(gpu, monkeypatch, wgs):
+    """Different grid sizes change only the summation tree of the dots."""
+    rng = np.random.default_rng(77)
+    ss, kp = 12, 2048
+    S, D = workloads.random_spd_strips(rng, 1, ss, kp, 0.05, np.float64)
+    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D), "b": rng.standard_normal((1, kp * ss)),
+           "x0": np.zeros((1, kp * ss))}
+    monkeypatch.setenv("GLASS_AMD_GRID_WGS", str(wgs))
+    say("grid wgs=%d" % wgs)
+    res = grid_gpu(gpu, inp, ss, kp, 200, 1e-10, 0.0)
+    assert res[2][0] == gpu.CONVERGED
+    assert_pcg_parity(inp, ss, kp, 200, 1e-10, 0.0, res, np.float64)
+
+
+def test_grid_status_cases(gpu):
+    rng = np.random.default_rng(5)
+    ss, kp = 6, 64
+    S, D = workloads.random_spd_strips(rng, 1, ss, kp, 0.3, np.float64)
+    P = workloads.block_jacobi_pinv(D)
+    b = rng.standard_normal((1, kp * ss))
+    x0 = rng.standard_normal((1, kp * ss))
+    base = {"S": S, "Pinv": P, "b": b, "x0": x0}
+    say("grid max_iters=3")
+    x, it, st, _ = grid_gpu(gpu, base, ss, kp, 3, 1e-12, 0.0)
+    assert it[0] == 3 and st[0] == gpu.MAX_ITERS
+    xo, _, _, _ = oracle.pcg(x0, S, P, b, ss, kp, 3, 1e-12, 0.0, "f64")
+    assert np.linalg.norm(x - xo) <= 1e-10 * np.linalg.norm(xo)
+    say("grid breakdown")
+    x, it, st, _ = grid_gpu(gpu, dict(base, S=-S), ss, kp, 20, 1e-8, 0.0)
+    assert st[0] == gpu.BREAKDOWN and it[0] == 0
+    np.testing.assert_array_equal(x, x0)
+    say("grid b=0, x0=0")
+    x, it, st, _ = grid_gpu(gpu, dict(base, b=0 * b, x0=0 * x0), ss, kp, 20, 1e-8, 0.0)
+    assert st[0] == gpu.CONVERGED and it[0] == 0 and np.all(x == 0)

@@ -1,0 +1,150 @@
+"""GPU parity of glass_pcg_batched against the CPU oracle through the C ABI.
+Bars (see gpu_common): iterations within +-2, x within 1e-4 (fp32) / 1e-10
+(fp64) relative L2 of the oracle at the same iteration count, final criterion
+met."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_common import assert_pcg_parity, pcg_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+def run_workload(gpu, cfg, n_problems=None, dtype=None):
+    w = workloads.CONFIGS[cfg]
+    inp = workloads.generate(w, n_problems=n_problems)
+    if dtype is not None:
+        inp = {k: v.astype(dtype) for k, v in inp.items()}
+    dt = inp["b"].dtype.type
+    say("pcg cfg%d B=%d %s" % (cfg, inp["b"].shape[0], np.dtype(dt).name))
+    res = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    assert np.all(res[2] == gpu.CONVERGED)
+    return assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, dt)
+
+
+@pytest.mark.parametrize("cfg", [0, 2, 3])
+def test_pcg_workloads_reduced_batch(gpu, cfg):
+    run_workload(gpu, cfg, n_problems=33)
+
+
+@pytest.mark.parametrize("cfg", [0, 2, 3])
+def test_pcg_workloads_full_batch(gpu, cfg):
+    its = run_workload(gpu, cfg)
+    say("  iterations: %s" % dict(zip(*np.unique(its, return_counts=True))))
+
+
+@pytest.mark.parametrize("cfg", [0, 2, 3])
+def test_pcg_fp64(gpu, cfg):
+    run_workload(gpu, cfg, n_problems=17, dtype=np.float64)
+
+
+def test_pcg_streamed_and_resident_agree(gpu, monkeypatch):
+    """The register-resident and the streamed kernels run the same steps; only
+    the summation tree of the dots may differ, so both meet the bars."""
+    w = workloads.CONFIGS[2]
+    inp = workloads.generate(w, n_problems=24)
+    a = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
+    say("pcg cfg2 forced streamed")
+    b = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    for res in (a, b):
+        assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float32)
+    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-5 * np.abs(a[0]).max())
+
+
+@pytest.mark.parametrize("ss,kp,B,margin", [(1, 1, 4, 0.5), (1, 700, 3, 0.3),
+                                            (2, 4, 5, 0.3), (5, 9, 6, 0.2),
+                                            (6, 1, 3, 0.5), (7, 150, 3, 0.2),
+                                            (14, 50, 4, 0.2), (21, 20, 3, 0.1),
+                                            (33, 10, 2, 0.2), (64, 5, 2, 0.3)])
+def test_pcg_generic_shapes(gpu, ss, kp, B, margin):
+    """Specialised and runtime state sizes, ragged last chunk, kp = 1, several
+    rows per lane (n up to 700), resident and streamed placements."""
+    rng = np.random.default_rng(ss * 100 + kp)
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, margin, np.float32)
+    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, np.float32),
+           "b": rng.standard_normal((B, kp * ss)).astype(np.float32),
+           "x0": np.zeros((B, kp * ss), np.float32)}
+    say("pcg ss=%d kp=%d B=%d" % (ss, kp, B))
+    res = pcg_gpu(gpu, inp, ss, kp, 300, 1e-8, 0.0)
+    assert_pcg_parity(inp, ss, kp, 300, 1e-8, 0.0, res, np.float32)
+
+
+def test_pcg_nonzero_initial_guess_and_block_tridiagonal_pinv(gpu):
+    """x0 != 0 and a Pinv with non-zero L/R blocks (the kernels treat Pinv as a
+    general [L|D|R] matrix)."""
+    rng = np.random.default_rng(3)
+    ss, kp, B = 6, 32, 16
+    S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.5, np.float64)
+    P, _ = workloads.random_spd_strips(rng, B, ss, kp, 3.0, np.float64)
+    P = P / 8.0
+    inp = {"S": S.astype(np.float32), "Pinv": P.astype(np.float32),
+           "b": rng.standard_normal((B, kp * ss)).astype(np.float32),
+           "x0": rng.standard_normal((B, kp * ss)).astype(np.float32)}
+    say("pcg x0!=0, tridiagonal Pinv")
+    res = pcg_gpu(gpu, inp, ss, kp, 200, 1e-7, 0.0)
+    assert np.all(res[2] == gpu.CONVERGED)
+    assert_pcg_parity(inp, ss, kp, 200, 1e-7, 0.0, res, np.float32)
+
+
+def test_pcg_status_cases(gpu):
+    rng = np.random.default_rng(8)
+    ss, kp, B = 6, 8, 6
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.5, np.float32)
+    P = workloads.block_jacobi_pinv(D, np.float32)
+    b = rng.standard_normal((B, kp * ss)).astype(np.float32)
+    x0 = rng.standard_normal((B, kp * ss)).astype(np.float32)
+    S[1] = -S[1]            # negative definite -> breakdown at the first step
+    b[2] = 0.0              # with x0 = 0 below: rho_init == 0 -> converged, 0 its
+    b[3, 5] = np.nan        # NaN -> breakdown, no hang
+    x0[2] = 0.0
+    inp = {"S": S, "Pinv": P, "b": b, "x0": x0}
+    say("pcg status cases")
+    x, it, st, rho = pcg_gpu(gpu, inp, ss, kp, 50, 1e-6, 0.0)
+    xo, ito, sto, rhoo = oracle.pcg(x0, S, P, b, ss, kp, 50, 1e-6, 0.0, "f32")
+    np.testing.assert_array_equal(st, sto)
+    assert st[1] == gpu.BREAKDOWN and it[1] == 0
+    assert st[2] == gpu.CONVERGED and it[2] == 0 and np.all(x[2] == 0)
+    assert st[3] == gpu.BREAKDOWN and it[3] == 0
+    assert np.all(np.abs(it - ito) <= 2)
+    # max_iters = 0 and a huge abs_tol
+    x, it, st, _ = pcg_gpu(gpu, inp, ss, kp, 0, 1e-6, 0.0)
+    assert np.all(it == 0)
+    assert st[0] == gpu.MAX_ITERS
+    np.testing.assert_array_equal(x[0], x0[0])
+    x, it, st, _ = pcg_gpu(gpu, inp, ss, kp, 50, 0.0, 1e30)
+    assert np.all(it == 0) and np.all(st[[0, 2, 4, 5]] == gpu.CONVERGED)
+
+
+def test_pcg_max_iters_exhausted(gpu):
+    w = workloads.CONFIGS[2]
+    inp = workloads.generate(w, n_problems=8)
+    say("pcg max_iters=2")
+    res = pcg_gpu(gpu, inp, w.ss, w.kp, 2, w.rel_tol, w.abs_tol)
+    assert np.all(res[1] == 2) and np.all(res[2] == gpu.MAX_ITERS)
+    assert_pcg_parity(inp, w.ss, w.kp, 2, w.rel_tol, w.abs_tol, res, np.float32)
+
+
+def test_pcg_run_to_run_deterministic(gpu):
+    w = workloads.CONFIGS[3]
+    inp = workloads.generate(w, n_problems=12)
+    a = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    b = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
+
+
+def test_pcg_rejects_inconsistent_buffers(gpu):
+    w = workloads.CONFIGS[0]
+    inp = workloads.generate(w, n_problems=2)
+    t = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
+    it = torch.zeros(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(ValueError):
+        gpu.pcg_batched(t["x0"][:1], t["S"], t["Pinv"], t["b"], w.ss, w.kp, 10, 1e-6, 0.0, it)
+    with pytest.raises(TypeError):
+        gpu.pcg_batched(t["x0"], t["S"], t["Pinv"], t["b"], w.ss, w.kp, 10, 1e-6, 0.0,
+                        it.to(torch.int64))
