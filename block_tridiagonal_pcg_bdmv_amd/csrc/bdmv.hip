@@ -12,7 +12,12 @@
 // of a wave are contiguous.  Each row is summed by one thread in a fixed
 // order, so the result is independent of NT.  The operation streams S once:
 // it is HBM-bandwidth bound, and the LDS hop only exists to turn the
-// 3*ss-strided per-row reads into coalesced 16-byte loads.
+// 3*ss-strided per-row reads into coalesced 16-byte loads.  For the
+// specialised state sizes every load of the tile is issued before the first
+// LDS store (ceil(3*ss*sizeof(T)/16) vectors per thread in flight), through a
+// buffer resource over exactly the tile's bytes, so lanes past the end read
+// zeros without branching.  The tile height is chosen so that the rows of a
+// problem split into tiles with as little of a ragged last tile as possible.
 #include <climits>
 
 #include "common.hpp"
@@ -21,8 +26,10 @@
 namespace glass {
 namespace {
 
+constexpr int kBdmvMaxThreads = 256;
+
 template <typename T, int SS>
-__global__ void __launch_bounds__(1024)
+__global__ void __launch_bounds__(kBdmvMaxThreads)
 bdmv_kernel(T* __restrict__ y, const T* __restrict__ S,
             const T* __restrict__ v, int ss_rt, int kp,
             int tiles_per_problem, int vec) {
@@ -40,13 +47,36 @@ bdmv_kernel(T* __restrict__ y, const T* __restrict__ S,
   const int vcount = (br_hi - br_lo + 3) * ss;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  T* s_mat = reinterpret_cast<T*>(smem_raw);  // rows * W, row-major
-  T* s_win = s_mat + (size_t)NT * W;          // v[br_lo*ss, (br_hi+3)*ss)
+  // s_mat: rows * W matrix entries, row-major (padded to whole vectors);
+  // s_win: v[br_lo*ss, (br_hi+3)*ss).
+  constexpr int U = SS > 0 ? (3 * SS * (int)sizeof(T) + 15) / 16 : 1;
+  T* s_mat = reinterpret_cast<T*>(smem_raw);
+  T* s_win = reinterpret_cast<T*>(smem_raw + (size_t)NT * W * sizeof(T)
+                                  + (SS > 0 ? (size_t)NT * (U * 16 - W * sizeof(T)) : 0));
 
   const T* gS = S + (prob * n + row0) * (long long)W;
-  copy_to_lds<true>(s_mat, gS, rows * W, tid, NT, vec != 0);
   const T* gv = v + prob * (long long)(kp + 2) * ss + (long long)br_lo * ss;
-  for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];
+  if constexpr (SS > 0) {
+    const int count = rows * W;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gS, count * (int)sizeof(T));
+    vec16_t t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = buffer_load16(rs, (tid + u * NT) * 16);
+    for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];
+    vec16_t* s4 = reinterpret_cast<vec16_t*>(s_mat);
+#pragma unroll
+    for (int u = 0; u < U; ++u) s4[tid + u * NT] = t[u];
+    // A ragged tile may end inside a vector: those elements directly, after
+    // every vector store (the condition is uniform over the workgroup).
+    if ((count * (int)sizeof(T)) % 16 != 0) {
+      __syncthreads();
+      const int nv = count * (int)sizeof(T) / 16;
+      for (int e = nv * (16 / (int)sizeof(T)) + tid; e < count; e += NT) s_mat[e] = gS[e];
+    }
+  } else {
+    copy_to_lds<true>(s_mat, gS, rows * W, tid, NT, vec != 0);
+    for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];
+  }
   __syncthreads();
 
   if (tid < rows) {
@@ -72,16 +102,28 @@ int launch_typed(T* y, const T* S, const T* v, int ss, int kp, int n_problems,
   if (int rc = current_device_info(&dev)) return rc;
   const int W = 3 * ss;
   const long long n = (long long)kp * ss;
-  // Threads per workgroup: 256 rows unless a tile of rows would exceed
-  // ~48 KB of LDS (large state_size / fp64); never below one wave.
-  int NT = (int)((48 * 1024) / ((size_t)W * sizeof(T)));
-  NT = NT / 64 * 64;
-  if (NT > 256) NT = 256;
-  if (NT < 64) NT = 64;
+  // Threads per workgroup (one per row): a multiple of 64 up to 256 rows and
+  // ~48 KB of LDS, picking the height that leaves the smallest ragged last
+  // tile per problem (ties: the taller tile).
+  int nt_max = (int)((48 * 1024) / ((size_t)W * sizeof(T)));
+  nt_max = nt_max / 64 * 64;
+  if (nt_max > 256) nt_max = 256;
+  if (nt_max < 64) nt_max = 64;
+  int NT = 64;
+  long long best_waste = -1;
+  for (int c = 64; c <= nt_max; c += 64) {
+    const long long waste = (n + c - 1) / c * c - n;
+    if (best_waste < 0 || waste <= best_waste) {
+      best_waste = waste;
+      NT = c;
+    }
+  }
   NT = env_int("GLASS_AMD_BDMV_THREADS", NT);
-  if (NT % 64 != 0 || NT > 1024)
-    return fail(GLASS_EINVAL, "GLASS_AMD_BDMV_THREADS must be a multiple of 64 <= 1024");
-  const size_t lds = ((size_t)NT * W + NT + 4 * (size_t)ss) * sizeof(T) + 16;
+  if (NT % 64 != 0 || NT > kBdmvMaxThreads)
+    return fail(GLASS_EINVAL, "GLASS_AMD_BDMV_THREADS must be a multiple of 64 <= 256");
+  const size_t row_bytes =
+      SS > 0 ? (size_t)((W * sizeof(T) + 15) / 16 * 16) : (size_t)W * sizeof(T);
+  const size_t lds = (size_t)NT * row_bytes + ((size_t)NT + 4 * (size_t)ss) * sizeof(T) + 16;
   if (lds > dev.max_lds_per_block)
     return fail(GLASS_EUNSUPPORTED, "bdmv tile does not fit in LDS");
   const long long tiles = (n + NT - 1) / NT;

@@ -99,14 +99,25 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+typedef float vec16_t __attribute__((ext_vector_type(4)));  // 16-byte bit copy
+
+// Buffer resource over `nbytes` bytes at `base` (raw addressing, gfx9
+// descriptor word 3).  Loads through it past `nbytes` return zeros.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes,
+                                           kBufferRsrcWord3);
+}
+__device__ __forceinline__ vec16_t buffer_load16(__amdgpu_buffer_rsrc_t rs, int byte_off) {
+  return __builtin_bit_cast(vec16_t, __builtin_amdgcn_raw_buffer_load_b128(rs, byte_off, 0, 0));
+}
+
 // Copy `count` contiguous elements global -> LDS using `nthreads` threads
 // (thread index `tid`).  With `vec`, src and dst must be 16-byte aligned; the
 // bulk moves as 16-byte vectors, issued in groups so several loads are in
 // flight per thread, and the tail moves element-wise.  STREAM marks data read
 // once (non-temporal loads); data re-read later is loaded normally so it can
 // stay in L2 / Infinity Cache.
-typedef float vec16_t __attribute__((ext_vector_type(4)));  // 16-byte bit copy
-
 template <bool STREAM>
 __device__ __forceinline__ vec16_t load16(const vec16_t* p) {
   if constexpr (STREAM) return __builtin_nontemporal_load(p);
@@ -136,6 +147,37 @@ __device__ __forceinline__ void copy_to_lds(T* __restrict__ dst,
     for (int e = nv * E + tid; e < count; e += nthreads) dst[e] = src[e];
   } else {
     for (int e = tid; e < count; e += nthreads) dst[e] = src[e];
+  }
+}
+
+// Load one W-wide matrix row straight into registers.  All loads are issued
+// before any is consumed, so a lane keeps W*sizeof(T) bytes in flight.  With
+// WIDE the row start must be aligned to the widest power of two (<= 16 bytes)
+// dividing W*sizeof(T) -- true for every row when the matrix base is 16-byte
+// aligned; otherwise element loads are used.
+template <typename T, int W, bool WIDE>
+__device__ __forceinline__ void load_row_regs(T (&reg)[W], const T* __restrict__ src) {
+  constexpr int RB = W * (int)sizeof(T);
+  if constexpr (WIDE && RB % 16 == 0) {
+    constexpr int NV = RB / 16, E = 16 / (int)sizeof(T);
+    const vec16_t* __restrict__ s = reinterpret_cast<const vec16_t*>(src);
+    vec16_t t[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) t[j] = s[j];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) __builtin_memcpy(&reg[j * E], &t[j], 16);
+  } else if constexpr (WIDE && RB % 8 == 0) {
+    typedef float vec8_t __attribute__((ext_vector_type(2)));
+    constexpr int NV = RB / 8, E = 8 / (int)sizeof(T);
+    const vec8_t* __restrict__ s = reinterpret_cast<const vec8_t*>(src);
+    vec8_t t[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) t[j] = s[j];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) __builtin_memcpy(&reg[j * E], &t[j], 8);
+  } else {
+#pragma unroll
+    for (int c = 0; c < W; ++c) reg[c] = src[c];
   }
 }
 

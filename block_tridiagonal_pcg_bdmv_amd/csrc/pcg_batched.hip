@@ -22,10 +22,17 @@
 //   decision are computed identically (same bits) by every thread and need no
 //   broadcast.  Two slot arrays alternate so one barrier per dot suffices.
 // * matrices: RESIDENT -- each lane holds its S row and Pinv row in VGPRs,
-//   loaded once through a small per-wave LDS stage with coalesced 16-byte
-//   loads; STREAMED -- every matvec re-stages the wave's 64-row chunk of S or
-//   Pinv HBM/L2 -> LDS (coalesced) and each lane multiplies its row from there.
+//   loaded once straight from HBM with every load of both rows in flight;
+//   STREAMED -- every matvec re-stages the wave's 64-row chunk of S or
+//   Pinv HBM/L2 -> LDS (coalesced 16-byte loads) and each lane multiplies its
+//   row from there.  With PREFETCH, the loads of the wave's next chunk in
+//   the fixed sequence (chunks of S, then of Pinv, then of S, ...) are issued
+//   into registers before the current chunk is multiplied, so they stay in
+//   flight across the multiply, the dots and the workgroup barriers (matrix
+//   loads never depend on the vectors).
 // Barriers per iteration: 4 (p^T Sp, r publish, r^T z, p publish).
+#include <cstdlib>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -50,37 +57,22 @@ struct PcgArgs {
   int stage_elems;  // per-wave LDS stage, elements
 };
 
-constexpr int kStageRowsResident = 16;
+// Placements of the matrices (see the header).
+enum Mode { kResident = 0, kStreamPrefetch = 1, kStream = 2 };
 
-// Load the W-wide rows of chunk `chunk` (rows 64*chunk + lane) of a problem's
-// matrix into per-lane registers, 16 rows at a time through the wave's stage.
-template <typename T, int W>
-__device__ __forceinline__ void load_rows_to_regs(T (&reg)[W],
-                                                  const T* __restrict__ gM,
-                                                  int chunk, int n,
-                                                  T* __restrict__ stage,
-                                                  int lane, bool vec) {
-#pragma unroll
-  for (int c = 0; c < W; ++c) reg[c] = T(0);
-  for (int j = 0; j < 64 / kStageRowsResident; ++j) {
-    const int r0 = chunk * 64 + j * kStageRowsResident;
-    const int nrows = min(kStageRowsResident, n - r0);
-    if (nrows <= 0) break;  // wave-uniform
-    copy_to_lds<true>(stage, gM + (long long)r0 * W, nrows * W, lane, kWave, vec);
-    wave_lds_sync();
-    const int local = lane - j * kStageRowsResident;
-    if (local >= 0 && local < nrows) {
-#pragma unroll
-      for (int c = 0; c < W; ++c) reg[c] = stage[local * W + c];
-    }
-    wave_lds_sync();
-  }
-}
+// Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for 3-4
+// rows per lane, which covers problems of 1537-2048 rows per wave group;
+// 16 waves otherwise (rows beyond 4096 need them, at the cost of spills).
+constexpr int max_threads_for(int rpt) { return (rpt == 3 || rpt == 4) ? 512 : 1024; }
 
-template <typename T, int SS, int RPT, bool RES>
-__global__ void __launch_bounds__(1024)
+template <typename T, int SS, int RPT, int MODE>
+__global__ void __launch_bounds__(max_threads_for(RPT))
 pcg_batched_kernel(PcgArgs<T> a) {
-  constexpr int WC = SS > 0 ? 3 * SS : 1;  // compile-time width (RES only)
+  constexpr bool RES = MODE == kResident;
+  constexpr bool PFM = MODE == kStreamPrefetch;
+  constexpr int WC = SS > 0 ? 3 * SS : 1;  // compile-time width
+  // 16-byte vectors one lane moves per 64-row chunk (PREFETCH).
+  constexpr int PF = PFM ? (WC * (int)sizeof(T) + 15) / 16 : 1;
   const int ss = SS > 0 ? SS : a.ss;
   const int W = 3 * ss;
   const int kp = a.kp;
@@ -115,15 +107,56 @@ pcg_batched_kernel(PcgArgs<T> a) {
     wstart[k] = br * ss;  // window start in a padded vector
   }
 
-  // Matrix rows in registers (RESIDENT only).
+  // Matrix rows in registers (RESIDENT only): every load of both rows is in
+  // flight at once.
   T mS[RES ? RPT : 1][WC], mP[RES ? RPT : 1][WC];
   if constexpr (RES) {
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
-      load_rows_to_regs<T, WC>(mS[k], gS, wave + k * NW, n, stage, lane, vec);
-      load_rows_to_regs<T, WC>(mP[k], gP, wave + k * NW, n, stage, lane, vec);
+#pragma unroll
+      for (int c = 0; c < WC; ++c) {
+        mS[k][c] = T(0);
+        mP[k][c] = T(0);
+      }
+      if (valid[k]) {
+        const long long off = (long long)row[k] * WC;
+        if (vec) {
+          load_row_regs<T, WC, true>(mS[k], gS + off);
+          load_row_regs<T, WC, true>(mP[k], gP + off);
+        } else {
+          load_row_regs<T, WC, false>(mS[k], gS + off);
+          load_row_regs<T, WC, false>(mP[k], gP + off);
+        }
+      }
     }
   }
+
+  // PREFETCH: pf holds the wave's next chunk (64 rows) as 16-byte vectors in
+  // the coalesced order (lane l holds vectors l, l+64, ...).  The loads are
+  // buffer loads over exactly the chunk's bytes: a vector past its end reads
+  // zeros instead of touching memory beyond the matrix, so no lane branches
+  // and one offset register serves all of them.  The LDS stage holds PF*64
+  // vectors; stores past the chunk land in its padding.
+  vec16_t pf[PF];
+  auto issue = [&](const T* __restrict__ gM, int k) {
+    const int r0 = (wave + k * NW) * 64;
+    const int nbytes = min(64, n - r0) * W * (int)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gM + (long long)r0 * W, nbytes);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) pf[u] = buffer_load16(rs, (lane + u * kWave) * 16);
+  };
+  auto stage_from_pf = [&](const T* __restrict__ gM, int k) {
+    const int r0 = (wave + k * NW) * 64;
+    const int count = min(64, n - r0) * W;
+    const int nv = count * (int)sizeof(T) / 16;
+    vec16_t* __restrict__ d4 = reinterpret_cast<vec16_t*>(stage);
+#pragma unroll
+    for (int u = 0; u < PF; ++u) d4[lane + u * kWave] = pf[u];
+    // A ragged last chunk may end inside a vector: those elements directly.
+    for (int e = nv * (16 / (int)sizeof(T)) + lane; e < count; e += kWave)
+      stage[e] = gM[(long long)r0 * W + e];
+  };
+  if constexpr (PFM) issue(gS, 0);  // the first matvec is S x0
 
   // out[k] = (M * vpad)[row k]: one lane, one row, serial 3*ss contraction.
   auto matvec = [&](T (&out)[RPT], const T* __restrict__ gM,
@@ -141,15 +174,31 @@ pcg_batched_kernel(PcgArgs<T> a) {
         const int chunk = wave + k * NW;
         const int r0 = chunk * 64;
         if (r0 < n) {  // wave-uniform
-          const int nrows = min(64, n - r0);
-          copy_to_lds<false>(stage, gM + (long long)r0 * W, nrows * W, lane, kWave, vec);
+          if constexpr (PFM) {
+            stage_from_pf(gM, k);
+            // Keep the next loads after these LDS stores, so one chunk's
+            // registers serve both (the compiler would otherwise hoist the
+            // loads and hold two chunks).
+            asm volatile("" ::: "memory");
+            // Next chunk in the sequence: this matrix's next chunk of this
+            // wave, else chunk 0 of the other matrix (matvecs alternate).
+            if (k + 1 < RPT && (wave + (k + 1) * NW) * 64 < n) issue(gM, k + 1);
+            else issue(gM == gS ? gP : gS, 0);
+          } else {
+            const int nrows = min(64, n - r0);
+            copy_to_lds<false>(stage, gM + (long long)r0 * W, nrows * W, lane, kWave, vec);
+          }
           wave_lds_sync();
           if (valid[k]) {
             const T* __restrict__ m = stage + lane * W;
             const T* __restrict__ w = vpad + wstart[k];
             if constexpr (SS > 0) {
+              // Partial unroll: bounds the LDS reads in flight (registers).
+#pragma unroll 3
+              for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
 #pragma unroll
-              for (int c = 0; c < 3 * SS; ++c) acc = fma(m[c], w[c], acc);
+                for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], w[c], acc);
+              }
             } else {
               for (int c = 0; c < W; ++c) acc = fma(m[c], w[c], acc);
             }
@@ -268,6 +317,7 @@ struct Plan {
   int NW = 0;
   int RPT = 0;
   bool res = false;
+  bool prefetch = false;
   int stage_elems = 0;
   size_t lds = 0;
 };
@@ -299,7 +349,7 @@ bool make_plan(int ss, int kp, bool res_available, size_t lds_max, Plan* plan) {
     p.NW = nchunks;
     p.RPT = 1;
     p.res = true;
-    p.stage_elems = kStageRowsResident * W;
+    p.stage_elems = 0;
     p.lds = lds_bytes<T>(ss, kp, p.NW, p.stage_elems);
     if (p.lds <= lds_max) {
       *plan = p;
@@ -312,7 +362,7 @@ bool make_plan(int ss, int kp, bool res_available, size_t lds_max, Plan* plan) {
   int best_waste = 1 << 30;
   for (int rpt : kRptChoices) {
     const int NW = (nchunks + rpt - 1) / rpt;
-    if (NW > 16) continue;
+    if (NW * 64 > max_threads_for(rpt)) continue;
     const int stage = 64 * W;
     const size_t lds = lds_bytes<T>(ss, kp, NW, stage);
     if (lds > lds_max) continue;
@@ -331,10 +381,10 @@ bool make_plan(int ss, int kp, bool res_available, size_t lds_max, Plan* plan) {
   return found;
 }
 
-template <typename T, int SS, int RPT, bool RES>
+template <typename T, int SS, int RPT, int MODE>
 int launch_one(const PcgArgs<T>& a, int n_problems, const Plan& pl,
                hipStream_t stream) {
-  auto kern = pcg_batched_kernel<T, SS, RPT, RES>;
+  auto kern = pcg_batched_kernel<T, SS, RPT, MODE>;
   if (pl.lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -348,19 +398,35 @@ int launch_one(const PcgArgs<T>& a, int n_problems, const Plan& pl,
   return GLASS_OK;
 }
 
+// Streamed with prefetch: specialised sizes whose 64-row chunk is at most 16
+// 16-byte vectors per lane.
+template <typename T>
+constexpr bool kPrefetchFits(int ss) {
+  return 3 * ss * (int)sizeof(T) <= 256;
+}
+
+template <typename T, int SS, int MODE>
+int launch_rpt(const PcgArgs<T>& a, int n_problems, const Plan& pl,
+               hipStream_t st) {
+  switch (pl.RPT) {
+    case 1: return launch_one<T, SS, 1, MODE>(a, n_problems, pl, st);
+    case 2: return launch_one<T, SS, 2, MODE>(a, n_problems, pl, st);
+    case 3: return launch_one<T, SS, 3, MODE>(a, n_problems, pl, st);
+    case 4: return launch_one<T, SS, 4, MODE>(a, n_problems, pl, st);
+    default: return launch_one<T, SS, 8, MODE>(a, n_problems, pl, st);
+  }
+}
+
 template <typename T, int SS>
 int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
               hipStream_t st) {
   if constexpr (SS > 0 && kResidentFits<T>(SS)) {
-    if (pl.res) return launch_one<T, SS, 1, true>(a, n_problems, pl, st);
+    if (pl.res) return launch_one<T, SS, 1, kResident>(a, n_problems, pl, st);
   }
-  switch (pl.RPT) {
-    case 1: return launch_one<T, SS, 1, false>(a, n_problems, pl, st);
-    case 2: return launch_one<T, SS, 2, false>(a, n_problems, pl, st);
-    case 3: return launch_one<T, SS, 3, false>(a, n_problems, pl, st);
-    case 4: return launch_one<T, SS, 4, false>(a, n_problems, pl, st);
-    default: return launch_one<T, SS, 8, false>(a, n_problems, pl, st);
+  if constexpr (SS > 0 && kPrefetchFits<T>(SS)) {
+    if (pl.prefetch) return launch_rpt<T, SS, kStreamPrefetch>(a, n_problems, pl, st);
   }
+  return launch_rpt<T, SS, kStream>(a, n_problems, pl, st);
 }
 
 template <typename T>
@@ -395,6 +461,22 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.vec = aligned(S, 16) && aligned(P, 16) &&
           ((n * 3 * ss * (long long)sizeof(T)) % 16 == 0);
   a.stage_elems = pl.stage_elems;
+  pl.prefetch = !pl.res && specialised && a.vec &&
+                3 * ss * (int)sizeof(T) <= 256 &&
+                std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
+  if (pl.prefetch) {
+    // The stage holds a whole number of 16-byte vectors per lane.
+    const int pf = (3 * ss * (int)sizeof(T) + 15) / 16;
+    const int stage = pf * 64 * 16 / (int)sizeof(T);
+    const size_t lds = lds_bytes<T>(ss, kp, pl.NW, stage);
+    if (lds <= dev.max_lds_per_block) {
+      pl.stage_elems = stage;
+      pl.lds = lds;
+      a.stage_elems = stage;
+    } else {
+      pl.prefetch = false;
+    }
+  }
   switch (ss) {
     case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
     case 12: return launch_ss<T, 12>(a, n_problems, pl, st);

@@ -16,21 +16,33 @@
 //   rebuild p = z + beta p on the ghosts themselves.  That leaves two grid
 //   barriers per iteration -- one per dot product -- and no separate halo
 //   exchange step.
-// * Dots: per-workgroup partial (wave64 DPP tree + fixed wave order) -> one
-//   global slot per workgroup -> after the barrier every wave re-adds all G
-//   slots in the same fixed order, so every workgroup holds identical alpha,
-//   beta and stopping decisions without a broadcast.
+// * Grid dot (grid_dot): per-thread partial -> wave64 DPP tree -> LDS slot
+//   per wave -> wave 0 adds the wave slots in order and publishes the
+//   workgroup partial (and the edge z values staged in LDS).  The workgroups
+//   form (up to) 8 groups of consecutive partitions -- one group per XCD.  A
+//   workgroup arrives at its group counter; the last arriver of a group (known
+//   from the fetch-add result) adds the group's partials in partition order,
+//   publishes the group sum and arrives at the top counter.  Every workgroup
+//   waits for the top counter, loads the group sums and adds them in group
+//   order, so every workgroup holds identical alpha, beta and stopping
+//   decisions.  Only wave 0 of a workgroup takes part.
+// * Publication without cache maintenance: every value another workgroup
+//   reads (partials, group sums, edge z) is written with device-scope
+//   atomic stores and read with device-scope atomic loads, which the
+//   hardware serves at the device coherence point; the writing wave waits for
+//   its stores to complete (s_waitcnt vmcnt(0)) before it arrives.  A
+//   device-scope release/acquire fence instead writes back / invalidates the
+//   XCD's L2, which costs several microseconds per barrier and grows with
+//   the number of workgroups.
 // * Matrices: for the specialised state sizes each thread keeps its S row
-//   (extended rows) and Pinv row (own rows) in VGPRs, loaded once with
-//   coalesced loads through a per-wave LDS stage; the iteration then touches
-//   only LDS, registers and the small exchange buffers.
-// * Grid barrier: every thread fences its global writes at device (agent)
-//   scope, one thread per workgroup adds to a monotonically increasing counter
-//   with release semantics and spins with acquire loads until the counter
-//   reaches (barrier number) * G.  The spin is bounded: a timeout sets a flag,
-//   every later wait returns as soon as it sees the flag, the kernel runs to
-//   its end, and the status output reports the timeout instead of the device
-//   hanging.
+//   (extended rows) and Pinv row (own rows) in VGPRs, loaded once with every
+//   load of the row in flight; the iteration then touches only registers,
+//   LDS and the small exchange buffers.
+// * Grid barrier: monotonically increasing arrival counters (group and
+//   top), polled by one lane with relaxed loads and s_sleep between polls.
+//   The poll is bounded: a timeout sets a flag, every later wait returns as
+//   soon as it sees the flag, the kernel runs to its end, and the status
+//   output reports the timeout instead of the device hanging.
 #include <climits>
 
 #include "common.hpp"
@@ -41,7 +53,6 @@ namespace {
 
 constexpr int kGridMaxWorkgroups = 2048;
 constexpr unsigned kSpinLimit = 1u << 21;
-constexpr int kGridStatusTimeout = 3;
 
 template <typename T>
 struct GridArgs {
@@ -57,18 +68,26 @@ struct GridArgs {
   int max_iters;
   T rel_tol;
   T abs_tol;
-  unsigned int* counter;  // barrier arrivals (zeroed before the launch)
-  unsigned int* flags;    // [0]: a barrier spin timed out
+  unsigned int* counter;  // top-level arrivals (zeroed before the launch)
+  unsigned int* flags;    // [0]: a barrier wait timed out
+  unsigned int* gcount;   // group arrivals, one per kCounterStride words
+  T* gsum1;               // [kGroups] group sums of the p^T S p partials
+  T* gsum2;               // [kGroups] group sums of the r^T z partials
   T* slot1;               // [G] per-workgroup p^T S p partials
   T* slot2;               // [G] per-workgroup r^T z partials
   T* edges;               // [G][4*ss]: z of block-rows A, A+1, B-2, B-1
   int G;
   int nb_max;
-  int stage_elems;
+  int wide;               // matrix bases 16-byte aligned: vector row loads
 };
 
+// Barrier groups (one per XCD) and the spacing of their counters (one
+// 128-byte cache line each).
+constexpr int kGroups = 8;
+constexpr int kCounterStride = 32;
+
 struct WorkspaceLayout {
-  size_t counter, slot1, slot2, edges, total;
+  size_t counter, gcount, gsum1, gsum2, slot1, slot2, edges, total;
 };
 
 inline size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -77,37 +96,19 @@ WorkspaceLayout layout(int ss, int kp, size_t elem) {
   const size_t gmax = (size_t)std::min(kp / 2, kGridMaxWorkgroups);
   WorkspaceLayout w;
   w.counter = 0;  // counter at +0, flags at +4
-  w.slot1 = 256;
+  w.gcount = 256;
+  w.gsum1 = w.gcount + kGroups * kCounterStride * sizeof(unsigned int);
+  w.gsum2 = w.gsum1 + 256;
+  w.slot1 = w.gsum2 + 256;
   w.slot2 = w.slot1 + round256(gmax * elem);
   w.edges = w.slot2 + round256(gmax * elem);
   w.total = w.edges + round256(gmax * 4 * (size_t)ss * elem);
   return w;
 }
 
-__global__ void grid_reset_kernel(unsigned int* counter) {
+__global__ void grid_reset_kernel(unsigned int* counter, unsigned int* gcount) {
   if (threadIdx.x < 2) counter[threadIdx.x] = 0u;  // counter, flags[0]
-}
-
-__device__ __forceinline__ void grid_barrier(unsigned int* counter,
-                                             unsigned int target,
-                                             unsigned int* flags) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    unsigned int spins = 0;
-    while (__hip_atomic_load(counter, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if ((++spins & 255u) == 0u &&
-          __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
-        break;  // another workgroup already gave up: do not wait again
-      if (spins > kSpinLimit) {
-        __hip_atomic_store(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
+  if (threadIdx.x < kGroups) gcount[threadIdx.x * kCounterStride] = 0u;
 }
 
 template <typename T>
@@ -115,43 +116,109 @@ __device__ __forceinline__ T load_shared_global(const T* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Sum of the G workgroup slots, added in slot order per lane then by the
-// fixed wave tree: identical bits in every wave of every workgroup.
 template <typename T>
-__device__ __forceinline__ T grid_sum(const T* slots, int G, int lane) {
-  T s = T(0);
-  for (int g = lane; g < G; g += kWave) s = s + load_shared_global(slots + g);
-  return wave_sum(s);
+__device__ __forceinline__ void store_shared_global(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Stage rows [row_lo, row_lo+64) of a matrix (clipped to [0, n)) so that
-// lane l receives row row_lo + l in registers; 16 rows per pass.
-template <typename T, int W>
-__device__ __forceinline__ void load_rows(T (&reg)[W], const T* __restrict__ gM,
-                                          long long row_lo, long long n,
-                                          T* __restrict__ stage, int lane) {
-#pragma unroll
-  for (int c = 0; c < W; ++c) reg[c] = T(0);
-  constexpr int R = 16;
-  for (int j = 0; j < 64 / R; ++j) {
-    long long r0 = row_lo + j * R;
-    long long r1 = r0 + R;
-    if (r0 < 0) r0 = 0;
-    if (r1 > n) r1 = n;
-    if (r1 <= r0) continue;  // wave-uniform
-    const T* src = gM + r0 * W;
-    const int count = (int)(r1 - r0) * W;
-    const bool vec = ((reinterpret_cast<uintptr_t>(src) & 15) == 0);
-    copy_to_lds<true>(stage, src, count, lane, kWave, vec);
-    wave_lds_sync();
-    const long long myrow = row_lo + lane;
-    if (myrow >= r0 && myrow < r1) {
-      const int local = (int)(myrow - r0);
-#pragma unroll
-      for (int c = 0; c < W; ++c) reg[c] = stage[local * W + c];
+// Wait until this wave's earlier global stores have completed.
+__device__ __forceinline__ void wait_stores_complete() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// Poll `counter` until it reaches `target` (one lane).  Bounded: see the
+// timeout rule at the top of the file.
+__device__ __forceinline__ void wait_counter(const unsigned int* counter,
+                                             unsigned int target,
+                                             unsigned int* flags) {
+  unsigned int spins = 0;
+  while (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    __builtin_amdgcn_s_sleep(1);
+    if ((++spins & 255u) == 0u &&
+        __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+      break;  // another workgroup already gave up: do not wait again
+    if (spins > kSpinLimit) {
+      __hip_atomic_store(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
     }
-    wave_lds_sync();
   }
+}
+
+// Partials one lane loads per batch in the group sum.
+constexpr int kSumBatch = 8;
+
+// Where the barrier groups split the G partitions: group k holds partitions
+// [group_begin(k), group_begin(k+1)).
+__device__ __forceinline__ int group_begin(int k, int G, int ngroups) {
+  return (int)((long long)k * G / ngroups);
+}
+
+struct GridSync {
+  unsigned int* counter;
+  unsigned int* gcount;
+  unsigned int* flags;
+  int g, G, ngroups, grp, gbeg, gsize;
+};
+
+// Grid-wide sum of the per-thread values v; every thread of every workgroup
+// must call it and gets the same bits.  If `edge_lds` is non-null, wave 0
+// also publishes the workgroup's n_edge edge z values staged there.  `bar`
+// is the barrier number (1-based).  Contains two __syncthreads().
+template <typename T>
+__device__ __forceinline__ T grid_dot(T v, T* __restrict__ slots, T* __restrict__ gsum,
+                                      const T* edge_lds, T* __restrict__ edges_g,
+                                      int n_edge, const GridSync& gs, unsigned int bar,
+                                      T* wsl, T* bcast, int NW, int wave, int lane) {
+  v = wave_sum(v);
+  if (lane == 0) wsl[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    T part = wsl[0];
+    for (int w = 1; w < NW; ++w) part = part + wsl[w];
+    if (edge_lds)
+      for (int j = lane; j < n_edge; j += kWave) store_shared_global(edges_g + j, edge_lds[j]);
+    if (lane == 0) store_shared_global(slots + gs.g, part);
+    wait_stores_complete();
+    unsigned int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(gs.gcount + gs.grp * kCounterStride, 1u,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old == bar * (unsigned)gs.gsize - 1u) {
+      // Last arriver of the group: every member's partial is published.
+      // Add them in partition order (lane-strided, then the wave tree).
+      T s = T(0);
+      for (int base = 0; base < gs.gsize; base += kSumBatch * kWave) {
+        T val[kSumBatch];
+#pragma unroll
+        for (int k = 0; k < kSumBatch; ++k) {
+          const int j = base + lane + k * kWave;
+          val[k] = j < gs.gsize ? load_shared_global(slots + gs.gbeg + j) : T(0);
+        }
+#pragma unroll
+        for (int k = 0; k < kSumBatch; ++k)
+          if (base + lane + k * kWave < gs.gsize) s = s + val[k];
+      }
+      s = wave_sum(s);
+      if (lane == 0) store_shared_global(gsum + gs.grp, s);
+      wait_stores_complete();
+      if (lane == 0)
+        __hip_atomic_fetch_add(gs.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (lane == 0) wait_counter(gs.counter, bar * (unsigned)gs.ngroups, gs.flags);
+    // Group sums in group order (every lane loads all of them).
+    T gv[kGroups];
+#pragma unroll
+    for (int k = 0; k < kGroups; ++k)
+      gv[k] = k < gs.ngroups ? load_shared_global(gsum + k) : T(0);
+    T t = gv[0];
+#pragma unroll
+    for (int k = 1; k < kGroups; ++k)
+      if (k < gs.ngroups) t = t + gv[k];
+    if (lane == 0) *bcast = t;
+  }
+  __syncthreads();
+  return *bcast;
 }
 
 template <typename T, int SS, bool RES>
@@ -161,7 +228,6 @@ pcg_grid_kernel(GridArgs<T> a) {
   const int ss = SS > 0 ? SS : a.ss;
   const int W = 3 * ss;
   const int kp = a.kp;
-  const long long n = (long long)kp * ss;
   const int G = a.G;
   const int NT = blockDim.x;
   const int NW = NT >> 6;
@@ -173,13 +239,14 @@ pcg_grid_kernel(GridArgs<T> a) {
   const int nb = B - A;
   const int next = (nb + 2) * ss;  // extended rows: block-rows A-1 .. B
   const int loc_len = (a.nb_max + 4) * ss;
+  const int n_edge = 4 * ss;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* p_loc = reinterpret_cast<T*>(smem_raw);  // block-rows A-2 .. B+1
   T* r_loc = p_loc + loc_len;                 // same indexing
-  T* wsl = r_loc + loc_len;                   // [NW]
-  const size_t head = ((size_t)(2 * loc_len + NW) * sizeof(T) + 15) & ~(size_t)15;
-  T* stage = reinterpret_cast<T*>(smem_raw + head) + (size_t)wave * a.stage_elems;
+  T* edge_lds = r_loc + loc_len;              // [4*ss] z of A, A+1, B-2, B-1
+  T* wsl = edge_lds + n_edge;                 // [NW]
+  T* bcast = wsl + NW;                        // [1]
 
   // This thread's extended row.
   const int e = tid;
@@ -193,34 +260,53 @@ pcg_grid_kernel(GridArgs<T> a) {
   // z of a block-row outside [A, B), as published by its owner (0 outside).
   auto ghost_z = [&](int gbr, int gi) -> T {
     if (gbr < 0 || gbr >= kp) return T(0);
-    if (gbr < A) return load_shared_global(a.edges + (size_t)(g - 1) * 4 * ss + 2 * ss +
+    if (gbr < A) return load_shared_global(a.edges + (size_t)(g - 1) * n_edge + 2 * ss +
                                            (gbr - (A - 2)) * ss + gi);
-    return load_shared_global(a.edges + (size_t)(g + 1) * 4 * ss + (gbr - B) * ss + gi);
+    return load_shared_global(a.edges + (size_t)(g + 1) * n_edge + (gbr - B) * ss + gi);
   };
-  auto publish_edges = [&](T zval) {
+  // Owners of the two edge block-rows on each side stage their z in LDS;
+  // wave 0 publishes the array inside the next grid_dot.
+  auto stage_edges = [&](T zval) {
     if (!own) return;
-    T* my = a.edges + (size_t)g * 4 * ss;
-    if (br < A + 2) my[(br - A) * ss + i] = zval;
-    if (br >= B - 2) my[2 * ss + (br - (B - 2)) * ss + i] = zval;
+    if (br < A + 2) edge_lds[(br - A) * ss + i] = zval;
+    if (br >= B - 2) edge_lds[2 * ss + (br - (B - 2)) * ss + i] = zval;
   };
-  auto block_partial = [&](T v) {
-    v = wave_sum(v);
-    if (lane == 0) wsl[wave] = v;
-    __syncthreads();
-    if (tid == 0) {
-      T s = wsl[0];
-      for (int w = 1; w < NW; ++w) s = s + wsl[w];
-      return s;
-    }
-    return T(0);
+  GridSync gs;
+  gs.counter = a.counter;
+  gs.gcount = a.gcount;
+  gs.flags = a.flags;
+  gs.g = g;
+  gs.G = G;
+  gs.ngroups = G < kGroups ? G : kGroups;
+  gs.grp = 0;
+  while (gs.grp + 1 < gs.ngroups && group_begin(gs.grp + 1, G, gs.ngroups) <= g) ++gs.grp;
+  gs.gbeg = group_begin(gs.grp, G, gs.ngroups);
+  gs.gsize = group_begin(gs.grp + 1, G, gs.ngroups) - gs.gbeg;
+  unsigned int barriers = 0;
+  auto dot = [&](T v, T* slots, T* gsum, bool with_edges) {
+    ++barriers;
+    return grid_dot(v, slots, gsum, with_edges ? edge_lds : (const T*)nullptr,
+                    a.edges + (size_t)g * n_edge, n_edge, gs, barriers, wsl, bcast,
+                    NW, wave, lane);
   };
 
-  // Matrix rows in registers (specialised sizes).
+  // Matrix rows in registers (specialised sizes): S for every valid extended
+  // row, Pinv for owned rows.
   T mS[WC], mP[WC];
   if constexpr (RES) {
-    const long long row_lo = (long long)(A - 1) * ss + wave * 64;
-    load_rows<T, WC>(mS, a.S, row_lo, n, stage, lane);
-    load_rows<T, WC>(mP, a.P, row_lo, n, stage, lane);
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      mS[c] = T(0);
+      mP[c] = T(0);
+    }
+    if (valid) {
+      if (a.wide) load_row_regs<T, WC, true>(mS, a.S + grow * WC);
+      else load_row_regs<T, WC, false>(mS, a.S + grow * WC);
+    }
+    if (own) {
+      if (a.wide) load_row_regs<T, WC, true>(mP, a.P + grow * WC);
+      else load_row_regs<T, WC, false>(mP, a.P + grow * WC);
+    }
   }
   auto row_dot = [&](const T* __restrict__ gM, const T* __restrict__ mreg,
                      const T* __restrict__ vloc) -> T {
@@ -251,13 +337,8 @@ pcg_grid_kernel(GridArgs<T> a) {
   if (e < next) r_loc[e + ss] = rr;
   __syncthreads();
   T z = own ? row_dot(a.P, mP, r_loc) : T(0);
-  publish_edges(z);
-  T part = block_partial(own ? rr * z : T(0));
-  if (tid == 0) a.slot2[g] = part;
-  unsigned int barriers = 1;
-  grid_barrier(a.counter, barriers * (unsigned)G, a.flags);
-
-  T rho = grid_sum(a.slot2, G, lane);
+  stage_edges(z);
+  T rho = dot(own ? rr * z : T(0), a.slot2, a.gsum2, true);
   const T rho0 = rho;
   const T rho_init = fabs(rho);
   const T thresh = mul_add_unfused(a.rel_tol, rho_init, a.abs_tol);
@@ -277,11 +358,7 @@ pcg_grid_kernel(GridArgs<T> a) {
 
     for (int it = 0; it < a.max_iters; ++it) {
       sv = valid ? row_dot(a.S, mS, p_loc) : T(0);  // S p on extended rows
-      part = block_partial(own ? pr * sv : T(0));
-      if (tid == 0) a.slot1[g] = part;
-      ++barriers;
-      grid_barrier(a.counter, barriers * (unsigned)G, a.flags);
-      const T pSp = grid_sum(a.slot1, G, lane);
+      const T pSp = dot(own ? pr * sv : T(0), a.slot1, a.gsum1, false);
       if (!(pSp > T(0)) || !is_finite_val(pSp)) {
         status = GLASS_PCG_BREAKDOWN;
         break;
@@ -293,12 +370,8 @@ pcg_grid_kernel(GridArgs<T> a) {
       iters = it + 1;
       __syncthreads();
       z = own ? row_dot(a.P, mP, r_loc) : T(0);
-      publish_edges(z);
-      part = block_partial(own ? rr * z : T(0));
-      if (tid == 0) a.slot2[g] = part;
-      ++barriers;
-      grid_barrier(a.counter, barriers * (unsigned)G, a.flags);
-      const T rz = grid_sum(a.slot2, G, lane);
+      stage_edges(z);
+      const T rz = dot(own ? rr * z : T(0), a.slot2, a.gsum2, true);
       rho_last = rz;
       if (fabs(rz) < thresh) {
         status = GLASS_PCG_CONVERGED;
@@ -324,7 +397,7 @@ pcg_grid_kernel(GridArgs<T> a) {
     const bool timed_out =
         __hip_atomic_load(a.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
     if (a.iters) a.iters[0] = iters;
-    if (a.status) a.status[0] = timed_out ? kGridStatusTimeout : status;
+    if (a.status) a.status[0] = timed_out ? GLASS_PCG_GRID_TIMEOUT : status;
     if (a.rho) {
       a.rho[0] = rho0;
       a.rho[1] = rho_last;
@@ -347,7 +420,7 @@ int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
   if (e != hipSuccess) return fail_hip(e, "occupancy query (grid)");
   if ((long long)per_cu * dev.cu_count < a.G)
     return fail(GLASS_ECOOP, "grid pcg: workgroups cannot all be co-resident");
-  hipLaunchKernelGGL(grid_reset_kernel, dim3(1), dim3(64), 0, st, a.counter);
+  hipLaunchKernelGGL(grid_reset_kernel, dim3(1), dim3(64), 0, st, a.counter, a.gcount);
   e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "grid reset launch");
   void* args[] = {&a};
@@ -405,11 +478,13 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
       return fail(GLASS_EUNSUPPORTED, "grid pcg: chain too long for the grid");
     G = std::min(gmax, G * 2);
   }
+  // The group counters count up to (2*max_iters + 1) * (group size) without
+  // wrapping (the group size is at most G).
+  if ((2.0 * max_iters + 1.0) * G >= (double)UINT_MAX)
+    return fail(GLASS_EUNSUPPORTED, "grid pcg: max_iters too large for the barrier counter");
   const int NW = NT / 64;
-  const int stage_elems = res ? 16 * 3 * ss : 0;
   const size_t loc_len = (size_t)(nb_max + 4) * ss;
-  const size_t head = ((2 * loc_len + NW) * sizeof(T) + 15) & ~(size_t)15;
-  const size_t lds = head + (size_t)NW * stage_elems * sizeof(T);
+  const size_t lds = (2 * loc_len + 4 * (size_t)ss + NW + 1) * sizeof(T);
   if (lds > dev.max_lds_per_block)
     return fail(GLASS_EUNSUPPORTED, "grid pcg: partition does not fit in LDS");
 
@@ -429,12 +504,15 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   a.counter = reinterpret_cast<unsigned int*>(ws + wl.counter);
   a.flags = a.counter + 1;
+  a.gcount = reinterpret_cast<unsigned int*>(ws + wl.gcount);
+  a.gsum1 = reinterpret_cast<T*>(ws + wl.gsum1);
+  a.gsum2 = reinterpret_cast<T*>(ws + wl.gsum2);
   a.slot1 = reinterpret_cast<T*>(ws + wl.slot1);
   a.slot2 = reinterpret_cast<T*>(ws + wl.slot2);
   a.edges = reinterpret_cast<T*>(ws + wl.edges);
   a.G = G;
   a.nb_max = nb_max;
-  a.stage_elems = stage_elems;
+  a.wide = aligned(S, 16) && aligned(P, 16);
   if (res) {
     switch (ss) {
       case 6: return launch_grid_res<T, 6>(a, NT, lds, dev, st);

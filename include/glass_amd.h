@@ -66,8 +66,11 @@ enum {
   GLASS_PCG_CONVERGED = 0, /* |rho| < abs_tol + rel_tol*|rho_init| was met
                               (also when rho_init == 0: nothing to do)   */
   GLASS_PCG_MAX_ITERS = 1, /* max_iters iterations ran without meeting it   */
-  GLASS_PCG_BREAKDOWN = 2  /* p^T S p <= 0 or not finite (S not SPD, NaN);
+  GLASS_PCG_BREAKDOWN = 2, /* p^T S p <= 0 or not finite (S not SPD, NaN);
                               x keeps the last completed update           */
+  GLASS_PCG_GRID_TIMEOUT = 3 /* glass_pcg_grid only: a grid barrier wait
+                              gave up (workgroups not co-resident after
+                              all); the kernel drained, x is unreliable   */
 };
 
 /* Largest state_size accepted by any entry point. */

@@ -71,7 +71,7 @@ def test_bdmv_thread_count_invariance(gpu, monkeypatch):
     bit-identical for every workgroup size."""
     S, v = random_case(9, 5, 14, 40, np.float32)
     outs = []
-    for nt in (64, 128, 256, 512):
+    for nt in (64, 128, 192, 256):
         monkeypatch.setenv("GLASS_AMD_BDMV_THREADS", str(nt))
         say("bdmv threads=%d" % nt)
         outs.append(bdmv_gpu(gpu, S, v, 14, 40))
