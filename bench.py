@@ -13,13 +13,29 @@ its own roofline and CPU-oracle baseline.
 Inputs are generated once, copied to HBM, and reused; each timed PCG step
 starts from its own copy of x0 = 0 (prepared before the timed region), so no
 step starts from an already-converged x.
+
+Roofline: ``achieved`` = algorithmic bytes per launch / mean launch duration
+(HIP events around each launch on the stream the library launches on).
+``traffic`` = HBM bytes per launch of the workload's kernel measured by the
+rocprofv3 FETCH_SIZE / WRITE_SIZE counters and calibrated against a copy of
+known size; it is read from ``profiles/hbm_traffic.md`` and reported only
+while the kernel sources still hash to the value recorded there (else null).
+
+Other modes:
+  --calibration-copy     also run a 1 GiB negation (read 1 GiB, write 1 GiB)
+                         whose counters calibrate FETCH_SIZE / WRITE_SIZE
+  --summarize-pmc F W    turn the two counter CSVs of rocprofv3 runs (F:
+                         FETCH_SIZE, W: WRITE_SIZE) into profiles/hbm_traffic.md
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +47,34 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, vendor peak
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+CALIBRATION_BYTES = 1 << 30
+METRIC = "PCG solves/sec (batched) and bdmv HBM GB/s as fraction of MI355X peak"
+
+# The kernel each workload spends its time in (a substring of the demangled
+# name rocprofv3 reports).
+KERNEL_OF = {
+    "pcg0": "pcg_batched_kernel<float, 6,",
+    "bdmv1": "bdmv_kernel<float, 14>",
+    "pcg2": "pcg_batched_kernel<float, 14,",
+    "pcg3": "pcg_batched_kernel<float, 21,",
+    "grid4": "pcg_grid_kernel<double, 12,",
+}
+CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4}
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the HIP sources and the C ABI header (sorted by name)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_tridiagonal_pcg_bdmv_amd", "csrc")
+    files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
+                   if f.endswith((".hip", ".hpp")))
+    files.append(os.path.join(ROOT, "include", "glass_amd.h"))
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def algorithmic_bytes_pcg(w, iters: np.ndarray, resident: bool) -> float:
@@ -70,12 +114,113 @@ def time_cpu(fn, budget_s: float):
             return el / calls, calls
 
 
+# --------------------------------------------------------------------------
+# measured HBM traffic (profiles/hbm_traffic.md)
+# --------------------------------------------------------------------------
+
+def read_traffic():
+    """{kernel key: calibrated bytes per dispatch} if the recorded source hash
+    matches the current sources, else {}."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return {}
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[0] in KERNEL_OF:
+            try:
+                out[cells[0]] = float(cells[5])
+            except ValueError:
+                pass
+    return out
+
+
+def _counter_rows(path):
+    """(kernel name, counter name, value) per row of a rocprofv3 counter CSV."""
+    with open(path, newline="") as f:
+        rd = csv.DictReader(f)
+        cols = rd.fieldnames or []
+        kcol = next(c for c in cols if c.lower() == "kernel_name")
+        ncol = next(c for c in cols if c.lower() == "counter_name")
+        vcol = next(c for c in cols if c.lower() == "counter_value")
+        dcol = next((c for c in cols if c.lower() == "dispatch_id"), None)
+        for row in rd:
+            yield row[kcol], row[ncol], float(row[vcol]), (row[dcol] if dcol else None)
+
+
+def _per_dispatch(path, counter):
+    """{kernel name: [value per dispatch]} (values of one dispatch summed over
+    counter instances)."""
+    acc = {}
+    for kname, cname, val, did in _counter_rows(path):
+        if cname != counter:
+            continue
+        acc.setdefault((kname, did), 0.0)
+        acc[(kname, did)] += val
+    out = {}
+    for (kname, _), v in acc.items():
+        out.setdefault(kname, []).append(v)
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd):
+    fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(write_csv, "WRITE_SIZE")
+
+    def find(table, sub):
+        hits = [k for k in table if sub in k]
+        if len(hits) != 1:
+            raise SystemExit("expected one kernel matching %r, found %s" % (sub, hits))
+        return float(np.mean(table[hits[0]])), len(table[hits[0]])
+
+    cal_f, _ = find(fetch, "neg_kernel")
+    cal_w, _ = find(write, "neg_kernel")
+    fr = CALIBRATION_BYTES / (cal_f * 1024.0)
+    fw = CALIBRATION_BYTES / (cal_w * 1024.0)
+    lines = [
+        "# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE)",
+        "",
+        "kernel source sha256: %s" % kernel_source_hash(),
+        "",
+        "FETCH_SIZE run: `%s`" % fetch_cmd,
+        "",
+        "WRITE_SIZE run: `%s`" % write_cmd,
+        "",
+        "Calibration: a negation kernel reading and writing %d bytes reads "
+        "FETCH_SIZE = %.1f KiB and WRITE_SIZE = %.1f KiB per dispatch, so "
+        "bytes = FETCH_SIZE KiB x 1024 x %.4f + WRITE_SIZE KiB x 1024 x %.4f."
+        % (CALIBRATION_BYTES, cal_f, cal_w, fr, fw),
+        "",
+        "| workload | kernel | dispatches | FETCH_SIZE KiB/dispatch | "
+        "WRITE_SIZE KiB/dispatch | calibrated bytes/dispatch |",
+        "|---|---|---|---|---|---|",
+    ]
+    for key, sub in KERNEL_OF.items():
+        try:
+            f, nd = find(fetch, sub)
+            wv, _ = find(write, sub)
+        except SystemExit:
+            continue
+        b = f * 1024.0 * fr + wv * 1024.0 * fw
+        lines.append("| %s | %s | %d | %.1f | %.1f | %.0f |" % (key, sub, nd, f, wv, b))
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
+
 class Timer:
     """HIP events on the stream the library launches on (torch's current
-    stream): per-launch durations plus the whole timed region."""
+    stream): per-launch durations inside the timed region."""
 
     def __init__(self, torch, steps):
-        self.torch = torch
         self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                    for _ in range(steps)]
 
@@ -83,7 +228,15 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.ev]
 
 
-def bench_pcg(torch, glass, cfg, steps, warmup, cpu_budget, with_cpu):
+def roofline(nbytes, avg_ms, traffic):
+    achieved = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "algorithmic_bytes_per_launch": nbytes}
+
+
+def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
+    cfg = CONFIG_OF[key]
     w = workloads.CONFIGS[cfg]
     inp = workloads.generate(w)
     dev = torch.device("cuda:0")
@@ -93,7 +246,7 @@ def bench_pcg(torch, glass, cfg, steps, warmup, cpu_budget, with_cpu):
     B = w.n_problems
     xs = [torch.zeros((B, w.n), dtype=S.dtype, device=dev) for _ in range(steps + warmup)]
     iters = torch.zeros(B, dtype=torch.int32, device=dev)
-    grid = cfg == 4
+    grid = w.kind == "grid"
     if grid:
         ws = torch.empty(glass.pcg_grid_workspace_bytes(w.ss, w.kp, S.dtype),
                          dtype=torch.uint8, device=dev)
@@ -122,14 +275,12 @@ def bench_pcg(torch, glass, cfg, steps, warmup, cpu_budget, with_cpu):
     nbytes = algorithmic_bytes_pcg(w, it, resident)
     out = {
         "workload": w.name, "kind": "grid_pcg" if grid else "batched_pcg",
-        "dtype": np.dtype(w.dtype).name, "state_size": w.ss, "knot_points": w.kp,
-        "n_problems": B, "solves_per_s": B * steps / wall, "ms_per_step": wall * 1e3 / steps,
-        "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
+        "kernel": KERNEL_OF[key], "dtype": np.dtype(w.dtype).name, "state_size": w.ss,
+        "knot_points": w.kp, "n_problems": B, "solves_per_s": B * steps / wall,
+        "ms_per_step": wall * 1e3 / steps, "kernel_ms_avg": avg_ms,
+        "kernel_ms_min": float(np.min(launch_ms)),
         "iterations": {str(k): int(v) for k, v in zip(*np.unique(it, return_counts=True))},
-        "roofline": {"bound": "hbm", "achieved": nbytes / (avg_ms * 1e-3) / 1e9,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": nbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
     }
     if grid:
         out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it[0]))
@@ -145,7 +296,7 @@ def bench_pcg(torch, glass, cfg, steps, warmup, cpu_budget, with_cpu):
     return out
 
 
-def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu):
+def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu, traffic):
     w = workloads.CONFIGS[1]
     inp = workloads.generate(w)
     dev = torch.device("cuda:0")
@@ -167,14 +318,11 @@ def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu):
     avg_ms = float(np.mean(launch_ms))
     nbytes = algorithmic_bytes_bdmv(w, w.n_problems)
     out = {
-        "workload": w.name, "kind": "bdmv", "dtype": "float32", "state_size": w.ss,
-        "knot_points": w.kp, "n_problems": w.n_problems,
+        "workload": w.name, "kind": "bdmv", "kernel": KERNEL_OF["bdmv1"], "dtype": "float32",
+        "state_size": w.ss, "knot_points": w.kp, "n_problems": w.n_problems,
         "gb_per_s": nbytes / (wall / steps) / 1e9, "ms_per_step": wall * 1e3 / steps,
         "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
-        "roofline": {"bound": "hbm", "achieved": nbytes / (avg_ms * 1e-3) / 1e9,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": nbytes / (avg_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None, "algorithmic_bytes_per_launch": nbytes},
+        "roofline": roofline(nbytes, avg_ms, traffic.get("bdmv1")),
     }
     if with_cpu:
         import oracle
@@ -189,20 +337,39 @@ def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu):
     return out
 
 
+def calibration_copy(torch):
+    """A plain streaming kernel of known traffic: y = -x over 1 GiB (reads
+    1 GiB, writes 1 GiB).  Its counters calibrate FETCH_SIZE / WRITE_SIZE."""
+    dev = torch.device("cuda:0")
+    x = torch.ones(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads", default="all",
-                    help="comma list of pcg0,bdmv1,pcg2,pcg3,grid4 or 'all' / 'primary'")
+                    help="comma list of pcg0,bdmv1,pcg2,pcg3,grid4 or 'all'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--cpu-budget", type=float, default=4.0,
                     help="seconds of oracle time per workload baseline")
+    ap.add_argument("--calibration-copy", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--pmc-commands", nargs=2, default=("?", "?"),
+                    metavar=("FETCH_CMD", "WRITE_CMD"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], *args.pmc_commands)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(problems are independent; see the sharding note in DESIGN.md)", file=sys.stderr)
+              "(problems are independent; DESIGN.md describes how it would shard)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -210,31 +377,30 @@ def main():
     glass.load()
     torch.cuda.set_device(0)
 
-    names = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4}
-    if args.workloads == "all":
-        sel = list(names)
-    elif args.workloads == "primary":
-        sel = ["pcg3"]
-    else:
-        sel = [s.strip() for s in args.workloads.split(",") if s.strip()]
+    sel = list(CONFIG_OF) if args.workloads == "all" else \
+        [s.strip() for s in args.workloads.split(",") if s.strip()]
     with_cpu = not args.no_cpu
+    traffic = read_traffic()
     res = {}
     for name in sel:
         print("[bench] %s ..." % name, file=sys.stderr, flush=True)
-        if names[name] == 1:
-            res[name] = bench_bdmv(torch, glass, args.steps, args.warmup, args.cpu_budget, with_cpu)
+        if name == "bdmv1":
+            res[name] = bench_bdmv(torch, glass, args.steps, args.warmup, args.cpu_budget,
+                                   with_cpu, traffic)
         else:
-            # the primary workload gets the larger CPU budget (10 s)
+            # the headline workload gets the larger CPU budget (10 s)
             budget = max(args.cpu_budget, 10.0) if name == "pcg3" else args.cpu_budget
-            res[name] = bench_pcg(torch, glass, names[name], args.steps, args.warmup, budget,
-                                  with_cpu)
+            res[name] = bench_pcg(torch, glass, name, args.steps, args.warmup, budget,
+                                  with_cpu, traffic)
         print("[bench] %s done: %s" % (name, json.dumps(res[name])[:300]), file=sys.stderr,
               flush=True)
+    if args.calibration_copy:
+        calibration_copy(torch)
 
     head = res.get("pcg3") or next(iter(res.values()))
     w = workloads.CONFIGS[3]
     line = {
-        "metric": "PCG solves/sec (batched) and bdmv HBM GB/s as fraction of MI355X peak",
+        "metric": METRIC,
         "value": head.get("solves_per_s", head.get("gb_per_s")),
         "unit": "solves/s" if "solves_per_s" in head else "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -23,7 +23,9 @@ __all__ = [
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libglass_amd.so")
+# GLASS_AMD_LIBRARY points at another build of the same library (for A/B
+# timing of build options); the default is the in-tree build.
+_LIB_PATH = os.environ.get("GLASS_AMD_LIBRARY") or os.path.join(_HERE, "libglass_amd.so")
 _lib = None
 _lock = threading.Lock()
 

@@ -33,29 +33,35 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, build_dir: str, extra) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src)[:-4] + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s%s" % (src, r.stdout, r.stderr))
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
+    """Compile every source and link ``out`` (default: the in-tree library).
+    ``defines``: extra ``NAME=VALUE`` preprocessor definitions (build options
+    such as GLASS_AMD_RING_DEPTH)."""
+    extra = ["-D" + d for d in defines]
+    build_dir = BUILD if not defines else BUILD + "_" + "_".join(
+        d.replace("=", "") for d in defines)
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), srcs))
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s%s" % (r.stdout, r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB, file=sys.stderr)
-    return LIB
+        print("built", out, file=sys.stderr)
+    return out
 
 
 if __name__ == "__main__":

@@ -15,8 +15,9 @@
 // 3*ss-strided per-row reads into coalesced 16-byte loads.  For the
 // specialised state sizes every load of the tile is issued before the first
 // LDS store (ceil(3*ss*sizeof(T)/16) vectors per thread in flight), through a
-// buffer resource over exactly the tile's bytes, so lanes past the end read
-// zeros without branching.  The tile height is chosen so that the rows of a
+// buffer resource over exactly the tile's bytes: the hardware range-checks
+// raw buffer loads per dword, so a tile ending inside a vector still arrives
+// whole and lanes past the end read zeros, without branching.  The tile height is chosen so that the rows of a
 // problem split into tiles with as little of a ragged last tile as possible.
 #include <climits>
 
@@ -66,13 +67,6 @@ bdmv_kernel(T* __restrict__ y, const T* __restrict__ S,
     vec16_t* s4 = reinterpret_cast<vec16_t*>(s_mat);
 #pragma unroll
     for (int u = 0; u < U; ++u) s4[tid + u * NT] = t[u];
-    // A ragged tile may end inside a vector: those elements directly, after
-    // every vector store (the condition is uniform over the workgroup).
-    if ((count * (int)sizeof(T)) % 16 != 0) {
-      __syncthreads();
-      const int nv = count * (int)sizeof(T) / 16;
-      for (int e = nv * (16 / (int)sizeof(T)) + tid; e < count; e += NT) s_mat[e] = gS[e];
-    }
   } else {
     copy_to_lds<true>(s_mat, gS, rows * W, tid, NT, vec != 0);
     for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];

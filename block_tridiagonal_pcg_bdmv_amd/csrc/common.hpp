@@ -102,7 +102,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 typedef float vec16_t __attribute__((ext_vector_type(4)));  // 16-byte bit copy
 
 // Buffer resource over `nbytes` bytes at `base` (raw addressing, gfx9
-// descriptor word 3).  Loads through it past `nbytes` return zeros.
+// descriptor word 3).  Raw buffer loads are range-checked per dword: dwords
+// at or past `nbytes` read as zero and touch no memory.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int nbytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes,

@@ -22,22 +22,33 @@
 //   decision are computed identically (same bits) by every thread and need no
 //   broadcast.  Two slot arrays alternate so one barrier per dot suffices.
 // * matrices: RESIDENT -- each lane holds its S row and Pinv row in VGPRs,
-//   loaded once straight from HBM with every load of both rows in flight;
+//   loaded once: coalesced 16-byte loads of the wave's 64-row chunks (all in
+//   flight), transposed into rows through a per-wave LDS stage;
 //   STREAMED -- every matvec re-stages the wave's 64-row chunk of S or
 //   Pinv HBM/L2 -> LDS (coalesced 16-byte loads) and each lane multiplies its
-//   row from there.  With PREFETCH, the loads of the wave's next chunk in
-//   the fixed sequence (chunks of S, then of Pinv, then of S, ...) are issued
-//   into registers before the current chunk is multiplied, so they stay in
-//   flight across the multiply, the dots and the workgroup barriers (matrix
-//   loads never depend on the vectors).
+//   row from there.  With PREFETCH, the wave's next two chunks in the fixed
+//   sequence (chunks of S, then of Pinv, then of S, ...) are loaded into
+//   registers ahead of use, so they stay in flight across the multiply, the
+//   dots and the workgroup barriers (matrix loads never depend on the
+//   vectors).
 // Barriers per iteration: 4 (p^T Sp, r publish, r^T z, p publish).
+#include <cstdio>
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
 
+// Chunks a wave keeps in flight in the prefetching placement (1 or 2).
+#ifndef GLASS_AMD_RING_DEPTH
+#define GLASS_AMD_RING_DEPTH 1
+#endif
+
 namespace glass {
 namespace {
+
+constexpr int kRingDepth = GLASS_AMD_RING_DEPTH;
+static_assert(kRingDepth == 1 || kRingDepth == 2, "ring depth must be 1 or 2");
 
 template <typename T>
 struct PcgArgs {
@@ -60,19 +71,20 @@ struct PcgArgs {
 // Placements of the matrices (see the header).
 enum Mode { kResident = 0, kStreamPrefetch = 1, kStream = 2 };
 
-// Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for 3-4
-// rows per lane, which covers problems of 1537-2048 rows per wave group;
-// 16 waves otherwise (rows beyond 4096 need them, at the cost of spills).
-constexpr int max_threads_for(int rpt) { return (rpt == 3 || rpt == 4) ? 512 : 1024; }
+// Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for the
+// prefetching placement (two chunk buffers per lane) and for 3-4 rows per
+// lane; 16 waves otherwise (rows beyond 4096 need them, at the cost of
+// spills).
+constexpr int max_threads_for(int rpt, int mode) {
+  return (mode == kStreamPrefetch || rpt == 3 || rpt == 4) ? 512 : 1024;
+}
 
 template <typename T, int SS, int RPT, int MODE>
-__global__ void __launch_bounds__(max_threads_for(RPT))
+__global__ void __launch_bounds__(max_threads_for(RPT, MODE))
 pcg_batched_kernel(PcgArgs<T> a) {
   constexpr bool RES = MODE == kResident;
   constexpr bool PFM = MODE == kStreamPrefetch;
   constexpr int WC = SS > 0 ? 3 * SS : 1;  // compile-time width
-  // 16-byte vectors one lane moves per 64-row chunk (PREFETCH).
-  constexpr int PF = PFM ? (WC * (int)sizeof(T) + 15) / 16 : 1;
   const int ss = SS > 0 ? SS : a.ss;
   const int W = 3 * ss;
   const int kp = a.kp;
@@ -81,7 +93,9 @@ pcg_batched_kernel(PcgArgs<T> a) {
   const int NT = blockDim.x;
   const int NW = NT >> 6;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  // The wave index is uniform within a wave; saying so keeps everything
+  // derived from it (chunk rows, buffer resources) in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const long long prob = blockIdx.x;
   const long long mstride = (long long)n * W;
   const T* __restrict__ gS = a.S + prob * mstride;
@@ -107,60 +121,85 @@ pcg_batched_kernel(PcgArgs<T> a) {
     wstart[k] = br * ss;  // window start in a padded vector
   }
 
-  // Matrix rows in registers (RESIDENT only): every load of both rows is in
-  // flight at once.
+  // Chunk k of this wave: rows [r0, r0 + nrows) of a matrix, which are one
+  // contiguous range of count = nrows * W elements.
+  auto chunk_r0 = [&](int k) { return (wave + k * NW) * 64; };
+
+  // Buffer-load the wave's chunk k of gM as 16-byte vectors in the coalesced
+  // order (lane l gets vectors l, l+64, ...).  The resource spans exactly the
+  // chunk's bytes and the hardware range-checks raw buffer loads per dword:
+  // dwords past the end read as zeros without touching memory, so a chunk
+  // that ends inside a vector still arrives whole, no lane branches, and one
+  // offset register serves every load.  A chunk this wave does not have
+  // (r0 >= n) becomes an empty resource: the loads return zeros.
+  constexpr int NV = (WC * (int)sizeof(T) + 15) / 16;  // vectors per lane
+  auto load_chunk = [&](vec16_t (&buf)[NV], const T* __restrict__ gM, int k) {
+    const int r0 = chunk_r0(k);
+    const bool has = r0 < n;
+    const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gM + (long long)r0 * W : gM, nbytes);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) buf[u] = buffer_load16(rs, (lane + u * kWave) * 16);
+  };
+  // Write a loaded chunk into the wave's LDS stage (same layout as in HBM; the
+  // stage holds NV*64 vectors, so every store is in bounds).
+  auto stage_chunk = [&](const vec16_t (&buf)[NV]) {
+    vec16_t* __restrict__ d4 = reinterpret_cast<vec16_t*>(stage);
+#pragma unroll
+    for (int u = 0; u < NV; ++u) d4[lane + u * kWave] = buf[u];
+  };
+
+  // RESIDENT: each lane's S and Pinv rows in registers for the whole solve,
+  // loaded straight from HBM with every load of both rows in flight.
   T mS[RES ? RPT : 1][WC], mP[RES ? RPT : 1][WC];
   if constexpr (RES) {
+    static_assert(!RES || RPT == 1, "resident placement deals one row per lane");
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
-#pragma unroll
-      for (int c = 0; c < WC; ++c) {
-        mS[k][c] = T(0);
-        mP[k][c] = T(0);
-      }
-      if (valid[k]) {
-        const long long off = (long long)row[k] * WC;
-        if (vec) {
-          load_row_regs<T, WC, true>(mS[k], gS + off);
-          load_row_regs<T, WC, true>(mP[k], gP + off);
-        } else {
-          load_row_regs<T, WC, false>(mS[k], gS + off);
-          load_row_regs<T, WC, false>(mP[k], gP + off);
-        }
+    for (int c = 0; c < WC; ++c) {
+      mS[0][c] = T(0);
+      mP[0][c] = T(0);
+    }
+    if (valid[0]) {
+      const long long off = (long long)row[0] * WC;
+      if (vec) {
+        load_row_regs<T, WC, true>(mS[0], gS + off);
+        load_row_regs<T, WC, true>(mP[0], gP + off);
+      } else {
+        load_row_regs<T, WC, false>(mS[0], gS + off);
+        load_row_regs<T, WC, false>(mP[0], gP + off);
       }
     }
   }
 
-  // PREFETCH: pf holds the wave's next chunk (64 rows) as 16-byte vectors in
-  // the coalesced order (lane l holds vectors l, l+64, ...).  The loads are
-  // buffer loads over exactly the chunk's bytes: a vector past its end reads
-  // zeros instead of touching memory beyond the matrix, so no lane branches
-  // and one offset register serves all of them.  The LDS stage holds PF*64
-  // vectors; stores past the chunk land in its padding.
-  vec16_t pf[PF];
-  auto issue = [&](const T* __restrict__ gM, int k) {
-    const int r0 = (wave + k * NW) * 64;
-    const int nbytes = min(64, n - r0) * W * (int)sizeof(T);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(gM + (long long)r0 * W, nbytes);
-#pragma unroll
-    for (int u = 0; u < PF; ++u) pf[u] = buffer_load16(rs, (lane + u * kWave) * 16);
+  // PREFETCH: a two-deep ring of chunk buffers.  The wave walks the fixed
+  // sequence of positions pos = m*RPT + k (m = 0 for S, 1 for Pinv; matvecs
+  // alternate S, Pinv, S, ...), and position pos lives in buffer pos % 2.
+  // After staging position pos it loads position pos + 2 (mod 2*RPT) into
+  // the buffer it just emptied, so two chunks are in flight while the wave
+  // multiplies, reduces and waits at barriers.  Every position is loaded
+  // (empty for a chunk the wave does not have), so the loads form one
+  // unbranched in-order stream and each staging waits only for its own
+  // buffer.
+  vec16_t pf0[PFM ? NV : 1], pf1[PFM ? NV : 1];
+  auto ring_load = [&](int pos) {
+    if constexpr (PFM) {
+      const int m = pos / RPT, k = pos % RPT;
+      const T* gM = m == 0 ? gS : gP;
+      if constexpr (kRingDepth == 1) {
+        load_chunk(pf0, gM, k);
+      } else {
+        if (pos % 2 == 0) load_chunk(pf0, gM, k);
+        else load_chunk(pf1, gM, k);
+      }
+    }
   };
-  auto stage_from_pf = [&](const T* __restrict__ gM, int k) {
-    const int r0 = (wave + k * NW) * 64;
-    const int count = min(64, n - r0) * W;
-    const int nv = count * (int)sizeof(T) / 16;
-    vec16_t* __restrict__ d4 = reinterpret_cast<vec16_t*>(stage);
-#pragma unroll
-    for (int u = 0; u < PF; ++u) d4[lane + u * kWave] = pf[u];
-    // A ragged last chunk may end inside a vector: those elements directly.
-    for (int e = nv * (16 / (int)sizeof(T)) + lane; e < count; e += kWave)
-      stage[e] = gM[(long long)r0 * W + e];
-  };
-  if constexpr (PFM) issue(gS, 0);  // the first matvec is S x0
 
   // out[k] = (M * vpad)[row k]: one lane, one row, serial 3*ss contraction.
-  auto matvec = [&](T (&out)[RPT], const T* __restrict__ gM,
-                    T (&mreg)[RES ? RPT : 1][WC], const T* __restrict__ vpad) {
+  // MI selects the matrix: 0 = S, 1 = Pinv.
+  auto matvec = [&](auto mi_tag, T (&out)[RPT], T (&mreg)[RES ? RPT : 1][WC],
+                    const T* __restrict__ vpad) {
+    constexpr int MI = decltype(mi_tag)::value;
+    const T* __restrict__ gM = MI == 0 ? gS : gP;
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       T acc = T(0);
@@ -171,20 +210,27 @@ pcg_batched_kernel(PcgArgs<T> a) {
           for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], w[c], acc);
         }
       } else {
-        const int chunk = wave + k * NW;
-        const int r0 = chunk * 64;
+        const int r0 = chunk_r0(k);
+        if constexpr (PFM) {
+          constexpr int pos = MI * RPT;  // + k, below
+          if (r0 < n) {  // wave-uniform
+            if constexpr (kRingDepth == 1) {
+              stage_chunk(pf0);
+            } else {
+              if ((pos + k) % 2 == 0) stage_chunk(pf0);
+              else stage_chunk(pf1);
+            }
+          }
+          // Keep the next loads after these LDS stores, so the emptied
+          // buffer's registers are reused (the compiler would otherwise
+          // hoist the loads and hold an extra chunk).
+          asm volatile("" ::: "memory");
+          // Position pos + depth goes into this position's buffer, whether
+          // or not this position had a chunk for this wave.
+          ring_load((pos + k + kRingDepth) % (2 * RPT));
+        }
         if (r0 < n) {  // wave-uniform
-          if constexpr (PFM) {
-            stage_from_pf(gM, k);
-            // Keep the next loads after these LDS stores, so one chunk's
-            // registers serve both (the compiler would otherwise hoist the
-            // loads and hold two chunks).
-            asm volatile("" ::: "memory");
-            // Next chunk in the sequence: this matrix's next chunk of this
-            // wave, else chunk 0 of the other matrix (matvecs alternate).
-            if (k + 1 < RPT && (wave + (k + 1) * NW) * 64 < n) issue(gM, k + 1);
-            else issue(gM == gS ? gP : gS, 0);
-          } else {
+          if constexpr (!PFM) {
             const int nrows = min(64, n - r0);
             copy_to_lds<false>(stage, gM + (long long)r0 * W, nrows * W, lane, kWave, vec);
           }
@@ -209,8 +255,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
       out[k] = acc;
     }
   };
+  using MatS = std::integral_constant<int, 0>;
+  using MatP = std::integral_constant<int, 1>;
 
   // Initial state: p_pad temporarily holds x0 (the vector S multiplies).
+  // x0 and b are loaded before the first matrix chunks so that waiting for
+  // them does not wait for the chunks too (loads complete in order).
   T xr[RPT], rr[RPT], pr[RPT], tmp[RPT];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
@@ -219,9 +269,15 @@ pcg_batched_kernel(PcgArgs<T> a) {
     if (valid[k]) {
       xr[k] = a.x[prob * n + row[k]];
       tmp[k] = a.b[prob * n + row[k]];
-      p_pad[ss + row[k]] = xr[k];
     }
   }
+  if constexpr (PFM) {
+    ring_load(0);
+    if (kRingDepth == 2) ring_load(1 % (2 * RPT));
+  }
+#pragma unroll
+  for (int k = 0; k < RPT; ++k)
+    if (valid[k]) p_pad[ss + row[k]] = xr[k];
   for (int e = tid; e < ss; e += NT) {
     p_pad[e] = T(0);
     p_pad[(kp + 1) * ss + e] = T(0);
@@ -231,14 +287,14 @@ pcg_batched_kernel(PcgArgs<T> a) {
   __syncthreads();
 
   T sv[RPT];
-  matvec(sv, gS, mS, p_pad);  // S x0
+  matvec(MatS{}, sv, mS, p_pad);  // S x0
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     rr[k] = valid[k] ? tmp[k] - sv[k] : T(0);
     if (valid[k]) r_pad[ss + row[k]] = rr[k];
   }
   __syncthreads();
-  matvec(sv, gP, mP, r_pad);  // z = Pinv r
+  matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
   T part = T(0);
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
@@ -257,7 +313,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     status = GLASS_PCG_CONVERGED;
   } else {
     for (int it = 0; it < a.max_iters; ++it) {
-      matvec(sv, gS, mS, p_pad);  // Sp
+      matvec(MatS{}, sv, mS, p_pad);  // Sp
       part = T(0);
 #pragma unroll
       for (int k = 0; k < RPT; ++k) part = fma(pr[k], sv[k], part);
@@ -275,7 +331,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
       }
       iters = it + 1;
       __syncthreads();
-      matvec(sv, gP, mP, r_pad);  // z = Pinv r
+      matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
       part = T(0);
 #pragma unroll
       for (int k = 0; k < RPT; ++k) part = fma(rr[k], sv[k], part);
@@ -337,8 +393,26 @@ constexpr bool kResidentFits(int ss) {
   return 6 * ss * (int)sizeof(T) / 4 <= 96;
 }
 
+// Streamed with prefetch: specialised sizes whose 64-row chunk is at most 16
+// 16-byte vectors per lane.
 template <typename T>
-bool make_plan(int ss, int kp, bool res_available, size_t lds_max, Plan* plan) {
+constexpr bool kPrefetchFits(int ss) {
+  return 3 * ss * (int)sizeof(T) <= 256;
+}
+
+// Elements of one wave's LDS stage for the prefetching placement: a whole
+// number of 16-byte vectors per lane.
+template <typename T>
+int prefetch_stage_elems(int ss) {
+  const int nv = (3 * ss * (int)sizeof(T) + 15) / 16;
+  return nv * 64 * 16 / (int)sizeof(T);
+}
+
+// res_available: specialised size (resident rows possible); prefetch: the
+// prefetching streamed placement is allowed (specialised, 16-byte aligned).
+template <typename T>
+bool make_plan(int ss, int kp, bool res_available, bool prefetch, size_t lds_max,
+               Plan* plan) {
   const int n = kp * ss;
   const int W = 3 * ss;
   const int nchunks = (n + 63) / 64;
@@ -350,35 +424,43 @@ bool make_plan(int ss, int kp, bool res_available, size_t lds_max, Plan* plan) {
     p.RPT = 1;
     p.res = true;
     p.stage_elems = 0;
-    p.lds = lds_bytes<T>(ss, kp, p.NW, p.stage_elems);
+    p.lds = lds_bytes<T>(ss, kp, p.NW, 0);
     if (p.lds <= lds_max) {
       *plan = p;
       return true;
     }
   }
-  // Streamed: the fewest idle chunk slots, then the most waves.
-  bool found = false;
-  Plan best;
-  int best_waste = 1 << 30;
-  for (int rpt : kRptChoices) {
-    const int NW = (nchunks + rpt - 1) / rpt;
-    if (NW * 64 > max_threads_for(rpt)) continue;
-    const int stage = 64 * W;
-    const size_t lds = lds_bytes<T>(ss, kp, NW, stage);
-    if (lds > lds_max) continue;
-    const int waste = NW * rpt - nchunks;
-    if (!found || waste < best_waste || (waste == best_waste && NW > best.NW)) {
-      found = true;
-      best_waste = waste;
-      best.NW = NW;
-      best.RPT = rpt;
-      best.res = false;
-      best.stage_elems = stage;
-      best.lds = lds;
+  // Streamed: the fewest idle chunk slots, then the most waves.  The
+  // prefetching placement is tried first; without it, plain staging.
+  for (int pf = prefetch ? 1 : 0; pf >= 0; --pf) {
+    const int mode = pf ? kStreamPrefetch : kStream;
+    bool found = false;
+    Plan best;
+    int best_waste = 1 << 30;
+    for (int rpt : kRptChoices) {
+      const int NW = (nchunks + rpt - 1) / rpt;
+      if (NW * 64 > max_threads_for(rpt, mode)) continue;
+      const int stage = pf ? prefetch_stage_elems<T>(ss) : 64 * W;
+      const size_t lds = lds_bytes<T>(ss, kp, NW, stage);
+      if (lds > lds_max) continue;
+      const int waste = NW * rpt - nchunks;
+      if (!found || waste < best_waste || (waste == best_waste && NW > best.NW)) {
+        found = true;
+        best_waste = waste;
+        best.NW = NW;
+        best.RPT = rpt;
+        best.res = false;
+        best.prefetch = pf != 0;
+        best.stage_elems = stage;
+        best.lds = lds;
+      }
+    }
+    if (found) {
+      *plan = best;
+      return true;
     }
   }
-  if (found) *plan = best;
-  return found;
+  return false;
 }
 
 template <typename T, int SS, int RPT, int MODE>
@@ -391,18 +473,19 @@ int launch_one(const PcgArgs<T>& a, int n_problems, const Plan& pl,
                                        (int)pl.lds);
     if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(pcg)");
   }
+  if (env_int("GLASS_AMD_VERBOSE", 0) > 0) {
+    int per_cu = 0;
+    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, pl.NW * 64, pl.lds);
+    std::fprintf(stderr,
+                 "glass pcg plan: ss=%d kp=%d mode=%d waves=%d rows/lane=%d "
+                 "lds=%zu stage=%d workgroups/CU=%d\n",
+                 a.ss, a.kp, MODE, pl.NW, RPT, pl.lds, a.stage_elems, per_cu);
+  }
   hipLaunchKernelGGL(kern, dim3((unsigned)n_problems), dim3(pl.NW * 64), pl.lds,
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "pcg launch");
   return GLASS_OK;
-}
-
-// Streamed with prefetch: specialised sizes whose 64-row chunk is at most 16
-// 16-byte vectors per lane.
-template <typename T>
-constexpr bool kPrefetchFits(int ss) {
-  return 3 * ss * (int)sizeof(T) <= 256;
 }
 
 template <typename T, int SS, int MODE>
@@ -436,15 +519,19 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
+  const long long n = (long long)kp * ss;
+  const bool vec = aligned(S, 16) && aligned(P, 16) &&
+                   ((n * 3 * ss * (long long)sizeof(T)) % 16 == 0);
+  const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
+                        std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
   Plan pl;
-  if (!make_plan<T>(ss, kp, specialised, dev.max_lds_per_block, &pl))
+  if (!make_plan<T>(ss, kp, specialised, prefetch, dev.max_lds_per_block, &pl))
     return fail(GLASS_EUNSUPPORTED,
                 "pcg: problem too large for one workgroup (rows or LDS)");
   if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl.res) {
     Plan alt;
-    if (make_plan<T>(ss, kp, false, dev.max_lds_per_block, &alt)) pl = alt;
+    if (make_plan<T>(ss, kp, false, prefetch, dev.max_lds_per_block, &alt)) pl = alt;
   }
-  const long long n = (long long)kp * ss;
   PcgArgs<T> a;
   a.x = x;
   a.S = S;
@@ -458,25 +545,8 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.max_iters = max_iters;
   a.rel_tol = (T)rel_tol;
   a.abs_tol = (T)abs_tol;
-  a.vec = aligned(S, 16) && aligned(P, 16) &&
-          ((n * 3 * ss * (long long)sizeof(T)) % 16 == 0);
+  a.vec = vec;
   a.stage_elems = pl.stage_elems;
-  pl.prefetch = !pl.res && specialised && a.vec &&
-                3 * ss * (int)sizeof(T) <= 256 &&
-                std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
-  if (pl.prefetch) {
-    // The stage holds a whole number of 16-byte vectors per lane.
-    const int pf = (3 * ss * (int)sizeof(T) + 15) / 16;
-    const int stage = pf * 64 * 16 / (int)sizeof(T);
-    const size_t lds = lds_bytes<T>(ss, kp, pl.NW, stage);
-    if (lds <= dev.max_lds_per_block) {
-      pl.stage_elems = stage;
-      pl.lds = lds;
-      a.stage_elems = stage;
-    } else {
-      pl.prefetch = false;
-    }
-  }
   switch (ss) {
     case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
     case 12: return launch_ss<T, 12>(a, n_problems, pl, st);

@@ -231,7 +231,8 @@ pcg_grid_kernel(GridArgs<T> a) {
   const int G = a.G;
   const int NT = blockDim.x;
   const int NW = NT >> 6;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
   const int bid = blockIdx.x;
   const int g = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
   const int A = (int)((long long)g * kp / G);

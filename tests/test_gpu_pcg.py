@@ -56,22 +56,30 @@ def test_pcg_streamed_and_resident_agree(gpu, monkeypatch):
     np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-5 * np.abs(a[0]).max())
 
 
-@pytest.mark.parametrize("ss,kp,B,margin", [(1, 1, 4, 0.5), (1, 700, 3, 0.3),
-                                            (2, 4, 5, 0.3), (5, 9, 6, 0.2),
-                                            (6, 1, 3, 0.5), (7, 150, 3, 0.2),
-                                            (14, 50, 4, 0.2), (21, 20, 3, 0.1),
-                                            (33, 10, 2, 0.2), (64, 5, 2, 0.3)])
-def test_pcg_generic_shapes(gpu, ss, kp, B, margin):
+@pytest.mark.parametrize("ss,kp,B,margin,dtype", [
+    (1, 1, 4, 0.5, np.float32), (1, 700, 3, 0.3, np.float32),
+    (2, 4, 5, 0.3, np.float32), (5, 9, 6, 0.2, np.float32),
+    (6, 1, 3, 0.5, np.float32), (7, 150, 3, 0.2, np.float32),
+    (14, 50, 4, 0.2, np.float32), (33, 10, 2, 0.2, np.float32),
+    (64, 5, 2, 0.3, np.float32),
+    # streamed with the two-deep prefetch ring: 1, 2, 4 and 8 chunks per
+    # wave, ragged last chunks, and float64
+    (21, 20, 3, 0.1, np.float32), (21, 40, 2, 0.1, np.float32),
+    (6, 200, 2, 0.3, np.float32), (12, 300, 2, 0.2, np.float32),
+    (21, 100, 1, 0.1, np.float32), (6, 200, 2, 0.3, np.float64),
+])
+def test_pcg_generic_shapes(gpu, ss, kp, B, margin, dtype):
     """Specialised and runtime state sizes, ragged last chunk, kp = 1, several
-    rows per lane (n up to 700), resident and streamed placements."""
+    rows per lane (n up to 3600), resident and streamed placements."""
     rng = np.random.default_rng(ss * 100 + kp)
-    S, D = workloads.random_spd_strips(rng, B, ss, kp, margin, np.float32)
-    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, np.float32),
-           "b": rng.standard_normal((B, kp * ss)).astype(np.float32),
-           "x0": np.zeros((B, kp * ss), np.float32)}
-    say("pcg ss=%d kp=%d B=%d" % (ss, kp, B))
-    res = pcg_gpu(gpu, inp, ss, kp, 300, 1e-8, 0.0)
-    assert_pcg_parity(inp, ss, kp, 300, 1e-8, 0.0, res, np.float32)
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, margin, dtype)
+    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
+           "b": rng.standard_normal((B, kp * ss)).astype(dtype),
+           "x0": np.zeros((B, kp * ss), dtype)}
+    rel = 1e-8 if dtype == np.float32 else 1e-14
+    say("pcg ss=%d kp=%d B=%d %s" % (ss, kp, B, np.dtype(dtype).name))
+    res = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0)
+    assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, res, dtype)
 
 
 def test_pcg_nonzero_initial_guess_and_block_tridiagonal_pinv(gpu):
@@ -148,3 +156,16 @@ def test_pcg_rejects_inconsistent_buffers(gpu):
     with pytest.raises(TypeError):
         gpu.pcg_batched(t["x0"], t["S"], t["Pinv"], t["b"], w.ss, w.kp, 10, 1e-6, 0.0,
                         it.to(torch.int64))
+
+
+def test_pcg_prefetch_ring_matches_plain_staging(gpu, monkeypatch):
+    """The prefetching and the plain streamed placements stage the same bytes
+    and run the same arithmetic in the same order: bit-identical outputs."""
+    w = workloads.CONFIGS[3]
+    inp = workloads.generate(w, n_problems=10)
+    say("pcg cfg3 prefetch vs plain staging")
+    a = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_PREFETCH", "1")
+    b = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    for u, v in zip(a, b):
+        np.testing.assert_array_equal(u, v)
