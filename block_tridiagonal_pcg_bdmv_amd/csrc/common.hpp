@@ -182,6 +182,13 @@ __device__ __forceinline__ void load_row_regs(T (&reg)[W], const T* __restrict__
   }
 }
 
+// Round-to-nearest a*b as its own operation (never fused into a later add).
+template <typename T>
+__device__ __forceinline__ T mul_unfused(T a, T b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
 // Round-to-nearest a*b + c with two roundings (no contraction), for the few
 // scalar decisions that must match a reference that never fuses.
 template <typename T>

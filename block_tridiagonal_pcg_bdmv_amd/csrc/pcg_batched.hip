@@ -17,10 +17,12 @@
 // * only p and r must be seen by other lanes (the 3*ss matvec window), so
 //   they are the two padded vectors kept in LDS; the page's other work
 //   vectors stay in registers.
-// * dots: per-lane partial -> wave64 DPP tree -> one LDS slot per wave ->
-//   every thread adds the slots in wave order, so alpha, beta and the stopping
-//   decision are computed identically (same bits) by every thread and need no
-//   broadcast.  Two slot arrays alternate so one barrier per dot suffices.
+// * dots: each 64-row chunk's products -> wave64 DPP tree -> one LDS slot per
+//   chunk -> every thread adds the slots in chunk order.  alpha, beta and the
+//   stopping decision are therefore computed identically (same bits) by every
+//   thread and need no broadcast, and the whole solve is bit-identical for
+//   every placement (number of waves, rows per lane, resident or streamed).
+//   Two slot arrays alternate so one barrier per dot suffices.
 // * matrices: RESIDENT -- each lane holds its S row and Pinv row in VGPRs,
 //   loaded once: coalesced 16-byte loads of the wave's 64-row chunks (all in
 //   flight), transposed into rows through a per-wave LDS stage;
@@ -105,9 +107,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   T* p_pad = reinterpret_cast<T*>(smem_raw);
   T* r_pad = p_pad + pad_len;
-  T* slotA = r_pad + pad_len;
-  T* slotB = slotA + NW;
-  const size_t head = ((size_t)(2 * pad_len + 2 * NW) * sizeof(T) + 15) & ~(size_t)15;
+  const int nchunks = (n + 63) / 64;
+  T* slotA = r_pad + pad_len;  // [nchunks] per-chunk dot partials
+  T* slotB = slotA + nchunks;
+  const size_t head = ((size_t)(2 * pad_len + 2 * nchunks) * sizeof(T) + 15) & ~(size_t)15;
   T* stage = reinterpret_cast<T*>(smem_raw + head) + (size_t)wave * a.stage_elems;
 
   // Row bookkeeping.
@@ -258,6 +261,27 @@ pcg_batched_kernel(PcgArgs<T> a) {
   using MatS = std::integral_constant<int, 0>;
   using MatP = std::integral_constant<int, 1>;
 
+  // Dot product of two row-distributed vectors, independent of the launch
+  // shape: each 64-row chunk's products go through the fixed wave64 tree
+  // into its own LDS slot, and every thread adds the slots in chunk order.
+  // The result has the same bits in every thread and for every placement
+  // (waves, rows per lane, resident or streamed).  One __syncthreads();
+  // the two slot arrays alternate so a read of one use never meets a write
+  // of the next.
+  auto chunk_dot = [&](const T (&u)[RPT], const T (&v)[RPT], T* slots) {
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      if (chunk_r0(k) < n) {  // wave-uniform
+        const T c = wave_sum(mul_unfused(u[k], v[k]));
+        if (lane == 0) slots[wave + k * NW] = c;
+      }
+    }
+    __syncthreads();
+    T s = slots[0];
+    for (int c = 1; c < nchunks; ++c) s = s + slots[c];
+    return s;
+  };
+
   // Initial state: p_pad temporarily holds x0 (the vector S multiplies).
   // x0 and b are loaded before the first matrix chunks so that waiting for
   // them does not wait for the chunks too (loads complete in order).
@@ -295,14 +319,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
   }
   __syncthreads();
   matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
-  T part = T(0);
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     pr[k] = sv[k];
     if (valid[k]) p_pad[ss + row[k]] = pr[k];  // p = z (x0 reads are done)
-    part = fma(rr[k], sv[k], part);
   }
-  T rho = block_sum(part, slotA, NW);  // also publishes p_pad
+  T rho = chunk_dot(rr, sv, slotA);  // also publishes p_pad
   const T rho0 = rho;
   const T rho_init = fabs(rho);
   const T thresh = mul_add_unfused(a.rel_tol, rho_init, a.abs_tol);
@@ -314,10 +336,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   } else {
     for (int it = 0; it < a.max_iters; ++it) {
       matvec(MatS{}, sv, mS, p_pad);  // Sp
-      part = T(0);
-#pragma unroll
-      for (int k = 0; k < RPT; ++k) part = fma(pr[k], sv[k], part);
-      const T pSp = block_sum(part, slotB, NW);
+      const T pSp = chunk_dot(pr, sv, slotB);
       if (!(pSp > T(0)) || !is_finite_val(pSp)) {
         status = GLASS_PCG_BREAKDOWN;
         break;
@@ -332,10 +351,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
       iters = it + 1;
       __syncthreads();
       matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
-      part = T(0);
-#pragma unroll
-      for (int k = 0; k < RPT; ++k) part = fma(rr[k], sv[k], part);
-      const T rz = block_sum(part, slotA, NW);
+      const T rz = chunk_dot(rr, sv, slotA);
       rho_last = rz;
       if (fabs(rz) < thresh) {
         status = GLASS_PCG_CONVERGED;
@@ -380,7 +396,8 @@ struct Plan {
 
 template <typename T>
 size_t lds_bytes(int ss, int kp, int NW, int stage_elems) {
-  const size_t head = ((size_t)(2 * (kp + 2) * ss + 2 * NW) * sizeof(T) + 15) & ~(size_t)15;
+  const size_t nchunks = ((size_t)kp * ss + 63) / 64;
+  const size_t head = ((size_t)(2 * (kp + 2) * ss + 2 * nchunks) * sizeof(T) + 15) & ~(size_t)15;
   return head + (size_t)NW * stage_elems * sizeof(T);
 }
 
@@ -432,12 +449,16 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, size_t lds_max
   }
   // Streamed: the fewest idle chunk slots, then the most waves.  The
   // prefetching placement is tried first; without it, plain staging.
+  // GLASS_AMD_PCG_RPT forces the rows per lane of the streamed placements
+  // (tests and tuning; an impossible value leaves no plan).
+  const int forced_rpt = env_int("GLASS_AMD_PCG_RPT", 0);
   for (int pf = prefetch ? 1 : 0; pf >= 0; --pf) {
     const int mode = pf ? kStreamPrefetch : kStream;
     bool found = false;
     Plan best;
     int best_waste = 1 << 30;
     for (int rpt : kRptChoices) {
+      if (forced_rpt > 0 && rpt != forced_rpt) continue;
       const int NW = (nchunks + rpt - 1) / rpt;
       if (NW * 64 > max_threads_for(rpt, mode)) continue;
       const int stage = pf ? prefetch_stage_elems<T>(ss) : 64 * W;

@@ -42,18 +42,27 @@ def test_pcg_fp64(gpu, cfg):
     run_workload(gpu, cfg, n_problems=17, dtype=np.float64)
 
 
-def test_pcg_streamed_and_resident_agree(gpu, monkeypatch):
-    """The register-resident and the streamed kernels run the same steps; only
-    the summation tree of the dots may differ, so both meet the bars."""
+def test_pcg_placements_bit_identical(gpu, monkeypatch):
+    """Thread-count invariance: the dots add fixed 64-row chunk partials in
+    chunk order and every row is contracted serially in index order, so the
+    register-resident placement and the streamed placements at 1, 2, 3, 4
+    and 8 rows per lane (1 to 7 waves) give the same bits."""
     w = workloads.CONFIGS[2]
     inp = workloads.generate(w, n_problems=24)
-    a = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, ref, np.float32)
     monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
-    say("pcg cfg2 forced streamed")
-    b = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
-    for res in (a, b):
-        assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float32)
-    np.testing.assert_allclose(a[0], b[0], rtol=0, atol=1e-5 * np.abs(a[0]).max())
+    for rpt in ("1", "2", "3", "4", "8"):
+        for pf in ("0", "1"):
+            monkeypatch.setenv("GLASS_AMD_PCG_RPT", rpt)
+            if pf == "0":
+                monkeypatch.setenv("GLASS_AMD_PCG_NO_PREFETCH", "1")
+            else:
+                monkeypatch.delenv("GLASS_AMD_PCG_NO_PREFETCH", raising=False)
+            say("pcg cfg2 streamed rows/lane=%s prefetch=%s" % (rpt, pf))
+            got = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+            for u, v in zip(ref, got):
+                np.testing.assert_array_equal(u, v)
 
 
 @pytest.mark.parametrize("ss,kp,B,margin,dtype", [
