@@ -17,6 +17,11 @@ Solves"):
 * ``dense_expand`` -- the n x n matrix the strips stand for (same layout
   section); used to pin ``bdmv`` against a plain dense product.
 * ``cholesky_solve`` -- a dense SPD solve, used to pin ``pcg`` on tiny systems.
+* ``bdsv`` -- the direct solve of the same page's opening paragraph
+  (glass::bdsv), whose steps the page does not give: block elimination
+  without pivoting across block-rows (block Thomas; Golub and Van Loan,
+  "Matrix Computations", section 4.5.1), each pivot block factored by
+  Cholesky.
 
 Pins: every function is checked in ``tests/test_oracle.py`` against something
 other than itself (hand-derived fixtures under ``tests/golden/``, a dense
@@ -70,6 +75,10 @@ def _load():
             for name in ("oracle_pcg_f64", "oracle_pcg_f32"):
                 f = getattr(lib, name)
                 f.argtypes = [P, P, P, P, I, I, LL, I, D, D, P, P, P, I]
+                f.restype = None
+            for name in ("oracle_bdsv_f64", "oracle_bdsv_f32"):
+                f = getattr(lib, name)
+                f.argtypes = [P, P, P, I, I, LL, P, I]
                 f.restype = None
             lib.oracle_dense_expand.argtypes = [P, P, I, I]
             lib.oracle_dense_expand.restype = None
@@ -135,6 +144,23 @@ def pcg(x0, S, Pinv, b, ss: int, kp: int, max_iters: int, rel_tol: float,
        float(rel_tol), float(abs_tol), _ptr(iters), _ptr(status), _ptr(rho),
        nthreads)
     return x, iters, status, rho
+
+
+def bdsv(S, b, ss: int, kp: int, precision: str = "f64", nthreads: int = 1, x=None):
+    """Batched direct solve S x = b.  Returns (x, status): status 0, or 1 when
+    a pivot block is not numerically SPD (that problem's x is left as given,
+    zeros by default)."""
+    dt = np.float64 if precision == "f64" else np.float32
+    n = kp * ss
+    b = _c(b, dt).reshape(-1, n)
+    B = b.shape[0]
+    S = _c(S, dt).reshape(B, -1)
+    assert S.shape[1] == n * 3 * ss, "S has the wrong per-problem size"
+    x = np.zeros((B, n), dtype=dt) if x is None else _c(x, dt).reshape(B, n).copy()
+    status = np.zeros(B, dtype=np.int32)
+    fn = _load().oracle_bdsv_f64 if dt == np.float64 else _load().oracle_bdsv_f32
+    fn(_ptr(x), _ptr(S), _ptr(b), ss, kp, B, _ptr(status), nthreads)
+    return x, status
 
 
 def dense_expand(S, ss: int, kp: int) -> np.ndarray:

@@ -21,6 +21,11 @@
 // standard preconditioned CG (Hestenes and Stiefel 1952; Saad, "Iterative
 // Methods for Sparse Linear Systems", Algorithm 9.1), whose initialisation
 // z = p = Pinv*r the page names in section "Matvec -- glass::bdmv".
+// The page's opening paragraph also names glass::bdsv, a direct solve of the
+// same block-tridiagonal SPD systems, without giving its steps; the oracle
+// follows block Gaussian elimination without pivoting across block-rows (the
+// block Thomas algorithm; Golub and Van Loan, "Matrix Computations", section
+// 4.5.1 on block tridiagonal systems), each pivot block factored by Cholesky.
 //
 // No blocking, fusion or reordering: every sum runs sequentially in index
 // order.  Build with -ffp-contract=off so a*b+c is never fused.
@@ -141,6 +146,108 @@ PcgOut pcg_one(T* x, const T* S, const T* Pinv, const T* b, int ss, int kp,
   return out;
 }
 
+// ---------------------------------------------------------------------------
+// Small dense helpers for bdsv (row-major m x m blocks).
+// ---------------------------------------------------------------------------
+
+// In-place Cholesky M = C C^T (Cholesky-Banachiewicz, lower triangle of M
+// receives C; the strict upper triangle is left alone).  Returns false if a
+// pivot is not positive (M not numerically SPD).
+template <typename T>
+bool chol_inplace(T* M, int m) {
+  for (int i = 0; i < m; ++i) {
+    for (int j = 0; j <= i; ++j) {
+      T s = M[i * m + j];
+      for (int k = 0; k < j; ++k) s = s - M[i * m + k] * M[j * m + k];
+      if (i == j) {
+        if (!(s > T(0))) return false;
+        M[i * m + i] = std::sqrt(s);
+      } else {
+        M[i * m + j] = s / M[j * m + j];
+      }
+    }
+  }
+  return true;
+}
+
+// X := (C C^T)^{-1} X for an m x ncol block X (row stride ncol), C from
+// chol_inplace: forward substitution with C, then back substitution with C^T,
+// column by column.
+template <typename T>
+void chol_solve_cols(const T* C, int m, T* X, int ncol) {
+  for (int j = 0; j < ncol; ++j) {
+    for (int i = 0; i < m; ++i) {  // C y = x
+      T s = X[i * ncol + j];
+      for (int k = 0; k < i; ++k) s = s - C[i * m + k] * X[k * ncol + j];
+      X[i * ncol + j] = s / C[i * m + i];
+    }
+    for (int i = m - 1; i >= 0; --i) {  // C^T x = y
+      T s = X[i * ncol + j];
+      for (int k = i + 1; k < m; ++k) s = s - C[k * m + i] * X[k * ncol + j];
+      X[i * ncol + j] = s / C[i * m + i];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bdsv on one problem: S x = b by block elimination (block Thomas), in
+// precision T.  With block-row br holding [L_br | D_br | R_br]:
+//   M_0 = D_0,                u_0 = M_0^{-1} b_0
+//   G_{br-1} = M_{br-1}^{-1} R_{br-1}
+//   M_br = D_br - L_br G_{br-1},   u_br = M_br^{-1} (b_br - L_br u_{br-1})
+//   x_{kp-1} = u_{kp-1},   x_br = u_br - G_br x_{br+1}
+// Every M_br (a Schur complement of the SPD matrix) is factored by Cholesky.
+// Returns 0, or 1 if some M_br is not numerically SPD (x is then unchanged).
+// ---------------------------------------------------------------------------
+template <typename T>
+int bdsv_one(T* x, const T* S, const T* b, int ss, int kp) {
+  const int width = 3 * ss;
+  auto blk = [&](int br, int which, int i, int j) {  // which: 0 L, 1 D, 2 R
+    return S[((size_t)br * ss + i) * width + which * ss + j];
+  };
+  // G and u of every block-row, stored side by side: [G_br | u_br], ss x (ss+1)
+  const int nc = ss + 1;
+  std::vector<T> GU((size_t)kp * ss * nc, T(0));
+  std::vector<T> M((size_t)ss * ss);
+  for (int br = 0; br < kp; ++br) {
+    T* gu = GU.data() + (size_t)br * ss * nc;
+    // M_br = D_br - L_br G_{br-1};  rhs = b_br - L_br u_{br-1}
+    for (int i = 0; i < ss; ++i) {
+      for (int j = 0; j < ss; ++j) M[i * ss + j] = blk(br, 1, i, j);
+      gu[i * nc + ss] = b[(size_t)br * ss + i];
+    }
+    if (br > 0) {
+      const T* prev = GU.data() + (size_t)(br - 1) * ss * nc;
+      for (int i = 0; i < ss; ++i) {
+        for (int j = 0; j < nc; ++j) {
+          T s = T(0);
+          for (int k = 0; k < ss; ++k) s = s + blk(br, 0, i, k) * prev[k * nc + j];
+          if (j < ss) M[i * ss + j] = M[i * ss + j] - s;
+          else gu[i * nc + ss] = gu[i * nc + ss] - s;
+        }
+      }
+    }
+    if (!chol_inplace(M.data(), ss)) return 1;
+    // [G_br | u_br] = M_br^{-1} [R_br | rhs]   (no R for the last block-row)
+    for (int i = 0; i < ss; ++i)
+      for (int j = 0; j < ss; ++j) gu[i * nc + j] = br + 1 < kp ? blk(br, 2, i, j) : T(0);
+    chol_solve_cols(M.data(), ss, gu, nc);
+  }
+  // Back substitution, from the last block-row up.
+  std::vector<T> xv((size_t)kp * ss);
+  for (int br = kp - 1; br >= 0; --br) {
+    const T* gu = GU.data() + (size_t)br * ss * nc;
+    for (int i = 0; i < ss; ++i) {
+      T s = gu[i * nc + ss];
+      if (br + 1 < kp)
+        for (int k = 0; k < ss; ++k) s = s - gu[i * nc + k] * xv[(size_t)(br + 1) * ss + k];
+      xv[(size_t)br * ss + i] = s;
+    }
+  }
+  for (size_t i = 0; i < xv.size(); ++i) x[i] = xv[i];
+  return 0;
+}
+
 // Run f(lo, hi) over [0, count) split into contiguous ranges on nthreads.
 template <typename F>
 void parallel_ranges(long long count, int nthreads, F f) {
@@ -189,6 +296,18 @@ void pcg_batched(T* x, const T* S, const T* Pinv, const T* b, int ss, int kp,
   });
 }
 
+template <typename T>
+void bdsv_batched(T* x, const T* S, const T* b, int ss, int kp,
+                  long long n_problems, int* status_out, int nthreads) {
+  const size_t strip = (size_t)kp * ss * 3 * ss, n = (size_t)kp * ss;
+  parallel_ranges(n_problems, nthreads, [=](long long lo, long long hi) {
+    for (long long q = lo; q < hi; ++q) {
+      const int st = bdsv_one<T>(x + q * n, S + q * strip, b + q * n, ss, kp);
+      if (status_out) status_out[q] = st;
+    }
+  });
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,6 +340,19 @@ void oracle_pcg_f32(float* x, const float* S, const float* Pinv,
                     int nthreads) {
   pcg_batched<float>(x, S, Pinv, b, ss, kp, n_problems, max_iters, rel_tol,
                      abs_tol, iters_out, status_out, rho_out, nthreads);
+}
+
+// x: [n_problems][kp*ss] solution of S x = b (left unchanged for a problem
+// whose status is 1: a pivot block not numerically SPD); status: int32
+// [n_problems] or NULL.
+void oracle_bdsv_f64(double* x, const double* S, const double* b, int ss,
+                     int kp, long long n_problems, int* status_out,
+                     int nthreads) {
+  bdsv_batched<double>(x, S, b, ss, kp, n_problems, status_out, nthreads);
+}
+void oracle_bdsv_f32(float* x, const float* S, const float* b, int ss, int kp,
+                     long long n_problems, int* status_out, int nthreads) {
+  bdsv_batched<float>(x, S, b, ss, kp, n_problems, status_out, nthreads);
 }
 
 // The dense n x n matrix (n = kp*ss, row-major) that one problem's strips

@@ -409,3 +409,120 @@ def test_pcg_threads_bitwise_equal():
                    w.max_iters, w.rel_tol, w.abs_tol, "f32", nthreads=3)
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+# ---------------------------------------------------------------------------
+# bdsv (direct solve)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["bdsv_ss2_kp3.txt", "bdsv_tridiag_ss1_kp5.txt"])
+def test_bdsv_golden_hand_examples(name):
+    """Systems whose solution was chosen and whose right-hand side was
+    multiplied out by hand: catches L/R swapped, a wrong Schur complement
+    sign, off-matrix blocks leaking in, or a broken back substitution."""
+    g = read_golden(name)
+    ss, kp = int(g["ss"][0]), int(g["kp"][0])
+    S = frac_array(g["S"]).reshape(1, -1)
+    b = frac_array(g["b"]).reshape(1, -1)
+    x, st = oracle.bdsv(S, b, ss, kp, "f64")
+    assert st[0] == 0
+    np.testing.assert_allclose(x[0], frac_array(g["x"]), rtol=0, atol=1e-13)
+    x32, st = oracle.bdsv(S.astype(np.float32), b.astype(np.float32), ss, kp, "f32")
+    np.testing.assert_allclose(x32[0], frac_array(g["x"]), rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("embedding", ["ss1", "ss2"])
+def test_bdsv_golden_2x2(embedding):
+    """A^-1 b = [1/11, 7/11] for the 2x2 system of the CG fixture, in both
+    block embeddings."""
+    g = read_golden("cg_2x2.txt")
+    S, _, ss, kp = _cg2x2_problem(embedding)
+    x, st = oracle.bdsv(S, frac_array(g["b"])[None], ss, kp)
+    assert st[0] == 0
+    np.testing.assert_allclose(x[0], frac_array(g["identity.x2"]), rtol=1e-15, atol=1e-16)
+
+
+@pytest.mark.parametrize("ss,kp", [(1, 1), (1, 9), (2, 4), (3, 1), (5, 6), (7, 3)])
+def test_bdsv_matches_dense_solves(ss, kp):
+    """Random SPD systems (the workload recipe) against numpy's LU solve and
+    the dense Cholesky solve of the expanded matrix."""
+    rng = np.random.default_rng(ss * 31 + kp)
+    B = 4
+    S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.2)
+    b = rng.standard_normal((B, kp * ss))
+    x, st = oracle.bdsv(S, b, ss, kp, nthreads=2)
+    assert np.all(st == 0)
+    for q in range(B):
+        A = oracle.dense_expand(S[q], ss, kp)
+        np.testing.assert_allclose(x[q], np.linalg.solve(A, b[q]), rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(x[q], oracle.cholesky_solve(A, b[q]), rtol=1e-11, atol=1e-12)
+
+
+def test_bdsv_symmetric_blocks_from_arbitrary_L():
+    """Any symmetric block-tridiagonal SPD matrix (here from random L blocks,
+    R_br = L_{br+1}^T, heavy D): catches a Schur complement built with R^T
+    where L belongs, or G taken from the wrong block-row."""
+    rng = np.random.default_rng(11)
+    ss, kp = 3, 5
+    L, D, _ = _random_blocks(rng, ss, kp)
+    D = D @ np.swapaxes(D, -1, -2) + 12 * np.eye(ss)
+    R = np.zeros_like(L)
+    R[:-1] = np.swapaxes(L[1:], -1, -2)
+    L[0] = 5.0   # off-matrix, must be ignored
+    R[-1] = -5.0
+    S = _strips_from_blocks(L, D, R)[None]
+    b = rng.standard_normal((1, kp * ss))
+    x, st = oracle.bdsv(S, b, ss, kp)
+    assert st[0] == 0
+    L[0] = 0.0
+    R[-1] = 0.0
+    np.testing.assert_allclose(x[0], np.linalg.solve(_dense_from_blocks(L, D, R), b[0]),
+                               rtol=1e-11, atol=1e-12)
+
+
+def test_bdsv_block_diagonal_and_identity():
+    """R = L = 0 decouples into ss x ss solves; D = I returns b."""
+    rng = np.random.default_rng(4)
+    ss, kp = 4, 3
+    S, D = workloads.random_spd_strips(rng, 1, ss, kp, 0.5, offdiag=False)
+    b = rng.standard_normal((1, kp * ss))
+    x, _ = oracle.bdsv(S, b, ss, kp)
+    for br in range(kp):
+        np.testing.assert_allclose(x[0, br * ss:(br + 1) * ss],
+                                   np.linalg.solve(D[0, br], b[0, br * ss:(br + 1) * ss]),
+                                   rtol=1e-12)
+    I = workloads.identity_pinv(1, ss, kp)
+    x, _ = oracle.bdsv(I, b, ss, kp)
+    np.testing.assert_array_equal(x, b)
+
+
+def test_bdsv_not_spd_status_leaves_x():
+    rng = np.random.default_rng(6)
+    ss, kp = 3, 4
+    S, _ = workloads.random_spd_strips(rng, 2, ss, kp, 0.3)
+    S[1] = -S[1]
+    b = rng.standard_normal((2, kp * ss))
+    x0 = np.full((2, kp * ss), 7.0)
+    x, st = oracle.bdsv(S, b, ss, kp, x=x0)
+    assert list(st) == [0, 1]
+    np.testing.assert_array_equal(x[1], x0[1])
+
+
+def test_bdsv_agrees_with_converged_pcg():
+    """The direct and the iterative solve of the same SPD systems meet."""
+    w = workloads.CONFIGS[0]
+    inp = workloads.generate(w, n_problems=6)
+    S64, P64, b64 = (inp[k].astype(np.float64) for k in ("S", "Pinv", "b"))
+    xd, st = oracle.bdsv(S64, b64, w.ss, w.kp)
+    xp, it, _, _ = oracle.pcg(np.zeros_like(b64), S64, P64, b64, w.ss, w.kp, 500, 1e-26, 0.0)
+    assert np.all(st == 0)
+    np.testing.assert_allclose(xd, xp, rtol=1e-10, atol=1e-12)
+
+
+def test_bdsv_f32_close_to_f64():
+    w = workloads.CONFIGS[2]
+    inp = workloads.generate(w, n_problems=4)
+    x32, _ = oracle.bdsv(inp["S"], inp["b"], w.ss, w.kp, "f32")
+    x64, _ = oracle.bdsv(inp["S"].astype(np.float64), inp["b"].astype(np.float64), w.ss, w.kp)
+    rel = np.linalg.norm(x32 - x64, axis=1) / np.linalg.norm(x64, axis=1)
+    assert rel.max() < 1e-5
