@@ -8,7 +8,8 @@ the path (strip loads, matvecs, dots, fused updates, stopping test, write-back)
 for the whole batch.  The same run also times the other workloads (bdmv
 ss=14/kp=64/8192 problems, PCG ss=6/kp=32/64 and ss=14/kp=32/4096, and the
 grid-wide fp64 chain ss=12/kp=8192) and reports each under ``workloads`` with
-its own roofline and CPU-oracle baseline.
+its own roofline and CPU-oracle baseline, as does the direct solve
+(``glass_bdsv_batched``) of the ss=14/kp=32/4096 systems.
 
 Inputs are generated once, copied to HBM, and reused; each timed PCG step
 starts from its own copy of x0 = 0 (prepared before the timed region), so no
@@ -59,8 +60,11 @@ KERNEL_OF = {
     "pcg2": "pcg_batched_kernel<float, 14,",
     "pcg3": "pcg_batched_kernel<float, 21,",
     "grid4": "pcg_grid_kernel<double, 12,",
+    "bdsv2": "bdsv_kernel<float, 14>",
 }
-CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4}
+# Workload inputs: the five configurations; bdsv2 is the direct solve of the
+# same systems as pcg2 (ss=14, kp=32, 4096 problems).
+CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2}
 
 
 def kernel_source_hash() -> str:
@@ -337,6 +341,49 @@ def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu, traffic):
     return out
 
 
+def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
+    w = workloads.CONFIGS[CONFIG_OF[key]]
+    inp = workloads.generate(w, with_pinv=False)
+    dev = torch.device("cuda:0")
+    S = torch.from_numpy(inp["S"]).to(dev)
+    b = torch.from_numpy(inp["b"]).to(dev)
+    B = w.n_problems
+    x = torch.zeros((B, w.n), dtype=S.dtype, device=dev)
+    status = torch.zeros(B, dtype=torch.int32, device=dev)
+    for _ in range(warmup):
+        glass.bdsv_batched(x, S, b, w.ss, w.kp, status)
+    torch.cuda.synchronize()
+    tm = Timer(torch, steps)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        tm.ev[k][0].record()
+        glass.bdsv_batched(x, S, b, w.ss, w.kp, status)
+        tm.ev[k][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = tm.launch_ms()
+    avg_ms = float(np.mean(launch_ms))
+    es = np.dtype(w.dtype).itemsize
+    # S once, b read, x written, status
+    nbytes = float(B) * (w.n * 3 * w.ss * es + 2 * w.n * es + 4)
+    out = {
+        "workload": "bdsv_ss14_kp32_b4096_f32", "kind": "bdsv", "kernel": KERNEL_OF[key],
+        "dtype": np.dtype(w.dtype).name, "state_size": w.ss, "knot_points": w.kp,
+        "n_problems": B, "solves_per_s": B * steps / wall, "ms_per_step": wall * 1e3 / steps,
+        "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
+        "not_spd": int((status.cpu().numpy() != 0).sum()),
+        "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
+    }
+    if with_cpu:
+        import oracle
+        nt = cpu_threads()
+        sec, calls = time_cpu(lambda: oracle.bdsv(inp["S"], inp["b"], w.ss, w.kp, "f32", nt),
+                              cpu_budget)
+        out["cpu_baseline"] = {"value": B / sec, "unit": "solves/s", "cores": nt, "kind": "oracle",
+                               "sample": "the full %d-problem workload, %d repetitions" % (B, calls)}
+    return out
+
+
 def calibration_copy(torch):
     """A plain streaming kernel of known traffic: y = -x over 1 GiB (reads
     1 GiB, writes 1 GiB).  Its counters calibrate FETCH_SIZE / WRITE_SIZE."""
@@ -354,7 +401,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads", default="all",
-                    help="comma list of pcg0,bdmv1,pcg2,pcg3,grid4 or 'all'")
+                    help="comma list of pcg0,bdmv1,pcg2,pcg3,grid4,bdsv2 or 'all'")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--cpu-budget", type=float, default=4.0,
                     help="seconds of oracle time per workload baseline")
@@ -386,6 +433,9 @@ def main():
         print("[bench] %s ..." % name, file=sys.stderr, flush=True)
         if name == "bdmv1":
             res[name] = bench_bdmv(torch, glass, args.steps, args.warmup, args.cpu_budget,
+                                   with_cpu, traffic)
+        elif name == "bdsv2":
+            res[name] = bench_bdsv(torch, glass, name, args.steps, args.warmup, args.cpu_budget,
                                    with_cpu, traffic)
         else:
             # the headline workload gets the larger CPU budget (10 s)

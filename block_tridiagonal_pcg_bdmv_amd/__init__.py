@@ -18,8 +18,8 @@ import threading
 
 __all__ = [
     "GlassError", "load", "library_path", "bdmv_batched", "pcg_batched",
-    "pcg_grid", "pcg_grid_workspace_bytes", "CONVERGED", "MAX_ITERS",
-    "BREAKDOWN", "GRID_TIMEOUT",
+    "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "CONVERGED",
+    "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,7 @@ _lock = threading.Lock()
 
 GLASS_F32, GLASS_F64 = 0, 1
 CONVERGED, MAX_ITERS, BREAKDOWN, GRID_TIMEOUT = 0, 1, 2, 3
+BDSV_OK, BDSV_NOT_SPD = 0, 1
 
 
 class GlassError(RuntimeError):
@@ -59,6 +60,7 @@ def load():
             "glass_bdmv_batched": ([P, P, P, I, I, I, I, P], I),
             "glass_pcg_batched": ([P, P, P, P, I, I, I, I, D, D, P, I, P], I),
             "glass_pcg_batched_ex": ([P, P, P, P, I, I, I, I, D, D, P, P, P, I, P], I),
+            "glass_bdsv_batched": ([P, P, P, I, I, I, P, I, P], I),
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, P], I),
@@ -151,6 +153,22 @@ def pcg_batched(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int
                                      float(abs_tol), it, st, rh, _dtype_code(S),
                                      _stream(stream))
     _check(rc, "glass_pcg_batched_ex")
+
+
+def bdsv_batched(x, S, b, state_size: int, knot_points: int, status_out=None,
+                 stream=None):
+    """Direct solve S x = b per problem (page "Block-tridiagonal Solves",
+    glass::bdsv).  x, b: [B, kp*ss]; status_out int32 [B] (BDSV_OK or
+    BDSV_NOT_SPD; x is written only where it is BDSV_OK)."""
+    import torch
+    ss, kp = int(state_size), int(knot_points)
+    B = _problems(S, ss, kp)
+    dt = S.dtype
+    n = kp * ss
+    a = (_dev(x, "x", B * n, dt), _dev(S, "S", S.numel(), dt), _dev(b, "b", B * n, dt))
+    st = _dev(status_out, "status_out", B, torch.int32) if status_out is not None else None
+    rc = load().glass_bdsv_batched(*a, ss, kp, B, st, _dtype_code(S), _stream(stream))
+    _check(rc, "glass_bdsv_batched")
 
 
 def pcg_grid_workspace_bytes(state_size: int, knot_points: int, dtype) -> int:

@@ -151,6 +151,21 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
                               iters_out, nullptr, nullptr, dtype, hip_stream);
 }
 
+int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
+                       int knot_points, int n_problems, int* status_out,
+                       glass_dtype dtype, void* hip_stream) {
+  if (int rc = check_common(dtype, state_size, knot_points, n_problems)) return rc;
+  if (state_size > GLASS_BDSV_MAX_STATE_SIZE)
+    return fail(GLASS_EUNSUPPORTED, "bdsv: state_size above GLASS_BDSV_MAX_STATE_SIZE");
+  if (n_problems == 0) return GLASS_OK;  // nothing to do; pointers may be NULL
+  if (int rc = check_ptr(x, dtype, "x")) return rc;
+  if (int rc = check_ptr(S, dtype, "S")) return rc;
+  if (int rc = check_ptr(b, dtype, "b")) return rc;
+  if (status_out && !glass::aligned(status_out, 4)) return fail(GLASS_EINVAL, "status_out misaligned");
+  return glass::launch_bdsv(dtype, x, S, b, state_size, knot_points, n_problems,
+                            status_out, (hipStream_t)hip_stream);
+}
+
 size_t glass_pcg_grid_workspace_bytes(int state_size, int knot_points,
                                       glass_dtype dtype) {
   if (dtype != GLASS_F32 && dtype != GLASS_F64) return 0;

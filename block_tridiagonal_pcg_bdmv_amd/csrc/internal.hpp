@@ -38,6 +38,9 @@ int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
                        double abs_tol, int* iters, int* status, void* rho,
                        hipStream_t stream);
 
+int launch_bdsv(glass_dtype dt, void* x, const void* S, const void* b, int ss,
+                int kp, int n_problems, int* status, hipStream_t stream);
+
 size_t grid_workspace_bytes(int ss, int kp, glass_dtype dt);
 int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     const void* b, int ss, int kp, int max_iters,

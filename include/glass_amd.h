@@ -73,8 +73,17 @@ enum {
                               all); the kernel drained, x is unreliable   */
 };
 
+/* Per-problem outcome of glass_bdsv_batched written to status_out. */
+enum {
+  GLASS_BDSV_OK = 0,      /* solved                                           */
+  GLASS_BDSV_NOT_SPD = 1  /* a pivot block (Schur complement) is not
+                             numerically positive definite; x is unchanged   */
+};
+
 /* Largest state_size accepted by any entry point. */
 #define GLASS_MAX_STATE_SIZE 64
+/* Largest state_size accepted by glass_bdsv_batched. */
+#define GLASS_BDSV_MAX_STATE_SIZE 24
 
 /*
  * y = A_bd * v for n_problems independent matrices (page "Block-tridiagonal
@@ -146,6 +155,29 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
                       int* status_out, void* rho_out, void* workspace,
                       size_t workspace_bytes, glass_dtype dtype,
                       void* hip_stream);
+
+/*
+ * Direct solve S x = b for n_problems independent block-tridiagonal
+ * symmetric positive definite systems (glass::bdsv, named in the opening
+ * paragraph of page "Block-tridiagonal Solves"; layout as above).  Steps:
+ * block elimination without pivoting across block-rows,
+ *   [M_br | y_br] = [D_br | b_br] - L_br [G_{br-1} | u_{br-1}]   (br > 0),
+ *   [G_br | u_br] = M_br^{-1} [R_br | y_br]   (no R for the last block-row),
+ *   x_{kp-1} = u_{kp-1},  x_br = u_br - G_br x_{br+1},
+ * each pivot block M_br (a Schur complement, SPD when S is SPD) eliminated
+ * with positive diagonal pivots.  S must be symmetric (R_br = L_{br+1}^T);
+ * otherwise the result is unspecified.  L of the first and R of the last
+ * block-row are ignored.
+ * x, b: [n_problems][knot_points*state_size] (unpadded); x is written only
+ * for problems whose status is GLASS_BDSV_OK.  status_out: int32
+ * [n_problems] or NULL.
+ * Limits: state_size <= GLASS_BDSV_MAX_STATE_SIZE; one problem's
+ * knot_points*state_size*(state_size+1) elements must fit in LDS
+ * (GLASS_EUNSUPPORTED otherwise).
+ */
+int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
+                       int knot_points, int n_problems, int* status_out,
+                       glass_dtype dtype, void* hip_stream);
 
 /* Static text for a GLASS_* return code. */
 const char* glass_status_string(int status);

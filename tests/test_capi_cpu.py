@@ -102,3 +102,16 @@ def test_grid_argument_errors_and_workspace_size(lib):
     assert grid(ws_ptr=ctypes.c_void_p(0x100080)) == EINVAL  # not 256-aligned
     assert grid(ws_bytes=ws - 1) == EINVAL
     assert grid(it=-3) == EINVAL
+
+
+def test_bdsv_argument_errors(lib):
+    def bdsv(x=FAKE, S=FAKE, b=FAKE, ss=14, kp=32, B=1, st=None, dt=0):
+        return lib.glass_bdsv_batched(x, S, b, ss, kp, B, st, dt, None)
+    assert bdsv(x=None) == EINVAL
+    assert bdsv(S=None) == EINVAL
+    assert bdsv(b=ctypes.c_void_p(0x100001)) == EINVAL
+    assert bdsv(st=ctypes.c_void_p(0x100002)) == EINVAL
+    assert bdsv(ss=0) == EINVAL
+    assert bdsv(dt=3) == EINVAL
+    assert bdsv(ss=25) == EUNSUPPORTED  # above GLASS_BDSV_MAX_STATE_SIZE
+    assert bdsv(B=0) == 0
