@@ -11,17 +11,19 @@
 // positive marks the problem as not SPD (status 1, x left unchanged).
 //
 // Mapping on gfx950: one wave per problem (no workgroup barriers at all).
-// * The working block W = [M | R | y] (ss x (2ss+1)) lives in registers:
-//   lane l owns elements e = l, l+64, ... of W in row-major order.
-// * M^{-1} [R | y] comes from Gauss-Jordan elimination on W: ss steps; step k
-//   publishes row k and column k of W through LDS, every lane scales row k by
-//   1/pivot and eliminates column k from its other rows.  Three times fewer
-//   dependent steps than a Cholesky factorisation plus two triangular solves,
-//   and diagonal pivots are positive for SPD blocks, so no row exchanges.
+// * The working block W = [M | R | y] (ss x (2ss+1)) lives in registers, one
+//   column per lane: lane j holds W[0..ss)[j].
+// * M^{-1} [R | y] comes from Gauss-Jordan elimination on W: ss steps; in
+//   step k each lane already holds its row-k entry, and column k is read from
+//   lane k with readlane into scalar registers, so the elimination touches
+//   neither LDS nor memory.  Diagonal pivots are positive for SPD blocks, so
+//   no row exchanges; three times fewer dependent steps than a Cholesky
+//   factorisation plus two triangular solves.
 // * [G_br | u_br] of every block-row stays in LDS for the back substitution.
 // * The next block-row's strip (ss x 3ss, one contiguous range) is
 //   buffer-loaded into registers while the current block-row is eliminated,
-//   then staged into LDS for the L_br [G|u] product and the W fill.
+//   then staged into LDS, where every lane reads L_br by broadcast for the
+//   L_br [G|u] product.
 #include <climits>
 
 #include "common.hpp"
@@ -42,11 +44,7 @@ struct BdsvArgs {
   int strip_vecs;  // 16-byte vectors per lane for one strip (LDS stage)
 };
 
-// Registers per lane: elements of W (ss x (2ss+1)) and vectors of a strip.
-template <int SS>
-constexpr int w_slots() {
-  return (SS * (2 * SS + 1) + 63) / 64;
-}
+// 16-byte vectors per lane that hold one strip.
 template <typename T, int SS>
 constexpr int strip_slots() {
   return (3 * SS * SS * (int)sizeof(T) + 1023) / 1024;
@@ -55,12 +53,10 @@ constexpr int strip_slots() {
 template <typename T, int SS>
 __global__ void __launch_bounds__(64)
 bdsv_kernel(BdsvArgs<T> a) {
-  constexpr int ME = w_slots<SS>();
+  static_assert(2 * SS + 1 <= 64, "one lane per column of [M | R | y]");
   constexpr int NVS = strip_slots<T, SS>();
-  constexpr int ss = SS;
-  constexpr int NCW = 2 * SS + 1;  // columns of W
-  constexpr int NGU = SS + 1;      // columns of [G | u]
-  constexpr int SW = 3 * SS;       // strip row width
+  constexpr int NGU = SS + 1;  // columns of [G | u]
+  constexpr int SW = 3 * SS;   // strip row width
   const int kp = a.kp;
   const int lane = threadIdx.x;
   const long long prob = blockIdx.x;
@@ -69,23 +65,15 @@ bdsv_kernel(BdsvArgs<T> a) {
   T* stage = reinterpret_cast<T*>(smem_raw);            // strip: ss x 3ss (+pad)
   T* GU = stage + (size_t)NVS * 64 * (16 / sizeof(T));  // kp x ss x (ss+1)
   T* bv = GU + (size_t)kp * SS * NGU;                   // b_br (ss)
-  T* colbuf = bv + SS;                                  // column k of W (ss)
-  T* rowbuf = colbuf + SS;                              // row k of W (2ss+1)
-  T* xbuf = rowbuf + NCW;                               // x_{br+1} (ss)
+  T* xbuf = bv + SS;                                    // x_{br+1} (ss)
 
   const T* gS = a.S + prob * (long long)kp * SS * SW;
   const T* gb = a.b + prob * (long long)kp * SS;
 
-  // Element coordinates of this lane's slots of W.
-  int ei[ME], ej[ME];
-  bool own[ME];
-#pragma unroll
-  for (int m = 0; m < ME; ++m) {
-    const int e = lane + m * 64;
-    own[m] = e < SS * NCW;
-    ei[m] = own[m] ? e / NCW : 0;
-    ej[m] = own[m] ? e % NCW : 0;
-  }
+  // This lane's column of W: 0..ss-1 -> M (and G source column), ss..2ss-1
+  // -> R, 2ss -> y; lanes past 2ss hold zeros and take part harmlessly.
+  const int j = lane;
+  const bool is_m = j < SS, is_r = j >= SS && j < 2 * SS, is_y = j == 2 * SS;
 
   // Strip prefetch: block-row br of S as 16-byte vectors (buffer loads over
   // exactly its bytes; dwords past the end read as zero) and b_br.
@@ -100,7 +88,7 @@ bdsv_kernel(BdsvArgs<T> a) {
   };
   prefetch(0);
 
-  T w[ME];
+  T w[SS];  // column j of W
   bool fail = false;
   for (int br = 0; br < kp; ++br) {
     // Stage strip br and b_br; start loading strip br+1.
@@ -111,61 +99,45 @@ bdsv_kernel(BdsvArgs<T> a) {
     wave_lds_sync();
     if (br + 1 < kp) prefetch(br + 1);
 
-    // W = [D_br | R_br | b_br] - L_br [G_{br-1} | 0 | u_{br-1}].
-    const T* GUp = GU + (size_t)(br - 1) * SS * NGU;
+    // W = [D_br | R_br | b_br] - L_br [G_{br-1} | 0 | u_{br-1}], column j.
+    const int c = is_m ? j : SS;  // the column of [G | u] this lane needs
+    T gcol[SS];
 #pragma unroll
-    for (int m = 0; m < ME; ++m) {
-      const int i = ei[m], j = ej[m];
-      T v;
-      if (j < SS) v = stage[i * SW + SS + j];                           // D
-      else if (j < 2 * SS) v = br + 1 < kp ? stage[i * SW + j + SS] : T(0);  // R
-      else v = bv[i];                                                    // b
-      if (br > 0 && (j < SS || j == 2 * SS)) {
-        const int c = j < SS ? j : SS;  // column of [G | u]
+    for (int i = 0; i < SS; ++i) {
+      if (is_m) w[i] = stage[i * SW + SS + j];
+      else if (is_r) w[i] = br + 1 < kp ? stage[i * SW + SS + j] : T(0);  // R: cols 2ss..3ss
+      else if (is_y) w[i] = bv[i];
+      else w[i] = T(0);
+      gcol[i] = br > 0 ? GU[(size_t)(br - 1) * SS * NGU + i * NGU + c] : T(0);
+    }
+    if (br > 0 && (is_m || is_y)) {
 #pragma unroll
-        for (int k = 0; k < SS; ++k) v = fma(-stage[i * SW + k], GUp[k * NGU + c], v);
-      }
-      w[m] = own[m] ? v : T(0);
+      for (int i = 0; i < SS; ++i)
+#pragma unroll
+        for (int k = 0; k < SS; ++k) w[i] = fma(-stage[i * SW + k], gcol[k], w[i]);
     }
 
-    // Gauss-Jordan: W -> [I | M^{-1} R | M^{-1} y].
+    // Gauss-Jordan: W -> [I | M^{-1} R | M^{-1} y].  Column k comes from
+    // lane k (scalar registers); each lane's row-k entry is its own.
+#pragma unroll
     for (int k = 0; k < SS; ++k) {
-      wave_lds_sync();  // previous step's reads of colbuf/rowbuf are done
+      T ck[SS];
 #pragma unroll
-      for (int m = 0; m < ME; ++m) {
-        if (own[m] && ej[m] == k) colbuf[ei[m]] = w[m];
-        if (own[m] && ei[m] == k) rowbuf[ej[m]] = w[m];
-      }
-      wave_lds_sync();
-      // Every slot reads its row-k and column-k entries together with the
-      // pivot (one LDS round trip), then updates without branches.  Columns
-      // <= k are already eliminated and keep their values.
-      const T piv = colbuf[k];
-      T rv[ME], cv[ME];
+      for (int i = 0; i < SS; ++i) ck[i] = read_lane(w[i], k);
+      const T piv = ck[k];
+      fail = fail || !(piv > T(0)) || !is_finite_val(piv);
+      const T rk = w[k] / piv;
 #pragma unroll
-      for (int m = 0; m < ME; ++m) {
-        rv[m] = rowbuf[ej[m]];
-        cv[m] = colbuf[ei[m]];
-      }
-      if (!(piv > T(0)) || !is_finite_val(piv)) {
-        fail = true;
-        break;
-      }
-      const T inv = T(1) / piv;
-#pragma unroll
-      for (int m = 0; m < ME; ++m) {
-        const T rk = rv[m] * inv;
-        const T upd = ei[m] == k ? rk : fma(-cv[m], rk, w[m]);
-        w[m] = ej[m] > k ? upd : w[m];
-      }
+      for (int i = 0; i < SS; ++i) w[i] = i == k ? rk : fma(-ck[i], rk, w[i]);
     }
     if (fail) break;  // uniform over the wave
 
     // Keep [G_br | u_br] (columns ss .. 2ss of W).
-    T* GUc = GU + (size_t)br * SS * NGU;
+    if (is_r || is_y) {
+      T* GUc = GU + (size_t)br * SS * NGU + (j - SS);
 #pragma unroll
-    for (int m = 0; m < ME; ++m)
-      if (own[m] && ej[m] >= SS) GUc[ei[m] * NGU + (ej[m] - SS)] = w[m];
+      for (int i = 0; i < SS; ++i) GUc[i * NGU] = w[i];
+    }
     wave_lds_sync();
   }
 
@@ -198,8 +170,7 @@ int launch_typed(T* x, const T* S, const T* b, int kp, int n_problems, int* stat
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   constexpr int NVS = strip_slots<T, SS>();
-  const size_t lds = ((size_t)NVS * 64 * 16) +
-                     ((size_t)kp * SS * (SS + 1) + SS + SS + (2 * SS + 1) + SS) * sizeof(T);
+  const size_t lds = ((size_t)NVS * 64 * 16) + ((size_t)kp * SS * (SS + 1) + 2 * SS) * sizeof(T);
   if (lds > dev.max_lds_per_block)
     return fail(GLASS_EUNSUPPORTED,
                 "bdsv: knot_points*state_size*(state_size+1) elements exceed LDS");
