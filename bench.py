@@ -61,10 +61,24 @@ KERNEL_OF = {
     "pcg3": "pcg_batched_kernel<float, 21,",
     "grid4": "pcg_grid_kernel<double, 12,",
     "bdsv2": "bdsv_kernel<float, 14>",
+    "pcg2_f64": "pcg_batched_kernel<double, 14,",
+    "grid4_f32": "pcg_grid_kernel<float, 12,",
 }
 # Workload inputs: the five configurations; bdsv2 is the direct solve of the
-# same systems as pcg2 (ss=14, kp=32, 4096 problems).
-CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2}
+# same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
+# are the precision variants of pcg2 and grid4 (same recipe and seeds).
+CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2,
+             "pcg2_f64": 2, "grid4_f32": 4}
+VARIANT_OF = {
+    "pcg2_f64": dict(name="pcg_ss14_kp32_b4096_f64", dtype=np.float64),
+    "grid4_f32": dict(name="grid_pcg_ss12_kp8192_f32", dtype=np.float32, rel_tol=1e-7),
+}
+
+
+def workload_of(key):
+    from dataclasses import replace
+    w = workloads.CONFIGS[CONFIG_OF[key]]
+    return replace(w, **VARIANT_OF[key]) if key in VARIANT_OF else w
 
 
 def kernel_source_hash() -> str:
@@ -232,6 +246,24 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.ev]
 
 
+def isolated_ms(torch, fn, reps=10):
+    """GPU-side duration per call with the host enqueueing ahead of the GPU
+    (a spin kernel holds the stream while the calls are queued), so host
+    launch overhead is excluded; measured after the timed region.  fn(k)
+    makes call k."""
+    torch.cuda.synchronize()
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(50_000_000)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for k, (a, b) in enumerate(ev):
+        a.record()
+        fn(k)
+        b.record()
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in ev]))
+
+
 def roofline(nbytes, avg_ms, traffic):
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -241,7 +273,7 @@ def roofline(nbytes, avg_ms, traffic):
 
 def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     cfg = CONFIG_OF[key]
-    w = workloads.CONFIGS[cfg]
+    w = workload_of(key)
     inp = workloads.generate(w)
     dev = torch.device("cuda:0")
     S = torch.from_numpy(inp["S"]).to(dev)
@@ -275,14 +307,20 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     launch_ms = tm.launch_ms()
     it = iters.cpu().numpy()
     avg_ms = float(np.mean(launch_ms))
-    resident = cfg in (0, 2, 4)
+    # S and Pinv count once if they stay on chip (the grid solve and the
+    # batched resident placement), else once per pass.
+    resident = grid or glass.pcg_batched_placement(w.ss, w.kp, S.dtype) == glass.PLACEMENT_RESIDENT
     nbytes = algorithmic_bytes_pcg(w, it, resident)
+    for k in range(min(10, len(xs))):
+        xs[k].zero_()
+    iso = isolated_ms(torch, lambda k: run(xs[k]), reps=min(10, len(xs)))
     out = {
         "workload": w.name, "kind": "grid_pcg" if grid else "batched_pcg",
         "kernel": KERNEL_OF[key], "dtype": np.dtype(w.dtype).name, "state_size": w.ss,
         "knot_points": w.kp, "n_problems": B, "solves_per_s": B * steps / wall,
         "ms_per_step": wall * 1e3 / steps, "kernel_ms_avg": avg_ms,
         "kernel_ms_min": float(np.min(launch_ms)),
+        "kernel_ms_isolated": iso,
         "iterations": {str(k): int(v) for k, v in zip(*np.unique(it, return_counts=True))},
         "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
     }
@@ -321,11 +359,13 @@ def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu, traffic):
     launch_ms = tm.launch_ms()
     avg_ms = float(np.mean(launch_ms))
     nbytes = algorithmic_bytes_bdmv(w, w.n_problems)
+    iso = isolated_ms(torch, lambda k: glass.bdmv_batched(y, S, v, w.ss, w.kp))
     out = {
         "workload": w.name, "kind": "bdmv", "kernel": KERNEL_OF["bdmv1"], "dtype": "float32",
         "state_size": w.ss, "knot_points": w.kp, "n_problems": w.n_problems,
         "gb_per_s": nbytes / (wall / steps) / 1e9, "ms_per_step": wall * 1e3 / steps,
         "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
+        "kernel_ms_isolated": iso,
         "roofline": roofline(nbytes, avg_ms, traffic.get("bdmv1")),
     }
     if with_cpu:
@@ -342,7 +382,7 @@ def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu, traffic):
 
 
 def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
-    w = workloads.CONFIGS[CONFIG_OF[key]]
+    w = workload_of(key)
     inp = workloads.generate(w, with_pinv=False)
     dev = torch.device("cuda:0")
     S = torch.from_numpy(inp["S"]).to(dev)
@@ -363,6 +403,7 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     wall = time.perf_counter() - t0
     launch_ms = tm.launch_ms()
     avg_ms = float(np.mean(launch_ms))
+    iso = isolated_ms(torch, lambda k: glass.bdsv_batched(x, S, b, w.ss, w.kp, status))
     es = np.dtype(w.dtype).itemsize
     # S once, b read, x written, status
     nbytes = float(B) * (w.n * 3 * w.ss * es + 2 * w.n * es + 4)
@@ -371,6 +412,7 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         "dtype": np.dtype(w.dtype).name, "state_size": w.ss, "knot_points": w.kp,
         "n_problems": B, "solves_per_s": B * steps / wall, "ms_per_step": wall * 1e3 / steps,
         "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
+        "kernel_ms_isolated": iso,
         "not_spd": int((status.cpu().numpy() != 0).sum()),
         "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
     }
@@ -401,7 +443,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workloads", default="all",
-                    help="comma list of pcg0,bdmv1,pcg2,pcg3,grid4,bdsv2 or 'all'")
+                    help="comma list of %s or 'all'" % ",".join(CONFIG_OF))
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--cpu-budget", type=float, default=4.0,
                     help="seconds of oracle time per workload baseline")

@@ -20,6 +20,8 @@ __all__ = [
     "GlassError", "load", "library_path", "bdmv_batched", "pcg_batched",
     "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD",
+    "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
+    "PLACEMENT_STREAMED",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +63,7 @@ def load():
             "glass_pcg_batched": ([P, P, P, P, I, I, I, I, D, D, P, I, P], I),
             "glass_pcg_batched_ex": ([P, P, P, P, I, I, I, I, D, D, P, P, P, I, P], I),
             "glass_bdsv_batched": ([P, P, P, I, I, I, P, I, P], I),
+            "glass_pcg_batched_placement": ([I, I, I, I], I),
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, P], I),
@@ -169,6 +172,22 @@ def bdsv_batched(x, S, b, state_size: int, knot_points: int, status_out=None,
     st = _dev(status_out, "status_out", B, torch.int32) if status_out is not None else None
     rc = load().glass_bdsv_batched(*a, ss, kp, B, st, _dtype_code(S), _stream(stream))
     _check(rc, "glass_bdsv_batched")
+
+
+PLACEMENT_RESIDENT, PLACEMENT_STREAMED_PREFETCH, PLACEMENT_STREAMED = 0, 1, 2
+
+
+def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=True) -> int:
+    """Where pcg_batched keeps S and Pinv on the current device for this shape:
+    PLACEMENT_RESIDENT (read once per solve) or PLACEMENT_STREAMED[_PREFETCH]
+    (read once per matvec pass).  Raises for shapes the solve rejects."""
+    import torch
+    code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
+    rc = load().glass_pcg_batched_placement(int(state_size), int(knot_points), code,
+                                            1 if aligned16 else 0)
+    if rc < 0:
+        _check(rc, "glass_pcg_batched_placement")
+    return rc
 
 
 def pcg_grid_workspace_bytes(state_size: int, knot_points: int, dtype) -> int:

@@ -151,6 +151,14 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
                               iters_out, nullptr, nullptr, dtype, hip_stream);
 }
 
+int glass_pcg_batched_placement(int state_size, int knot_points,
+                                glass_dtype dtype, int aligned16) {
+  if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
+  if ((long long)knot_points * state_size > 8192)
+    return fail(GLASS_EUNSUPPORTED, "knot_points*state_size above 8192 (use glass_pcg_grid)");
+  return glass::pcg_batched_placement(dtype, state_size, knot_points, aligned16 != 0);
+}
+
 int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
                        int knot_points, int n_problems, int* status_out,
                        glass_dtype dtype, void* hip_stream) {

@@ -38,6 +38,9 @@ int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
                        double abs_tol, int* iters, int* status, void* rho,
                        hipStream_t stream);
 
+// Placement glass_pcg_batched would choose (GLASS_PLACEMENT_*), or an error.
+int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16);
+
 int launch_bdsv(glass_dtype dt, void* x, const void* S, const void* b, int ss,
                 int kp, int n_problems, int* status, hipStream_t stream);
 

@@ -577,7 +577,30 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   }
 }
 
+template <typename T>
+int placement_typed(int ss, int kp, bool vec) {
+  DeviceInfo dev;
+  if (int rc = current_device_info(&dev)) return rc;
+  const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
+  const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
+                        std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
+  Plan pl;
+  if (!make_plan<T>(ss, kp, specialised, prefetch, dev.max_lds_per_block, &pl))
+    return fail(GLASS_EUNSUPPORTED, "pcg: problem too large for one workgroup (rows or LDS)");
+  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl.res) {
+    Plan alt;
+    if (make_plan<T>(ss, kp, false, prefetch, dev.max_lds_per_block, &alt)) pl = alt;
+  }
+  return pl.res ? GLASS_PLACEMENT_RESIDENT
+                : (pl.prefetch ? GLASS_PLACEMENT_STREAMED_PREFETCH : GLASS_PLACEMENT_STREAMED);
+}
+
 }  // namespace
+
+int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16) {
+  return dt == GLASS_F32 ? placement_typed<float>(ss, kp, aligned16)
+                         : placement_typed<double>(ss, kp, aligned16);
+}
 
 int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
                        const void* Pinv, const void* b, int ss, int kp,

@@ -129,6 +129,20 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
                          double abs_tol, int* iters_out, int* status_out,
                          void* rho_out, glass_dtype dtype, void* hip_stream);
 
+/* Where glass_pcg_batched keeps S and Pinv for a problem shape on the
+ * current device: GLASS_PLACEMENT_RESIDENT (each lane's rows in registers,
+ * read from HBM once per solve) or GLASS_PLACEMENT_STREAMED[_PREFETCH]
+ * (re-read from memory for every matvec).  aligned16: whether S and Pinv
+ * will be 16-byte aligned.  Returns a negative GLASS_E* code for shapes the
+ * solve rejects.  Enqueues nothing. */
+enum {
+  GLASS_PLACEMENT_RESIDENT = 0,
+  GLASS_PLACEMENT_STREAMED_PREFETCH = 1,
+  GLASS_PLACEMENT_STREAMED = 2
+};
+int glass_pcg_batched_placement(int state_size, int knot_points,
+                                glass_dtype dtype, int aligned16);
+
 /*
  * One PCG solve (same steps and outputs as glass_pcg_batched with
  * n_problems = 1) spread over a cooperative grid of workgroups that stay

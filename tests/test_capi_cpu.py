@@ -115,3 +115,9 @@ def test_bdsv_argument_errors(lib):
     assert bdsv(dt=3) == EINVAL
     assert bdsv(ss=25) == EUNSUPPORTED  # above GLASS_BDSV_MAX_STATE_SIZE
     assert bdsv(B=0) == 0
+
+
+def test_placement_query_argument_errors(lib):
+    assert lib.glass_pcg_batched_placement(0, 32, 0, 1) == EINVAL
+    assert lib.glass_pcg_batched_placement(6, 32, 5, 1) == EINVAL
+    assert lib.glass_pcg_batched_placement(64, 200, 0, 1) == EUNSUPPORTED

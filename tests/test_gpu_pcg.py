@@ -178,3 +178,17 @@ def test_pcg_prefetch_ring_matches_plain_staging(gpu, monkeypatch):
     b = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+def test_pcg_placement_query_matches_the_workloads(gpu, monkeypatch):
+    """S and Pinv stay in registers for the ss=6 and ss=14 fp32 workloads and
+    stream (with prefetch) for ss=21 kp=64; forcing streaming is reported."""
+    assert gpu.pcg_batched_placement(6, 32, torch.float32) == gpu.PLACEMENT_RESIDENT
+    assert gpu.pcg_batched_placement(14, 32, torch.float32) == gpu.PLACEMENT_RESIDENT
+    assert gpu.pcg_batched_placement(21, 64, torch.float32) == gpu.PLACEMENT_STREAMED_PREFETCH
+    assert gpu.pcg_batched_placement(21, 64, torch.float32, aligned16=False) == \
+        gpu.PLACEMENT_STREAMED
+    monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
+    assert gpu.pcg_batched_placement(14, 32, torch.float32) != gpu.PLACEMENT_RESIDENT
+    with pytest.raises(gpu.GlassError):
+        gpu.pcg_batched_placement(64, 200, torch.float32)
