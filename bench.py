@@ -390,23 +390,29 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     B = w.n_problems
     x = torch.zeros((B, w.n), dtype=S.dtype, device=dev)
     status = torch.zeros(B, dtype=torch.int32, device=dev)
+    # The per-block-row factors go to a workspace in HBM (more problems per CU).
+    ws = torch.empty(glass.bdsv_workspace_bytes(w.ss, w.kp, B, S.dtype), dtype=torch.uint8,
+                     device=dev)
     for _ in range(warmup):
-        glass.bdsv_batched(x, S, b, w.ss, w.kp, status)
+        glass.bdsv_batched(x, S, b, w.ss, w.kp, status, workspace=ws)
     torch.cuda.synchronize()
     tm = Timer(torch, steps)
     t0 = time.perf_counter()
     for k in range(steps):
         tm.ev[k][0].record()
-        glass.bdsv_batched(x, S, b, w.ss, w.kp, status)
+        glass.bdsv_batched(x, S, b, w.ss, w.kp, status, workspace=ws)
         tm.ev[k][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     launch_ms = tm.launch_ms()
     avg_ms = float(np.mean(launch_ms))
-    iso = isolated_ms(torch, lambda k: glass.bdsv_batched(x, S, b, w.ss, w.kp, status))
+    iso = isolated_ms(torch, lambda k: glass.bdsv_batched(x, S, b, w.ss, w.kp, status,
+                                                         workspace=ws))
     es = np.dtype(w.dtype).itemsize
-    # S once, b read, x written, status
-    nbytes = float(B) * (w.n * 3 * w.ss * es + 2 * w.n * es + 4)
+    # S once, b read, x written, status; plus the factors [G|u] written to and
+    # read back from the workspace (kp*ss*(ss+1) each way)
+    nbytes = float(B) * (w.n * 3 * w.ss * es + 2 * w.n * es + 4
+                         + 2 * w.kp * w.ss * (w.ss + 1) * es)
     out = {
         "workload": "bdsv_ss14_kp32_b4096_f32", "kind": "bdsv", "kernel": KERNEL_OF[key],
         "dtype": np.dtype(w.dtype).name, "state_size": w.ss, "knot_points": w.kp,

@@ -18,7 +18,8 @@ import threading
 
 __all__ = [
     "GlassError", "load", "library_path", "bdmv_batched", "pcg_batched",
-    "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "CONVERGED",
+    "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "bdsv_workspace_bytes",
+    "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD",
     "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED",
@@ -62,7 +63,8 @@ def load():
             "glass_bdmv_batched": ([P, P, P, I, I, I, I, P], I),
             "glass_pcg_batched": ([P, P, P, P, I, I, I, I, D, D, P, I, P], I),
             "glass_pcg_batched_ex": ([P, P, P, P, I, I, I, I, D, D, P, P, P, I, P], I),
-            "glass_bdsv_batched": ([P, P, P, I, I, I, P, I, P], I),
+            "glass_bdsv_batched": ([P, P, P, I, I, I, P, P, Z, I, P], I),
+            "glass_bdsv_workspace_bytes": ([I, I, I, I], Z),
             "glass_pcg_batched_placement": ([I, I, I, I], I),
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
@@ -158,11 +160,19 @@ def pcg_batched(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int
     _check(rc, "glass_pcg_batched_ex")
 
 
+def bdsv_workspace_bytes(state_size: int, knot_points: int, n_problems: int, dtype) -> int:
+    import torch
+    code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
+    return int(load().glass_bdsv_workspace_bytes(int(state_size), int(knot_points),
+                                                 int(n_problems), code))
+
+
 def bdsv_batched(x, S, b, state_size: int, knot_points: int, status_out=None,
-                 stream=None):
+                 workspace=None, stream=None):
     """Direct solve S x = b per problem (page "Block-tridiagonal Solves",
     glass::bdsv).  x, b: [B, kp*ss]; status_out int32 [B] (BDSV_OK or
-    BDSV_NOT_SPD; x is written only where it is BDSV_OK)."""
+    BDSV_NOT_SPD; x is written only where it is BDSV_OK); workspace: None or
+    a contiguous device tensor of at least ``bdsv_workspace_bytes`` bytes."""
     import torch
     ss, kp = int(state_size), int(knot_points)
     B = _problems(S, ss, kp)
@@ -170,7 +180,13 @@ def bdsv_batched(x, S, b, state_size: int, knot_points: int, status_out=None,
     n = kp * ss
     a = (_dev(x, "x", B * n, dt), _dev(S, "S", S.numel(), dt), _dev(b, "b", B * n, dt))
     st = _dev(status_out, "status_out", B, torch.int32) if status_out is not None else None
-    rc = load().glass_bdsv_batched(*a, ss, kp, B, st, _dtype_code(S), _stream(stream))
+    if workspace is None:
+        wp, wb = None, 0
+    else:
+        if not (workspace.is_cuda and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous device tensor")
+        wp, wb = ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+    rc = load().glass_bdsv_batched(*a, ss, kp, B, st, wp, wb, _dtype_code(S), _stream(stream))
     _check(rc, "glass_bdsv_batched")
 
 

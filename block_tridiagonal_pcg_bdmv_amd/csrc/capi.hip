@@ -159,8 +159,18 @@ int glass_pcg_batched_placement(int state_size, int knot_points,
   return glass::pcg_batched_placement(dtype, state_size, knot_points, aligned16 != 0);
 }
 
+size_t glass_bdsv_workspace_bytes(int state_size, int knot_points, int n_problems,
+                                  glass_dtype dtype) {
+  if (dtype != GLASS_F32 && dtype != GLASS_F64) return 0;
+  if (state_size < 1 || state_size > GLASS_BDSV_MAX_STATE_SIZE || knot_points < 1 ||
+      n_problems < 0)
+    return 0;
+  return glass::bdsv_workspace_bytes(state_size, knot_points, n_problems, dtype);
+}
+
 int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
                        int knot_points, int n_problems, int* status_out,
+                       void* workspace, size_t workspace_bytes,
                        glass_dtype dtype, void* hip_stream) {
   if (int rc = check_common(dtype, state_size, knot_points, n_problems)) return rc;
   if (state_size > GLASS_BDSV_MAX_STATE_SIZE)
@@ -170,8 +180,14 @@ int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
   if (int rc = check_ptr(S, dtype, "S")) return rc;
   if (int rc = check_ptr(b, dtype, "b")) return rc;
   if (status_out && !glass::aligned(status_out, 4)) return fail(GLASS_EINVAL, "status_out misaligned");
+  if (workspace) {
+    if (int rc = check_ptr(workspace, dtype, "workspace")) return rc;
+    if (workspace_bytes <
+        glass::bdsv_workspace_bytes(state_size, knot_points, n_problems, dtype))
+      return fail(GLASS_EINVAL, "workspace smaller than glass_bdsv_workspace_bytes()");
+  }
   return glass::launch_bdsv(dtype, x, S, b, state_size, knot_points, n_problems,
-                            status_out, (hipStream_t)hip_stream);
+                            status_out, workspace, (hipStream_t)hip_stream);
 }
 
 size_t glass_pcg_grid_workspace_bytes(int state_size, int knot_points,

@@ -41,8 +41,10 @@ int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
 // Placement glass_pcg_batched would choose (GLASS_PLACEMENT_*), or an error.
 int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16);
 
+size_t bdsv_workspace_bytes(int ss, int kp, long long n_problems, glass_dtype dt);
 int launch_bdsv(glass_dtype dt, void* x, const void* S, const void* b, int ss,
-                int kp, int n_problems, int* status, hipStream_t stream);
+                int kp, int n_problems, int* status, void* workspace,
+                hipStream_t stream);
 
 size_t grid_workspace_bytes(int ss, int kp, glass_dtype dt);
 int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,

@@ -185,12 +185,22 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
  * x, b: [n_problems][knot_points*state_size] (unpadded); x is written only
  * for problems whose status is GLASS_BDSV_OK.  status_out: int32
  * [n_problems] or NULL.
- * Limits: state_size <= GLASS_BDSV_MAX_STATE_SIZE; one problem's
- * knot_points*state_size*(state_size+1) elements must fit in LDS
+ * workspace: NULL, or caller-owned device memory of at least
+ * glass_bdsv_workspace_bytes(...) bytes aligned to the element size, where
+ * the per-block-row factors [G_br | u_br] are kept for the back substitution.
+ * Without it they are kept in on-chip memory, which limits how many problems
+ * run at once and how long a chain can be; with it many more problems run
+ * concurrently.  Its contents on entry do not matter; it must not be used by
+ * another call at the same time.
+ * Limits: state_size <= GLASS_BDSV_MAX_STATE_SIZE; without a workspace, one
+ * problem's knot_points*state_size*(state_size+1) elements must fit in LDS
  * (GLASS_EUNSUPPORTED otherwise).
  */
+size_t glass_bdsv_workspace_bytes(int state_size, int knot_points,
+                                  int n_problems, glass_dtype dtype);
 int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
                        int knot_points, int n_problems, int* status_out,
+                       void* workspace, size_t workspace_bytes,
                        glass_dtype dtype, void* hip_stream);
 
 /* Static text for a GLASS_* return code. */

@@ -105,8 +105,8 @@ def test_grid_argument_errors_and_workspace_size(lib):
 
 
 def test_bdsv_argument_errors(lib):
-    def bdsv(x=FAKE, S=FAKE, b=FAKE, ss=14, kp=32, B=1, st=None, dt=0):
-        return lib.glass_bdsv_batched(x, S, b, ss, kp, B, st, dt, None)
+    def bdsv(x=FAKE, S=FAKE, b=FAKE, ss=14, kp=32, B=1, st=None, ws=None, wsb=0, dt=0):
+        return lib.glass_bdsv_batched(x, S, b, ss, kp, B, st, ws, wsb, dt, None)
     assert bdsv(x=None) == EINVAL
     assert bdsv(S=None) == EINVAL
     assert bdsv(b=ctypes.c_void_p(0x100001)) == EINVAL
@@ -115,6 +115,11 @@ def test_bdsv_argument_errors(lib):
     assert bdsv(dt=3) == EINVAL
     assert bdsv(ss=25) == EUNSUPPORTED  # above GLASS_BDSV_MAX_STATE_SIZE
     assert bdsv(B=0) == 0
+    need = lib.glass_bdsv_workspace_bytes(14, 32, 1, 0)
+    assert need >= 32 * 14 * 15 * 4 and need % 256 == 0
+    assert lib.glass_bdsv_workspace_bytes(25, 32, 1, 0) == 0
+    assert bdsv(ws=FAKE, wsb=need - 1) == EINVAL  # too small
+    assert bdsv(ws=ctypes.c_void_p(0x100002), wsb=need) == EINVAL  # misaligned
 
 
 def test_placement_query_argument_errors(lib):

@@ -19,11 +19,17 @@ from gpu_common import X_REL, pcg_gpu, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def bdsv_gpu(glass, S, b, ss, kp, x0=None):
+def bdsv_gpu(glass, S, b, ss, kp, x0=None, ws=False):
+    """ws: keep the per-block-row factors in a workspace in HBM instead of
+    LDS (the two placements must agree bit for bit)."""
     St, bt = to_dev(S), to_dev(b)
     x = to_dev(np.full(b.shape, np.nan, b.dtype) if x0 is None else x0).clone()
     st = torch.full((b.shape[0],), -1, dtype=torch.int32, device="cuda")
-    glass.bdsv_batched(x, St, bt, ss, kp, st)
+    work = None
+    if ws:
+        nbytes = glass.bdsv_workspace_bytes(ss, kp, b.shape[0], St.dtype)
+        work = torch.full((nbytes // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    glass.bdsv_batched(x, St, bt, ss, kp, st, workspace=work)
     torch.cuda.synchronize()
     return x.cpu().numpy(), st.cpu().numpy()
 
@@ -39,37 +45,44 @@ def assert_bdsv_parity(S, b, ss, kp, x, st, dtype):
     assert worst <= X_REL[dtype], "x relative L2 error %g" % worst
 
 
+@pytest.mark.parametrize("ws", [False, True])
 @pytest.mark.parametrize("cfg,B", [(0, 64), (2, 33), (3, 9)])
-def test_bdsv_workload_shapes(gpu, cfg, B):
+def test_bdsv_workload_shapes(gpu, cfg, B, ws):
     w = workloads.CONFIGS[cfg]
     inp = workloads.generate(w, n_problems=B)
-    say("bdsv cfg%d shape ss=%d kp=%d B=%d" % (cfg, w.ss, w.kp, B))
-    x, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp)
+    say("bdsv cfg%d shape ss=%d kp=%d B=%d ws=%s" % (cfg, w.ss, w.kp, B, ws))
+    x, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp, ws=ws)
     assert np.all(st == gpu.BDSV_OK)
     assert_bdsv_parity(inp["S"], inp["b"], w.ss, w.kp, x, st, np.float32)
 
 
-def test_bdsv_full_batch_ss14(gpu):
-    """All 4096 systems of the ss=14, kp=32 workload, every x checked."""
+def test_bdsv_full_batch_ss14_both_placements(gpu):
+    """All 4096 systems of the ss=14, kp=32 workload, every x checked; the
+    LDS and the workspace placements give the same bits."""
     w = workloads.CONFIGS[2]
     inp = workloads.generate(w)
     say("bdsv full ss=14 kp=32 B=4096")
     x, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp)
     assert np.all(st == gpu.BDSV_OK)
     assert_bdsv_parity(inp["S"], inp["b"], w.ss, w.kp, x, st, np.float32)
+    x2, st2 = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp, ws=True)
+    np.testing.assert_array_equal(st2, st)
+    np.testing.assert_array_equal(x2, x)
 
 
+@pytest.mark.parametrize("ws", [False, True])
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 @pytest.mark.parametrize("ss,kp,B", [(1, 1, 3), (1, 300, 2), (2, 5, 4), (5, 1, 3),
-                                     (7, 40, 3), (12, 64, 2), (16, 20, 2), (24, 12, 2)])
-def test_bdsv_edge_shapes(gpu, ss, kp, B, dtype):
+                                     (7, 40, 3), (12, 64, 2), (16, 20, 2), (24, 12, 2),
+                                     (13, 7, 3)])
+def test_bdsv_edge_shapes(gpu, ss, kp, B, dtype, ws):
     rng = np.random.default_rng(ss * 1000 + kp)
     S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.2, dtype)
     S[:, 0, :, :ss] = 3.0        # off-matrix blocks are ignored
     S[:, -1, :, 2 * ss:] = -3.0
     b = rng.standard_normal((B, kp * ss)).astype(dtype)
-    say("bdsv ss=%d kp=%d B=%d %s" % (ss, kp, B, np.dtype(dtype).name))
-    x, st = bdsv_gpu(gpu, S, b, ss, kp)
+    say("bdsv ss=%d kp=%d B=%d %s ws=%s" % (ss, kp, B, np.dtype(dtype).name, ws))
+    x, st = bdsv_gpu(gpu, S, b, ss, kp, ws=ws)
     assert np.all(st == gpu.BDSV_OK)
     assert_bdsv_parity(S, b, ss, kp, x, st, dtype)
 
@@ -86,7 +99,8 @@ def test_bdsv_golden_fixtures(gpu, name):
     np.testing.assert_allclose(x[0], frac_array(g["x"]), rtol=0, atol=1e-12)
 
 
-def test_bdsv_not_spd_leaves_x_and_flags(gpu):
+@pytest.mark.parametrize("ws", [False, True])
+def test_bdsv_not_spd_leaves_x_and_flags(gpu, ws):
     rng = np.random.default_rng(12)
     ss, kp, B = 6, 10, 4
     S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.3, np.float32)
@@ -94,8 +108,8 @@ def test_bdsv_not_spd_leaves_x_and_flags(gpu):
     S[3, 4, :, ss:2 * ss] = 0.0   # a singular diagonal block mid-chain
     b = rng.standard_normal((B, kp * ss)).astype(np.float32)
     x0 = np.full((B, kp * ss), 5.0, np.float32)
-    say("bdsv status cases")
-    x, st = bdsv_gpu(gpu, S, b, ss, kp, x0=x0)
+    say("bdsv status cases ws=%s" % ws)
+    x, st = bdsv_gpu(gpu, S, b, ss, kp, x0=x0, ws=ws)
     _, so = oracle.bdsv(S, b, ss, kp, "f32")
     np.testing.assert_array_equal(st, so)
     assert st[1] == gpu.BDSV_NOT_SPD and st[0] == gpu.BDSV_OK
@@ -117,10 +131,19 @@ def test_bdsv_agrees_with_gpu_pcg_and_is_deterministic(gpu):
     assert rel.max() < 1e-4
 
 
-def test_bdsv_lds_limit_is_reported(gpu):
-    S = torch.zeros(24 * 3 * 24 * 100, dtype=torch.float32, device="cuda")
-    b = torch.zeros(24 * 100, dtype=torch.float32, device="cuda")
-    x = torch.zeros_like(b)
+def test_bdsv_lds_limit_is_reported_and_the_workspace_lifts_it(gpu):
+    """ss=24, kp=100: the factors (240 KB per problem) exceed LDS; with a
+    workspace the chain solves."""
+    rng = np.random.default_rng(21)
+    ss, kp, B = 24, 100, 2
+    S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.2, np.float32)
+    b = rng.standard_normal((B, kp * ss)).astype(np.float32)
+    St, bt = to_dev(S), to_dev(b)
+    x = torch.zeros_like(bt)
     with pytest.raises(gpu.GlassError) as ei:
-        gpu.bdsv_batched(x, S, b, 24, 100)
+        gpu.bdsv_batched(x, St, bt, ss, kp)
     assert ei.value.code == -2
+    say("bdsv long chain with workspace")
+    xg, st = bdsv_gpu(gpu, S, b, ss, kp, ws=True)
+    assert np.all(st == gpu.BDSV_OK)
+    assert_bdsv_parity(S, b, ss, kp, xg, st, np.float32)
