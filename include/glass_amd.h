@@ -114,7 +114,11 @@ int glass_bdmv_batched(void* y, const void* S, const void* v, int state_size,
  * must be symmetric positive definite for the result to be meaningful; a
  * non-positive p^T S p stops that problem with GLASS_PCG_BREAKDOWN.
  * Limits: state_size <= GLASS_MAX_STATE_SIZE; knot_points*state_size <= 8192
- * (further limited by LDS for large state_size: GLASS_EUNSUPPORTED).
+ * rows.  When S and Pinv do not stay in registers they are staged through a
+ * 64-row LDS chunk per wave, which must fit in LDS next to two padded
+ * vectors: in float32 that allows up to about 4000 rows at state_size 12-21
+ * and 8190 at state_size 6.  Larger shapes return GLASS_EUNSUPPORTED before
+ * anything is launched (glass_pcg_batched_placement reports it too).
  */
 int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
                       int state_size, int knot_points, int n_problems,

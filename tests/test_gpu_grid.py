@@ -103,3 +103,15 @@ def test_grid_status_cases(gpu):
     say("grid b=0, x0=0")
     x, it, st, _ = grid_gpu(gpu, dict(base, b=0 * b, x0=0 * x0), ss, kp, 20, 1e-8, 0.0)
     assert st[0] == gpu.CONVERGED and it[0] == 0 and np.all(x == 0)
+
+
+def test_grid_full_chain_fp32_variant(gpu):
+    """The float32 variant of the kp=8192 chain as bench.py times it
+    (rel_tol 1e-7), every entry of x checked."""
+    from dataclasses import replace
+    w = replace(workloads.CONFIGS[4], dtype=np.float32, rel_tol=1e-7)
+    inp = workloads.generate(w)
+    say("grid ss=12 kp=8192 fp32")
+    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    assert res[2][0] == gpu.CONVERGED, res[2]
+    assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float32)

@@ -192,3 +192,44 @@ def test_pcg_placement_query_matches_the_workloads(gpu, monkeypatch):
     assert gpu.pcg_batched_placement(14, 32, torch.float32) != gpu.PLACEMENT_RESIDENT
     with pytest.raises(gpu.GlassError):
         gpu.pcg_batched_placement(64, 200, torch.float32)
+
+
+def test_pcg_full_batch_fp64_variant(gpu):
+    """The float64 variant of the ss=14 workload at the size bench.py times
+    (4096 problems), every x checked against the float64 oracle."""
+    run_workload(gpu, 2, dtype=np.float64)
+
+
+@pytest.mark.parametrize("ss,kp,fits", [(6, 1365, True), (12, 340, True), (12, 682, False),
+                                         (21, 195, True), (21, 390, False)])
+def test_pcg_largest_batched_rows(gpu, ss, kp, fits):
+    """Near the row limit of one workgroup: the streamed placement holds a
+    64-row LDS stage per wave, so wide rows cap the rows per problem below
+    8192 (ss=12: 16 waves x 8 rows per lane need more than 160 KB of LDS).
+    Shapes that fit solve to the parity bar; the others are refused with
+    GLASS_EUNSUPPORTED before anything is launched."""
+    rng = np.random.default_rng(ss + kp)
+    B = 2
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.2, np.float32)
+    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, np.float32),
+           "b": rng.standard_normal((B, kp * ss)).astype(np.float32),
+           "x0": np.zeros((B, kp * ss), np.float32)}
+    say("pcg ss=%d kp=%d (n=%d)" % (ss, kp, ss * kp))
+    if not fits:
+        with pytest.raises(gpu.GlassError) as ei:
+            gpu.pcg_batched_placement(ss, kp, torch.float32)
+        assert ei.value.code == -2
+        with pytest.raises(gpu.GlassError) as ei:
+            pcg_gpu(gpu, inp, ss, kp, 300, 1e-8, 0.0)
+        assert ei.value.code == -2
+        return
+    res = pcg_gpu(gpu, inp, ss, kp, 300, 1e-8, 0.0)
+    assert_pcg_parity(inp, ss, kp, 300, 1e-8, 0.0, res, np.float32)
+
+
+def test_empty_batches_are_no_ops(gpu):
+    z = torch.zeros(0, dtype=torch.float32, device="cuda")
+    zi = torch.zeros(0, dtype=torch.int32, device="cuda")
+    gpu.pcg_batched(z, z, z, z, 6, 32, 10, 1e-6, 0.0, zi)
+    gpu.bdsv_batched(z, z, z, 6, 32, zi)
+    torch.cuda.synchronize()
