@@ -287,9 +287,12 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         ws = torch.empty(glass.pcg_grid_workspace_bytes(w.ss, w.kp, S.dtype),
                          dtype=torch.uint8, device=dev)
 
-    def run(x):
+    # The grid solve is timed with the exclusive launch (this process is the
+    # only user of the device); the cooperative launch is timed after it.
+    def run(x, exclusive=True):
         if grid:
-            glass.pcg_grid(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters, ws)
+            glass.pcg_grid(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters, ws,
+                           exclusive=exclusive)
         else:
             glass.pcg_batched(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters)
 
@@ -325,7 +328,12 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
     }
     if grid:
+        out["launch"] = "exclusive"
         out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it[0]))
+        for k in range(min(10, len(xs))):
+            xs[k].zero_()
+        out["kernel_ms_isolated_cooperative"] = isolated_ms(
+            torch, lambda k: run(xs[k], exclusive=False), reps=min(10, len(xs)))
     if with_cpu:
         import oracle
         nt = 1 if grid else cpu_threads()

@@ -20,7 +20,7 @@ __all__ = [
     "GlassError", "load", "library_path", "bdmv_batched", "pcg_batched",
     "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "bdsv_workspace_bytes",
     "CONVERGED",
-    "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD",
+    "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
     "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED",
 ]
@@ -35,6 +35,7 @@ _lock = threading.Lock()
 GLASS_F32, GLASS_F64 = 0, 1
 CONVERGED, MAX_ITERS, BREAKDOWN, GRID_TIMEOUT = 0, 1, 2, 3
 BDSV_OK, BDSV_NOT_SPD = 0, 1
+GRID_EXCLUSIVE = 1  # glass_pcg_grid_ex flag: ordinary dispatch on the stream's queue
 
 
 class GlassError(RuntimeError):
@@ -58,7 +59,7 @@ def load():
                 "libglass_amd.so is not built (run __graft_entry__.build() or "
                 "python block_tridiagonal_pcg_bdmv_amd/build.py)")
         lib = ctypes.CDLL(_LIB_PATH)
-        P, I, D, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t
+        P, I, D, Z, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_size_t, ctypes.c_uint
         sigs = {
             "glass_bdmv_batched": ([P, P, P, I, I, I, I, P], I),
             "glass_pcg_batched": ([P, P, P, P, I, I, I, I, D, D, P, I, P], I),
@@ -68,7 +69,7 @@ def load():
             "glass_pcg_batched_placement": ([I, I, I, I], I),
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
-            "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, P], I),
+            "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
             "glass_status_string": ([I], ctypes.c_char_p),
             "glass_last_error": ([], ctypes.c_char_p),
             "glass_version": ([], I),
@@ -214,10 +215,13 @@ def pcg_grid_workspace_bytes(state_size: int, knot_points: int, dtype) -> int:
 
 def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
              rel_tol: float, abs_tol: float, iters_out, workspace,
-             status_out=None, rho_out=None, stream=None):
+             status_out=None, rho_out=None, stream=None, exclusive=False):
     """One PCG solve over a cooperative grid.  Same arguments as
     ``pcg_batched`` with one problem, plus a device ``workspace`` tensor of at
-    least ``pcg_grid_workspace_bytes`` bytes (any dtype, 256-byte aligned)."""
+    least ``pcg_grid_workspace_bytes`` bytes (any dtype, 256-byte aligned).
+    ``exclusive=True`` passes GLASS_GRID_EXCLUSIVE: an ordinary dispatch on
+    the stream's queue, for callers that know no other kernel occupies the
+    device during the solve."""
     import torch
     ss, kp = int(state_size), int(knot_points)
     if _problems(S, ss, kp) != 1:
@@ -235,5 +239,6 @@ def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
     rc = load().glass_pcg_grid_ex(*a, ss, kp, int(max_iters), float(rel_tol),
                                   float(abs_tol), it, st, rh,
                                   ctypes.c_void_p(workspace.data_ptr()), wbytes,
-                                  _dtype_code(S), _stream(stream))
+                                  _dtype_code(S), GRID_EXCLUSIVE if exclusive else 0,
+                                  _stream(stream))
     _check(rc, "glass_pcg_grid_ex")

@@ -202,8 +202,9 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
                       double rel_tol, double abs_tol, int* iters_out,
                       int* status_out, void* rho_out, void* workspace,
                       size_t workspace_bytes, glass_dtype dtype,
-                      void* hip_stream) {
+                      unsigned flags, void* hip_stream) {
   if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
+  if (flags & ~(unsigned)GLASS_GRID_EXCLUSIVE) return fail(GLASS_EINVAL, "unknown grid flags");
   if (knot_points < 4) return fail(GLASS_EINVAL, "grid pcg needs knot_points >= 4");
   if (int rc = check_ptr(x, dtype, "x")) return rc;
   if (int rc = check_ptr(S, dtype, "S")) return rc;
@@ -221,6 +222,7 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
   return glass::launch_pcg_grid(dtype, x, S, Pinv, b, state_size, knot_points,
                                 max_iters, rel_tol, abs_tol, iters_out,
                                 status_out, rho_out, workspace, workspace_bytes,
+                                (flags & GLASS_GRID_EXCLUSIVE) != 0,
                                 (hipStream_t)hip_stream);
 }
 
@@ -231,7 +233,7 @@ int glass_pcg_grid(void* x, const void* S, const void* Pinv, const void* b,
                    void* hip_stream) {
   return glass_pcg_grid_ex(x, S, Pinv, b, state_size, knot_points, max_iters,
                            rel_tol, abs_tol, iters_out, nullptr, nullptr,
-                           workspace, workspace_bytes, dtype, hip_stream);
+                           workspace, workspace_bytes, dtype, 0u, hip_stream);
 }
 
 const char* glass_status_string(int status) {

@@ -103,6 +103,13 @@ def test_grid_argument_errors_and_workspace_size(lib):
     assert grid(ws_bytes=ws - 1) == EINVAL
     assert grid(it=-3) == EINVAL
 
+    def grid_ex(flags):
+        return lib.glass_pcg_grid_ex(FAKE, FAKE, FAKE, FAKE, 12, 8192, 10, 1e-10, 0.0,
+                                     FAKE, None, None, ctypes.c_void_p(0x100000), ws, 1,
+                                     flags, None)
+    assert grid_ex(2) == EINVAL  # unknown flag bit
+    assert grid_ex(0x80000000) == EINVAL
+
 
 def test_bdsv_argument_errors(lib):
     def bdsv(x=FAKE, S=FAKE, b=FAKE, ss=14, kp=32, B=1, st=None, ws=None, wsb=0, dt=0):

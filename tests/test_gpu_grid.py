@@ -14,7 +14,7 @@ from gpu_common import X_REL, assert_pcg_parity, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol):
+def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, exclusive=False):
     t = {k: to_dev(v) for k, v in inp.items()}
     x = t["x0"].clone()
     iters = torch.full((1,), -1, dtype=torch.int32, device="cuda")
@@ -23,7 +23,7 @@ def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol):
     nbytes = glass.pcg_grid_workspace_bytes(ss, kp, x.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     glass.pcg_grid(x, t["S"], t["Pinv"], t["b"], ss, kp, max_iters, rel_tol, abs_tol,
-                   iters, ws, status, rho)
+                   iters, ws, status, rho, exclusive=exclusive)
     torch.cuda.synchronize()
     return (x.cpu().numpy(), iters.cpu().numpy(), status.cpu().numpy(),
             rho.cpu().numpy().reshape(1, 2))
@@ -115,3 +115,31 @@ def test_grid_full_chain_fp32_variant(gpu):
     res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
     assert res[2][0] == gpu.CONVERGED, res[2]
     assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float32)
+
+
+@pytest.mark.parametrize("ss,kp,dtype", [(12, 8192, np.float64), (12, 8192, np.float32),
+                                         (21, 40, np.float32), (5, 33, np.float64)])
+def test_grid_exclusive_launch_is_bit_identical(gpu, ss, kp, dtype):
+    """GLASS_GRID_EXCLUSIVE changes only how the grid is dispatched: x,
+    iterations, status and rho match the cooperative launch bit for bit,
+    also on two solves in a row that reuse the workspace."""
+    if kp == 8192:
+        from dataclasses import replace
+        w = replace(workloads.CONFIGS[4], dtype=dtype,
+                    rel_tol=1e-7 if dtype == np.float32 else workloads.CONFIGS[4].rel_tol)
+        inp = workloads.generate(w)
+        rel = w.rel_tol
+    else:
+        rng = np.random.default_rng(ss * 11 + kp)
+        S, D = workloads.random_spd_strips(rng, 1, ss, kp, 0.1, dtype)
+        inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
+               "b": rng.standard_normal((1, kp * ss)).astype(dtype),
+               "x0": np.zeros((1, kp * ss), dtype)}
+        rel = 1e-10 if dtype == np.float64 else 1e-7
+    say("grid exclusive ss=%d kp=%d %s" % (ss, kp, np.dtype(dtype).name))
+    coop = grid_gpu(gpu, inp, ss, kp, 500, rel, 0.0)
+    for _ in range(2):
+        excl = grid_gpu(gpu, inp, ss, kp, 500, rel, 0.0, exclusive=True)
+        assert excl[2][0] == gpu.CONVERGED
+        for a, b in zip(coop, excl):
+            np.testing.assert_array_equal(a, b)
