@@ -10,7 +10,31 @@
 // M_br is a Schur complement of the SPD matrix, hence SPD; a pivot that is not
 // positive marks the problem as not SPD (status 1, x left unchanged).
 //
-// Mapping on gfx950: one wave per problem (no workgroup barriers at all).
+// Two mappings on gfx950, neither with workgroup barriers.
+//
+// Row mapping (ss <= 16; bdsv_rows_kernel): four problems per wave, one per
+// 16-lane DPP row; lane i of a row holds row i of W = [M | R | y] (2ss+1
+// registers).
+// * Broadcasts within a problem are DPP row_newbcast:k moves, which give every
+//   lane of a 16-lane row the value of lane k of that row, so four problems
+//   share each instruction and no lane waits on a scalar register.
+// * Fill: row i of M and y needs row i of L_br (own registers) and every row
+//   of [G_{br-1} | u_{br-1}] (row m broadcast from lane m): ss*(ss+1) FMAs.
+// * Gauss-Jordan without normalising the pivot row: in step k every lane
+//   reads the pivot W_k[k] and subtracts (W_i[k] / W_k[k]) times the
+//   broadcast pivot row from its columns > k (the pivot lane subtracts zero).
+//   Rows end as piv_i [e_i | G_i | u_i] with piv_i the step-i pivot, so each
+//   lane scales its [G|u] by 1/piv_i once.  About ss*(2ss+1) - ss^2/2 FMAs
+//   per block-row for four problems.
+// * Back substitution: lane i of a row computes x_br[i] from its row of
+//   [G_br | u_br] and x_{br+1} broadcast from the row's lanes.
+// * [G_br | u_br] rows go to the caller's workspace (or, without one, to
+//   LDS when four problems' factors fit).  Each lane loads its own S row with
+//   range-checked buffer loads (missing rows and problems read as zero), the
+//   next block-row's row while the current one is eliminated.
+//
+// Column mapping (ss <= 24, and chains whose factors fit in LDS only for one
+// problem; bdsv_kernel): one wave per problem.
 // * The working block W = [M | R | y] (ss x (2ss+1)) lives in registers, one
 //   column per lane: lane j holds W[0..ss)[j].
 // * M^{-1} [R | y] comes from Gauss-Jordan elimination on W: ss steps; in
@@ -31,6 +55,7 @@
 //   then staged into LDS, where every lane reads L_br by broadcast for the
 //   L_br [G|u] product.
 #include <climits>
+#include <type_traits>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -235,6 +260,239 @@ bdsv_kernel(BdsvArgs<T> a) {
   if (lane == 0 && a.status) a.status[prob] = fail ? GLASS_BDSV_NOT_SPD : GLASS_BDSV_OK;
 }
 
+// ---------------------------------------------------------------------------
+// Row mapping
+// ---------------------------------------------------------------------------
+
+// Value of lane K of this lane's 16-lane row (DPP row_newbcast:K).
+template <int K>
+__device__ __forceinline__ int row_bcast_i32(int v) {
+  static_assert(K >= 0 && K < 16, "row_newbcast lane");
+  // Every source lane of a row broadcast is valid, so no old value is needed.
+  return __builtin_amdgcn_mov_dpp(v, 0x150 + K, 0xF, 0xF, true);
+}
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(row_bcast_i32<K>(__float_as_int(v)));
+}
+template <int K>
+__device__ __forceinline__ double row_bcast(double v) {
+  const long long bits = __double_as_longlong(v);
+  const int lo = row_bcast_i32<K>((int)(bits & 0xffffffffLL));
+  const int hi = row_bcast_i32<K>((int)(bits >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+
+// f(std::integral_constant<int, I>) for I = B .. E-1, unrolled at compile time.
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// 1/p: hardware reciprocal refined by Newton steps (error below one unit in
+// the last place of T for normal p).
+__device__ __forceinline__ float recip(float p) {
+  float r = __builtin_amdgcn_rcpf(p);
+  const float e = fmaf(-p, r, 1.0f);
+  return fmaf(e, r, r);
+}
+__device__ __forceinline__ double recip(double p) {
+  double r = __builtin_amdgcn_rcp(p);
+  double e = fma(-p, r, 1.0);
+  r = fma(e, r, r);
+  e = fma(-p, r, 1.0);
+  return fma(e, r, r);
+}
+
+// Buffer access of one element (range-checked; out of range reads zero and
+// writes nothing).
+__device__ __forceinline__ float rsrc_load(__amdgpu_buffer_rsrc_t rs, int off, float) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+}
+__device__ __forceinline__ double rsrc_load(__amdgpu_buffer_rsrc_t rs, int off, double) {
+  return __builtin_bit_cast(double, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0));
+}
+__device__ __forceinline__ void rsrc_store(__amdgpu_buffer_rsrc_t rs, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, v), rs, off, 0, 0);
+}
+__device__ __forceinline__ void rsrc_store(__amdgpu_buffer_rsrc_t rs, int off, double v) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, 0);
+}
+
+constexpr int kRowsProblemsPerWave = 4;
+
+template <typename T, int SS, bool WS>
+__global__ void __launch_bounds__(64)
+bdsv_rows_kernel(BdsvArgs<T> a) {
+  static_assert(SS <= 16, "one 16-lane row per problem");
+  constexpr int NGU = SS + 1;  // columns of [G | u]
+  constexpr int NW = 2 * SS + 1;
+  constexpr int SW = 3 * SS;   // S row width
+  constexpr int ES = (int)sizeof(T);
+  const int kp = a.kp;
+  const int lane = threadIdx.x;
+  const int r = lane >> 4, i = lane & 15;
+  const long long p0 = (long long)blockIdx.x * kRowsProblemsPerWave;
+  const int nlive = (int)((long long)a.n_problems - p0 < kRowsProblemsPerWave
+                              ? (long long)a.n_problems - p0
+                              : kRowsProblemsPerWave);
+  const long long prob = p0 + r;
+  const bool act = r < nlive && i < SS;  // this lane owns row i of a problem
+  const int n = kp * SS;
+
+  // Range-checked views of this wave's problems: lanes that own no row use
+  // an offset past the end, so they read zeros and write nothing.
+  const int ps_bytes = n * SW * ES;
+  const __amdgpu_buffer_rsrc_t rS = make_rsrc(a.S + p0 * n * SW, nlive * ps_bytes);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(a.b + p0 * n, nlive * n * ES);
+  const int oS = act ? r * ps_bytes + i * SW * ES : INT_MAX / 2;
+  const int ob = act ? (r * n + i) * ES : INT_MAX / 2;
+  __amdgpu_buffer_rsrc_t rW = make_rsrc(a.S, 0);
+  int oW = INT_MAX / 2;
+  if constexpr (WS) {
+    rW = make_rsrc(a.ws + p0 * n * NGU, nlive * n * NGU * ES);
+    oW = act ? (r * n + i) * NGU * ES : INT_MAX / 2;
+  }
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* GUl = reinterpret_cast<T*>(smem_raw);  // !WS: [kp][4*ss][ss+1]
+
+  T sr[SW], sb;
+  auto load_row = [&](int br) {
+    const int o = oS + br * SS * SW * ES;
+#pragma unroll
+    for (int c = 0; c < SW; ++c) sr[c] = rsrc_load(rS, o + c * ES, T(0));
+    sb = rsrc_load(rb, ob + br * SS * ES, T(0));
+  };
+  load_row(0);
+
+  T W[NW];
+  T gp[NGU];  // this lane's row of [G_{br-1} | u_{br-1}]
+#pragma unroll
+  for (int j = 0; j < NGU; ++j) gp[j] = T(0);
+  bool bad = false;
+  for (int br = 0; br < kp; ++br) {
+    // W = [D | R | b] - L [G_{br-1} | 0 | u_{br-1}]; L, D, R from the S row.
+#pragma unroll
+    for (int j = 0; j < SS; ++j) {
+      W[j] = sr[SS + j];
+      W[SS + j] = br + 1 < kp ? sr[2 * SS + j] : T(0);
+    }
+    W[2 * SS] = sb;
+    if (br > 0) {
+      static_for<0, SS>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        const T nl = -sr[m];
+#pragma unroll
+        for (int j = 0; j < SS; ++j) W[j] = fma(row_bcast<m>(gp[j]), nl, W[j]);
+        W[2 * SS] = fma(row_bcast<m>(gp[SS]), nl, W[2 * SS]);
+      });
+    }
+    if (br + 1 < kp) load_row(br + 1);
+
+    // Gauss-Jordan without normalising the pivot row (see the file header).
+    T mypiv = T(1);
+    static_for<0, SS>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const T piv = row_bcast<k>(W[k]);
+      bad = bad || !(piv > T(0)) || !is_finite_val(piv);
+      mypiv = i == k ? piv : mypiv;
+      const T nf = i == k ? T(0) : -(W[k] * recip(piv));
+#pragma unroll
+      for (int j = k + 1; j < NW; ++j) W[j] = fma(row_bcast<k>(W[j]), nf, W[j]);
+    });
+    const T inv = recip(mypiv);
+#pragma unroll
+    for (int j = 0; j < SS; ++j) gp[j] = W[SS + j] * inv;
+    gp[SS] = W[2 * SS] * inv;
+
+    if constexpr (WS) {
+      const int o = oW + br * SS * NGU * ES;
+#pragma unroll
+      for (int j = 0; j < NGU; ++j) rsrc_store(rW, o + j * ES, gp[j]);
+    } else {
+      if (act) {
+        T* dst = GUl + ((size_t)br * kRowsProblemsPerWave * SS + r * SS + i) * NGU;
+#pragma unroll
+        for (int j = 0; j < NGU; ++j) dst[j] = gp[j];
+      }
+    }
+  }
+
+  // Back substitution: x_{kp-1} = u_{kp-1}; x_br = u_br - G_br x_{br+1}.
+  if constexpr (WS) {
+    // This wave's workspace stores must be complete before the lanes read
+    // them back.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  } else {
+    wave_lds_sync();
+  }
+  T* gx = a.x + prob * n;
+  const bool write = act && !bad;
+  T xv = gp[SS];  // x_{kp-1}[i] (G_{kp-1} is zero)
+  if (write) gx[(long long)(kp - 1) * SS + i] = xv;
+  T rowA[NGU], rowB[NGU];
+  auto load_gu = [&](T (&row)[NGU], int br) {
+    if constexpr (WS) {
+      const int o = oW + br * SS * NGU * ES;
+#pragma unroll
+      for (int j = 0; j < NGU; ++j) row[j] = rsrc_load(rW, o + j * ES, T(0));
+    } else {
+      const T* src = GUl + ((size_t)br * kRowsProblemsPerWave * SS + r * SS + (i < SS ? i : 0)) * NGU;
+#pragma unroll
+      for (int j = 0; j < NGU; ++j) row[j] = i < SS ? src[j] : T(0);
+    }
+  };
+  auto apply = [&](const T (&row)[NGU], int br) {
+    T acc0 = row[SS], acc1 = T(0);
+    static_for<0, SS>([&](auto jc) {
+      constexpr int j = decltype(jc)::value;
+      const T xj = row_bcast<j>(xv);
+      if constexpr (j % 2 == 0) acc0 = fma(-row[j], xj, acc0);
+      else acc1 = fma(-row[j], xj, acc1);
+    });
+    xv = acc0 + acc1;
+    if (write) gx[(long long)br * SS + i] = xv;
+  };
+  int br = kp - 2;
+  if (br >= 0) load_gu(rowA, br);
+  while (br >= 0) {
+    if (br - 1 >= 0) load_gu(rowB, br - 1);
+    apply(rowA, br);
+    --br;
+    if (br < 0) break;
+    if (br - 1 >= 0) load_gu(rowA, br - 1);
+    apply(rowB, br);
+    --br;
+  }
+  if (i == 0 && r < nlive && a.status)
+    a.status[prob] = bad ? GLASS_BDSV_NOT_SPD : GLASS_BDSV_OK;
+}
+
+template <typename T, int SS, bool WS>
+int launch_rows_kernel(const BdsvArgs<T>& a, size_t lds, hipStream_t st) {
+  auto kern = bdsv_rows_kernel<T, SS, WS>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(bdsv rows)");
+  }
+  const unsigned grid =
+      (unsigned)(((long long)a.n_problems + kRowsProblemsPerWave - 1) / kRowsProblemsPerWave);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(64), lds, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "bdsv launch");
+  return GLASS_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launch
+// ---------------------------------------------------------------------------
+
 template <typename T, int SS, bool WS>
 int launch_kernel(const BdsvArgs<T>& a, size_t lds, hipStream_t st) {
   auto kern = bdsv_kernel<T, SS, WS>;
@@ -254,13 +512,6 @@ int launch_typed(T* x, const T* S, const T* b, int kp, int n_problems, int* stat
                  hipStream_t st) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
-  constexpr int NVS = strip_slots<T, SS>();
-  const size_t blocks = ws ? 1 : (size_t)kp;  // [G|u] blocks held in LDS
-  const size_t lds = ((size_t)NVS * 64 * 16) + (blocks * SS * (SS + 1) + 2 * SS) * sizeof(T);
-  if (lds > dev.max_lds_per_block)
-    return fail(GLASS_EUNSUPPORTED,
-                "bdsv: knot_points*state_size*(state_size+1) elements exceed LDS "
-                "(pass a workspace)");
   BdsvArgs<T> a;
   a.x = x;
   a.S = S;
@@ -270,7 +521,26 @@ int launch_typed(T* x, const T* S, const T* b, int kp, int n_problems, int* stat
   a.ss = SS;
   a.kp = kp;
   a.n_problems = n_problems;
+  constexpr int NVS = strip_slots<T, SS>();
   a.strip_vecs = NVS;
+  // Row mapping where it applies: a workspace, or four problems' factors in
+  // LDS.  Byte offsets inside one wave's four problems must fit in an int.
+  const bool columns = env_int("GLASS_AMD_BDSV_COLUMNS", 0) != 0;  // A/B and tests
+  if constexpr (SS <= 16) {
+    const double wave_bytes =
+        (double)kRowsProblemsPerWave * kp * SS * 3 * SS * sizeof(T);
+    const size_t rows_lds =
+        ws ? 0 : (size_t)kp * kRowsProblemsPerWave * SS * (SS + 1) * sizeof(T);
+    if (!columns && wave_bytes < (double)(INT_MAX / 2) && rows_lds <= dev.max_lds_per_block)
+      return ws ? launch_rows_kernel<T, SS, true>(a, rows_lds, st)
+                : launch_rows_kernel<T, SS, false>(a, rows_lds, st);
+  }
+  const size_t blocks = ws ? 1 : (size_t)kp;  // [G|u] blocks held in LDS
+  const size_t lds = ((size_t)NVS * 64 * 16) + (blocks * SS * (SS + 1) + 2 * SS) * sizeof(T);
+  if (lds > dev.max_lds_per_block)
+    return fail(GLASS_EUNSUPPORTED,
+                "bdsv: knot_points*state_size*(state_size+1) elements exceed LDS "
+                "(pass a workspace)");
   return ws ? launch_kernel<T, SS, true>(a, lds, st) : launch_kernel<T, SS, false>(a, lds, st);
 }
 

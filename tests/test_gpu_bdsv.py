@@ -19,6 +19,18 @@ from gpu_common import X_REL, pcg_gpu, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["rows", "columns"])
+def mapping(request, monkeypatch):
+    """The two kernel mappings: four problems per wave with one row of W per
+    lane (state sizes up to 16), or one problem per wave with one column per
+    lane (forced here with GLASS_AMD_BDSV_COLUMNS)."""
+    if request.param == "columns":
+        monkeypatch.setenv("GLASS_AMD_BDSV_COLUMNS", "1")
+    else:
+        monkeypatch.delenv("GLASS_AMD_BDSV_COLUMNS", raising=False)
+    return request.param
+
+
 def bdsv_gpu(glass, S, b, ss, kp, x0=None, ws=False):
     """ws: keep the per-block-row factors in a workspace in HBM instead of
     LDS (the two placements must agree bit for bit)."""
@@ -47,10 +59,10 @@ def assert_bdsv_parity(S, b, ss, kp, x, st, dtype):
 
 @pytest.mark.parametrize("ws", [False, True])
 @pytest.mark.parametrize("cfg,B", [(0, 64), (2, 33), (3, 9)])
-def test_bdsv_workload_shapes(gpu, cfg, B, ws):
+def test_bdsv_workload_shapes(gpu, cfg, B, ws, mapping):
     w = workloads.CONFIGS[cfg]
     inp = workloads.generate(w, n_problems=B)
-    say("bdsv cfg%d shape ss=%d kp=%d B=%d ws=%s" % (cfg, w.ss, w.kp, B, ws))
+    say("bdsv cfg%d shape ss=%d kp=%d B=%d ws=%s %s" % (cfg, w.ss, w.kp, B, ws, mapping))
     x, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp, ws=ws)
     assert np.all(st == gpu.BDSV_OK)
     assert_bdsv_parity(inp["S"], inp["b"], w.ss, w.kp, x, st, np.float32)
@@ -74,14 +86,15 @@ def test_bdsv_full_batch_ss14_both_placements(gpu):
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 @pytest.mark.parametrize("ss,kp,B", [(1, 1, 3), (1, 300, 2), (2, 5, 4), (5, 1, 3),
                                      (7, 40, 3), (12, 64, 2), (16, 20, 2), (24, 12, 2),
-                                     (13, 7, 3)])
-def test_bdsv_edge_shapes(gpu, ss, kp, B, dtype, ws):
+                                     (13, 7, 3), (6, 10, 7), (14, 3, 5), (16, 9, 9),
+                                     (3, 2, 1)])
+def test_bdsv_edge_shapes(gpu, ss, kp, B, dtype, ws, mapping):
     rng = np.random.default_rng(ss * 1000 + kp)
     S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.2, dtype)
     S[:, 0, :, :ss] = 3.0        # off-matrix blocks are ignored
     S[:, -1, :, 2 * ss:] = -3.0
     b = rng.standard_normal((B, kp * ss)).astype(dtype)
-    say("bdsv ss=%d kp=%d B=%d %s ws=%s" % (ss, kp, B, np.dtype(dtype).name, ws))
+    say("bdsv ss=%d kp=%d B=%d %s ws=%s %s" % (ss, kp, B, np.dtype(dtype).name, ws, mapping))
     x, st = bdsv_gpu(gpu, S, b, ss, kp, ws=ws)
     assert np.all(st == gpu.BDSV_OK)
     assert_bdsv_parity(S, b, ss, kp, x, st, dtype)
@@ -100,7 +113,7 @@ def test_bdsv_golden_fixtures(gpu, name):
 
 
 @pytest.mark.parametrize("ws", [False, True])
-def test_bdsv_not_spd_leaves_x_and_flags(gpu, ws):
+def test_bdsv_not_spd_leaves_x_and_flags(gpu, ws, mapping):
     rng = np.random.default_rng(12)
     ss, kp, B = 6, 10, 4
     S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.3, np.float32)
@@ -108,7 +121,7 @@ def test_bdsv_not_spd_leaves_x_and_flags(gpu, ws):
     S[3, 4, :, ss:2 * ss] = 0.0   # a singular diagonal block mid-chain
     b = rng.standard_normal((B, kp * ss)).astype(np.float32)
     x0 = np.full((B, kp * ss), 5.0, np.float32)
-    say("bdsv status cases ws=%s" % ws)
+    say("bdsv status cases ws=%s %s" % (ws, mapping))
     x, st = bdsv_gpu(gpu, S, b, ss, kp, x0=x0, ws=ws)
     _, so = oracle.bdsv(S, b, ss, kp, "f32")
     np.testing.assert_array_equal(st, so)
@@ -147,3 +160,30 @@ def test_bdsv_lds_limit_is_reported_and_the_workspace_lifts_it(gpu):
     xg, st = bdsv_gpu(gpu, S, b, ss, kp, ws=True)
     assert np.all(st == gpu.BDSV_OK)
     assert_bdsv_parity(S, b, ss, kp, xg, st, np.float32)
+
+
+def test_bdsv_rows_and_columns_meet_the_oracle_on_the_full_batch(gpu, monkeypatch):
+    """Both mappings on all 4096 ss=14 kp=32 systems, each against the
+    oracle (they round differently, so they are not compared bit for bit)."""
+    w = workloads.CONFIGS[2]
+    inp = workloads.generate(w)
+    for cols in ("0", "1"):
+        monkeypatch.setenv("GLASS_AMD_BDSV_COLUMNS", cols)
+        say("bdsv full ss=14 kp=32 columns=%s" % cols)
+        x, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp, ws=True)
+        assert np.all(st == gpu.BDSV_OK)
+        assert_bdsv_parity(inp["S"], inp["b"], w.ss, w.kp, x, st, np.float32)
+
+
+def test_bdsv_long_chain_without_workspace_uses_the_column_mapping(gpu):
+    """ss=14, kp=100 without a workspace: four problems' factors (336 KB)
+    do not fit in LDS for the row mapping, one problem's (84 KB) do, so the
+    solve runs (column mapping) and meets the oracle."""
+    rng = np.random.default_rng(31)
+    ss, kp, B = 14, 100, 5
+    S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.2, np.float32)
+    b = rng.standard_normal((B, kp * ss)).astype(np.float32)
+    say("bdsv ss=14 kp=100 no workspace")
+    x, st = bdsv_gpu(gpu, S, b, ss, kp)
+    assert np.all(st == gpu.BDSV_OK)
+    assert_bdsv_parity(S, b, ss, kp, x, st, np.float32)
