@@ -77,7 +77,7 @@ VARIANT_OF = {
 
 def workload_of(key):
     from dataclasses import replace
-    w = workloads.CONFIGS[CONFIG_OF[key]]
+    w = workloads.WORKLOADS[CONFIG_OF[key]]
     return replace(w, **VARIANT_OF[key]) if key in VARIANT_OF else w
 
 
@@ -136,12 +136,12 @@ def time_cpu(fn, budget_s: float):
 # measured HBM traffic (profiles/hbm_traffic.md)
 # --------------------------------------------------------------------------
 
-def read_traffic():
+def read_traffic(path=TRAFFIC_FILE):
     """{kernel key: calibrated bytes per dispatch} if the recorded source hash
     matches the current sources, else {}."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return {}
-    text = open(TRAFFIC_FILE).read()
+    text = open(path).read()
     m = re.search(r"kernel source sha256: ([0-9a-f]{64})", text)
     if not m or m.group(1) != kernel_source_hash():
         return {}
@@ -184,7 +184,7 @@ def _per_dispatch(path, counter):
     return out
 
 
-def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd):
+def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd, out=TRAFFIC_FILE):
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
 
@@ -224,8 +224,8 @@ def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd):
             continue
         b = f * 1024.0 * fr + wv * 1024.0 * fw
         lines.append("| %s | %s | %d | %.1f | %.1f | %.0f |" % (key, sub, nd, f, wv, b))
-    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-    with open(TRAFFIC_FILE, "w") as fh:
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
@@ -269,6 +269,35 @@ def roofline(nbytes, avg_ms, traffic):
     return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
             "algorithmic_bytes_per_launch": nbytes}
+
+
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X dense fp32 vector
+FP64_VECTOR_PEAK_TFLOPS = 78.6
+
+
+def algorithmic_flops_bdsv(w) -> float:
+    """Floating-point operations of one direct solve by the plainest block
+    elimination (a multiply-add counts two): per block-row, factor the pivot
+    block by Cholesky (2 ss^3 / 3) and solve it for the ss+1 columns of
+    [R | y] (2 ss^2 (ss+1)); for every block-row after the first, the update
+    [D | b] - L [G | u] (2 ss^2 (ss+1)); the back substitution x_br = u_br -
+    G_br x_{br+1} (2 ss^2 per block-row after the last)."""
+    ss, kp = w.ss, w.kp
+    per_row = 2.0 * ss ** 3 / 3.0 + 2.0 * ss * ss * (ss + 1)
+    return kp * per_row + (kp - 1) * (2.0 * ss * ss * (ss + 1) + 2.0 * ss * ss)
+
+
+def roofline_alu(flops, nbytes, avg_ms, traffic, dtype):
+    """Arithmetic-bound kernel: useful FLOP/s against the vector peak of its
+    dtype; the HBM rate of its algorithmic bytes is given beside it."""
+    peak = FP32_VECTOR_PEAK_TFLOPS if np.dtype(dtype) == np.float32 else FP64_VECTOR_PEAK_TFLOPS
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    gbs = nbytes / (avg_ms * 1e-3) / 1e9
+    return {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+            "frac": achieved / peak, "traffic": traffic,
+            "algorithmic_flops_per_launch": flops,
+            "algorithmic_bytes_per_launch": nbytes,
+            "hbm_achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
 
 
 def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
@@ -347,7 +376,7 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
 
 
 def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu, traffic):
-    w = workloads.CONFIGS[1]
+    w = workloads.WORKLOADS[1]
     inp = workloads.generate(w)
     dev = torch.device("cuda:0")
     S = torch.from_numpy(inp["S"]).to(dev)
@@ -428,7 +457,8 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
         "kernel_ms_isolated": iso,
         "not_spd": int((status.cpu().numpy() != 0).sum()),
-        "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
+        "roofline": roofline_alu(B * algorithmic_flops_bdsv(w), nbytes, avg_ms, traffic.get(key),
+                                 w.dtype),
     }
     if with_cpu:
         import oracle
@@ -470,8 +500,8 @@ def main():
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], *args.pmc_commands)
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(problems are independent; DESIGN.md describes how it would shard)",
+        print("bench.py measures one GPU only: there is no multi-GPU path (the batched "
+              "problems are independent, so a batch would be split across GPUs)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -504,7 +534,7 @@ def main():
         calibration_copy(torch)
 
     head = res.get("pcg3") or next(iter(res.values()))
-    w = workloads.CONFIGS[3]
+    w = workloads.WORKLOADS[3]
     line = {
         "metric": METRIC,
         "value": head.get("solves_per_s", head.get("gb_per_s")),

@@ -386,9 +386,12 @@ bdsv_rows_kernel(BdsvArgs<T> a) {
       static_for<0, SS>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
         const T nl = -sr[m];
+        T t[NGU];  // row m of [G | u], issued before it is used
 #pragma unroll
-        for (int j = 0; j < SS; ++j) W[j] = fma(row_bcast<m>(gp[j]), nl, W[j]);
-        W[2 * SS] = fma(row_bcast<m>(gp[SS]), nl, W[2 * SS]);
+        for (int j = 0; j < NGU; ++j) t[j] = row_bcast<m>(gp[j]);
+#pragma unroll
+        for (int j = 0; j < SS; ++j) W[j] = fma(t[j], nl, W[j]);
+        W[2 * SS] = fma(t[SS], nl, W[2 * SS]);
       });
     }
     if (br + 1 < kp) load_row(br + 1);
@@ -398,11 +401,16 @@ bdsv_rows_kernel(BdsvArgs<T> a) {
     static_for<0, SS>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       const T piv = row_bcast<k>(W[k]);
+      // The pivot row's broadcasts do not wait for the multiplier, so they
+      // cover the latency of the reciprocal.
+      T t[NW];
+#pragma unroll
+      for (int j = k + 1; j < NW; ++j) t[j] = row_bcast<k>(W[j]);
       bad = bad || !(piv > T(0)) || !is_finite_val(piv);
       mypiv = i == k ? piv : mypiv;
       const T nf = i == k ? T(0) : -(W[k] * recip(piv));
 #pragma unroll
-      for (int j = k + 1; j < NW; ++j) W[j] = fma(row_bcast<k>(W[j]), nf, W[j]);
+      for (int j = k + 1; j < NW; ++j) W[j] = fma(t[j], nf, W[j]);
     });
     const T inv = recip(mypiv);
 #pragma unroll
@@ -449,12 +457,16 @@ bdsv_rows_kernel(BdsvArgs<T> a) {
   };
   auto apply = [&](const T (&row)[NGU], int br) {
     T acc0 = row[SS], acc1 = T(0);
+    T xb[SS];  // x_{br+1}, one entry per lane of the row
     static_for<0, SS>([&](auto jc) {
       constexpr int j = decltype(jc)::value;
-      const T xj = row_bcast<j>(xv);
-      if constexpr (j % 2 == 0) acc0 = fma(-row[j], xj, acc0);
-      else acc1 = fma(-row[j], xj, acc1);
+      xb[j] = row_bcast<j>(xv);
     });
+#pragma unroll
+    for (int j = 0; j < SS; ++j) {
+      if (j % 2 == 0) acc0 = fma(-row[j], xb[j], acc0);
+      else acc1 = fma(-row[j], xb[j], acc1);
+    }
     xv = acc0 + acc1;
     if (write) gx[(long long)br * SS + i] = xv;
   };

@@ -26,7 +26,7 @@ def random_case(seed, B, ss, kp, dtype, garbage=True):
 
 def test_bdmv_workload_shape_several_tiles_ragged(gpu):
     """ss=14, kp=64: 896 rows per problem = 3 full 256-row tiles + a half tile."""
-    w = workloads.CONFIGS[1]
+    w = workloads.WORKLOADS[1]
     inp = workloads.generate(w, n_problems=37)
     say("bdmv ss=14 kp=64 B=37")
     y = bdmv_gpu(gpu, inp["S"], inp["v"], w.ss, w.kp)
@@ -36,7 +36,7 @@ def test_bdmv_workload_shape_several_tiles_ragged(gpu):
 
 def test_bdmv_full_workload_all_problems(gpu):
     """The full 8192-problem fp32 workload, every row checked."""
-    w = workloads.CONFIGS[1]
+    w = workloads.WORKLOADS[1]
     inp = workloads.generate(w)
     say("bdmv full ss=14 kp=64 B=8192")
     y = bdmv_gpu(gpu, inp["S"], inp["v"], w.ss, w.kp)

@@ -60,7 +60,7 @@ def assert_bdsv_parity(S, b, ss, kp, x, st, dtype):
 @pytest.mark.parametrize("ws", [False, True])
 @pytest.mark.parametrize("cfg,B", [(0, 64), (2, 33), (3, 9)])
 def test_bdsv_workload_shapes(gpu, cfg, B, ws, mapping):
-    w = workloads.CONFIGS[cfg]
+    w = workloads.WORKLOADS[cfg]
     inp = workloads.generate(w, n_problems=B)
     say("bdsv cfg%d shape ss=%d kp=%d B=%d ws=%s %s" % (cfg, w.ss, w.kp, B, ws, mapping))
     x, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp, ws=ws)
@@ -71,7 +71,7 @@ def test_bdsv_workload_shapes(gpu, cfg, B, ws, mapping):
 def test_bdsv_full_batch_ss14_both_placements(gpu):
     """All 4096 systems of the ss=14, kp=32 workload, every x checked; the
     LDS and the workspace placements give the same bits."""
-    w = workloads.CONFIGS[2]
+    w = workloads.WORKLOADS[2]
     inp = workloads.generate(w)
     say("bdsv full ss=14 kp=32 B=4096")
     x, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp)
@@ -133,7 +133,7 @@ def test_bdsv_not_spd_leaves_x_and_flags(gpu, ws, mapping):
 def test_bdsv_agrees_with_gpu_pcg_and_is_deterministic(gpu):
     """The direct solve meets the GPU's PCG solution to PCG's own accuracy,
     and repeats bit for bit."""
-    w = workloads.CONFIGS[0]
+    w = workloads.WORKLOADS[0]
     inp = workloads.generate(w)
     say("bdsv vs pcg")
     x1, st = bdsv_gpu(gpu, inp["S"], inp["b"], w.ss, w.kp)
@@ -165,7 +165,7 @@ def test_bdsv_lds_limit_is_reported_and_the_workspace_lifts_it(gpu):
 def test_bdsv_rows_and_columns_meet_the_oracle_on_the_full_batch(gpu, monkeypatch):
     """Both mappings on all 4096 ss=14 kp=32 systems, each against the
     oracle (they round differently, so they are not compared bit for bit)."""
-    w = workloads.CONFIGS[2]
+    w = workloads.WORKLOADS[2]
     inp = workloads.generate(w)
     for cols in ("0", "1"):
         monkeypatch.setenv("GLASS_AMD_BDSV_COLUMNS", cols)

@@ -31,7 +31,7 @@ def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, exclusive=False):
 
 def test_grid_full_chain_fp64(gpu):
     """The kp=8192, ss=12 fp64 chain, every entry of x checked."""
-    w = workloads.CONFIGS[4]
+    w = workloads.WORKLOADS[4]
     inp = workloads.generate(w)
     say("grid ss=12 kp=8192 fp64")
     res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
@@ -109,7 +109,7 @@ def test_grid_full_chain_fp32_variant(gpu):
     """The float32 variant of the kp=8192 chain as bench.py times it
     (rel_tol 1e-7), every entry of x checked."""
     from dataclasses import replace
-    w = replace(workloads.CONFIGS[4], dtype=np.float32, rel_tol=1e-7)
+    w = replace(workloads.WORKLOADS[4], dtype=np.float32, rel_tol=1e-7)
     inp = workloads.generate(w)
     say("grid ss=12 kp=8192 fp32")
     res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
@@ -125,8 +125,8 @@ def test_grid_exclusive_launch_is_bit_identical(gpu, ss, kp, dtype):
     also on two solves in a row that reuse the workspace."""
     if kp == 8192:
         from dataclasses import replace
-        w = replace(workloads.CONFIGS[4], dtype=dtype,
-                    rel_tol=1e-7 if dtype == np.float32 else workloads.CONFIGS[4].rel_tol)
+        w = replace(workloads.WORKLOADS[4], dtype=dtype,
+                    rel_tol=1e-7 if dtype == np.float32 else workloads.WORKLOADS[4].rel_tol)
         inp = workloads.generate(w)
         rel = w.rel_tol
     else:

@@ -15,7 +15,7 @@ pytestmark = pytest.mark.gpu
 
 
 def run_workload(gpu, cfg, n_problems=None, dtype=None):
-    w = workloads.CONFIGS[cfg]
+    w = workloads.WORKLOADS[cfg]
     inp = workloads.generate(w, n_problems=n_problems)
     if dtype is not None:
         inp = {k: v.astype(dtype) for k, v in inp.items()}
@@ -47,7 +47,7 @@ def test_pcg_placements_bit_identical(gpu, monkeypatch):
     chunk order and every row is contracted serially in index order, so the
     register-resident placement and the streamed placements at 1, 2, 3, 4
     and 8 rows per lane (1 to 7 waves) give the same bits."""
-    w = workloads.CONFIGS[2]
+    w = workloads.WORKLOADS[2]
     inp = workloads.generate(w, n_problems=24)
     ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
     assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, ref, np.float32)
@@ -138,7 +138,7 @@ def test_pcg_status_cases(gpu):
 
 
 def test_pcg_max_iters_exhausted(gpu):
-    w = workloads.CONFIGS[2]
+    w = workloads.WORKLOADS[2]
     inp = workloads.generate(w, n_problems=8)
     say("pcg max_iters=2")
     res = pcg_gpu(gpu, inp, w.ss, w.kp, 2, w.rel_tol, w.abs_tol)
@@ -147,7 +147,7 @@ def test_pcg_max_iters_exhausted(gpu):
 
 
 def test_pcg_run_to_run_deterministic(gpu):
-    w = workloads.CONFIGS[3]
+    w = workloads.WORKLOADS[3]
     inp = workloads.generate(w, n_problems=12)
     a = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
     b = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
@@ -156,7 +156,7 @@ def test_pcg_run_to_run_deterministic(gpu):
 
 
 def test_pcg_rejects_inconsistent_buffers(gpu):
-    w = workloads.CONFIGS[0]
+    w = workloads.WORKLOADS[0]
     inp = workloads.generate(w, n_problems=2)
     t = {k: torch.from_numpy(v).cuda() for k, v in inp.items()}
     it = torch.zeros(2, dtype=torch.int32, device="cuda")
@@ -170,7 +170,7 @@ def test_pcg_rejects_inconsistent_buffers(gpu):
 def test_pcg_prefetch_ring_matches_plain_staging(gpu, monkeypatch):
     """The prefetching and the plain streamed placements stage the same bytes
     and run the same arithmetic in the same order: bit-identical outputs."""
-    w = workloads.CONFIGS[3]
+    w = workloads.WORKLOADS[3]
     inp = workloads.generate(w, n_problems=10)
     say("pcg cfg3 prefetch vs plain staging")
     a = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)

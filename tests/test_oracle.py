@@ -122,7 +122,7 @@ def test_bdmv_symmetry_of_generated_matrix():
 def test_bdmv_f32_within_dot_error_bound():
     """Float32 accumulation stays inside the classical dot-product bound
     gamma_k * sum|a_i b_i| (Higham, Accuracy and Stability, sec. 3.1)."""
-    w = workloads.CONFIGS[1]
+    w = workloads.WORKLOADS[1]
     inp = workloads.generate(w, n_problems=4)
     S, v = inp["S"], inp["v"]
     y64 = oracle.bdmv(S, v, w.ss, w.kp, "f64")
@@ -138,7 +138,7 @@ def test_bdmv_f32_within_dot_error_bound():
 
 
 def test_bdmv_threads_bitwise_equal():
-    w = workloads.CONFIGS[1]
+    w = workloads.WORKLOADS[1]
     inp = workloads.generate(w, n_problems=9)
     a = oracle.bdmv(inp["S"], inp["v"], w.ss, w.kp, "f32", nthreads=1)
     b = oracle.bdmv(inp["S"], inp["v"], w.ss, w.kp, "f32", nthreads=4)
@@ -324,7 +324,7 @@ def test_pcg_iteration_count_is_first_to_meet_criterion():
     """The returned x meets |r^T z| < abs + rel*|rho_init| (recomputed densely
     in fp64) and one iteration fewer does not: catches a test placed before
     or after the right point, and a non-strict comparison drift."""
-    w = workloads.CONFIGS[0]
+    w = workloads.WORKLOADS[0]
     inp = workloads.generate(w, n_problems=8)
     S = inp["S"].astype(np.float64)
     P = inp["Pinv"].astype(np.float64)
@@ -385,7 +385,7 @@ def test_pcg_status_cases():
 def test_pcg_f32_close_to_f64_on_config0():
     """The float32 solve stays within 1e-4 of the float64 solve at equal
     iteration counts (well-conditioned: block-Jacobi kappa ~ 2)."""
-    w = workloads.CONFIGS[0]
+    w = workloads.WORKLOADS[0]
     inp = workloads.generate(w, n_problems=16)
     x32, it32, st32, _ = oracle.pcg(inp["x0"], inp["S"], inp["Pinv"], inp["b"],
                                     w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, "f32")
@@ -401,7 +401,7 @@ def test_pcg_f32_close_to_f64_on_config0():
 
 
 def test_pcg_threads_bitwise_equal():
-    w = workloads.CONFIGS[2]
+    w = workloads.WORKLOADS[2]
     inp = workloads.generate(w, n_problems=6)
     a = oracle.pcg(inp["x0"], inp["S"], inp["Pinv"], inp["b"], w.ss, w.kp,
                    w.max_iters, w.rel_tol, w.abs_tol, "f32", nthreads=1)
@@ -510,7 +510,7 @@ def test_bdsv_not_spd_status_leaves_x():
 
 def test_bdsv_agrees_with_converged_pcg():
     """The direct and the iterative solve of the same SPD systems meet."""
-    w = workloads.CONFIGS[0]
+    w = workloads.WORKLOADS[0]
     inp = workloads.generate(w, n_problems=6)
     S64, P64, b64 = (inp[k].astype(np.float64) for k in ("S", "Pinv", "b"))
     xd, st = oracle.bdsv(S64, b64, w.ss, w.kp)
@@ -520,7 +520,7 @@ def test_bdsv_agrees_with_converged_pcg():
 
 
 def test_bdsv_f32_close_to_f64():
-    w = workloads.CONFIGS[2]
+    w = workloads.WORKLOADS[2]
     inp = workloads.generate(w, n_problems=4)
     x32, _ = oracle.bdsv(inp["S"], inp["b"], w.ss, w.kp, "f32")
     x64, _ = oracle.bdsv(inp["S"].astype(np.float64), inp["b"].astype(np.float64), w.ss, w.kp)

@@ -8,7 +8,7 @@ import workloads
 
 
 def test_generator_is_deterministic_and_prefix_stable():
-    w = workloads.CONFIGS[0]
+    w = workloads.WORKLOADS[0]
     a = workloads.generate(w, n_problems=10)
     b = workloads.generate(w, n_problems=10)
     c = workloads.generate(w, n_problems=3, chunk=2)
@@ -19,7 +19,7 @@ def test_generator_is_deterministic_and_prefix_stable():
 
 @pytest.mark.parametrize("cfg", [0, 2, 3])
 def test_generated_matrix_is_symmetric_spd_with_margin(cfg):
-    w = workloads.CONFIGS[cfg]
+    w = workloads.WORKLOADS[cfg]
     inp = workloads.generate(w, n_problems=2)
     for q in range(2):
         A = oracle.dense_expand(inp["S"][q].astype(np.float64), w.ss, w.kp)
@@ -34,7 +34,7 @@ def test_generated_matrix_is_symmetric_spd_with_margin(cfg):
 
 
 def test_off_matrix_blocks_and_pads_are_zero():
-    w = workloads.CONFIGS[1]
+    w = workloads.WORKLOADS[1]
     inp = workloads.generate(w, n_problems=3)
     S, v = inp["S"], inp["v"]
     assert S.shape == (3, w.kp, w.ss, 3 * w.ss) and S.dtype == np.float32
@@ -44,7 +44,7 @@ def test_off_matrix_blocks_and_pads_are_zero():
 
 
 def test_pinv_is_block_jacobi_inverse():
-    w = workloads.CONFIGS[2]
+    w = workloads.WORKLOADS[2]
     inp = workloads.generate(w, n_problems=2)
     S = inp["S"].astype(np.float64)
     P = inp["Pinv"].astype(np.float64)
@@ -55,7 +55,7 @@ def test_pinv_is_block_jacobi_inverse():
 
 
 def test_config_table_matches_stated_workloads():
-    c = workloads.CONFIGS
+    c = workloads.WORKLOADS
     assert (c[0].ss, c[0].kp, c[0].n_problems, c[0].dtype) == (6, 32, 64, np.float32)
     assert (c[1].ss, c[1].kp, c[1].n_problems, c[1].kind) == (14, 64, 8192, "bdmv")
     assert (c[2].ss, c[2].kp, c[2].n_problems, c[2].margin) == (14, 32, 4096, 0.2)

@@ -58,7 +58,7 @@ class Workload:
 
 
 # The five workloads of the hot path.  Seed = 1000 + index.
-CONFIGS = {
+WORKLOADS = {
     0: Workload("pcg_ss6_kp32_b64_f32", "pcg", np.float32, 6, 32, 64, 1.0,
                 rel_tol=1e-6, abs_tol=0.0, max_iters=200, seed=1000),
     1: Workload("bdmv_ss14_kp64_b8192_f32", "bdmv", np.float32, 14, 64, 8192,
