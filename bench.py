@@ -60,7 +60,7 @@ KERNEL_OF = {
     "pcg2": "pcg_batched_kernel<float, 14,",
     "pcg3": "pcg_batched_kernel<float, 21,",
     "grid4": "pcg_grid_kernel<double, 12,",
-    "bdsv2": "bdsv_kernel<float, 14,",
+    "bdsv2": "bdsv_rows_kernel<float, 14,",
     "pcg2_f64": "pcg_batched_kernel<double, 14,",
     "grid4_f32": "pcg_grid_kernel<float, 12,",
 }
