@@ -356,6 +356,8 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         "iterations": {str(k): int(v) for k, v in zip(*np.unique(it, return_counts=True))},
         "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
     }
+    if not grid:
+        out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it.max()))
     if grid:
         out["launch"] = "exclusive"
         out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it[0]))
@@ -470,6 +472,27 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     return out
 
 
+def measured_copy_gbs(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate on this GPU (torch copy of 1 GiB; read +
+    write bytes per second), the measured reference the HBM fractions are
+    also given against."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    del src, dst
+    return 2.0 * nbytes / (ms * 1e-3) / 1e9
+
+
 def calibration_copy(torch):
     """A plain streaming kernel of known traffic: y = -x over 1 GiB (reads
     1 GiB, writes 1 GiB).  Its counters calibrate FETCH_SIZE / WRITE_SIZE."""
@@ -532,6 +555,12 @@ def main():
               flush=True)
     if args.calibration_copy:
         calibration_copy(torch)
+    copy_gbs = measured_copy_gbs(torch)
+    for r in res.values():
+        rl = r["roofline"]
+        gbs = rl["achieved"] if rl["bound"] == "hbm" else rl.get("hbm_achieved_gbs")
+        if gbs is not None:
+            rl["frac_of_measured_copy"] = gbs / copy_gbs
 
     head = res.get("pcg3") or next(iter(res.values()))
     w = workloads.WORKLOADS[3]
@@ -548,6 +577,7 @@ def main():
                    "parallelism": "one problem per workgroup"},
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
+        "measured_copy_gbs": copy_gbs,
         "workloads": res,
     }
     print(json.dumps(line), flush=True)
