@@ -63,13 +63,18 @@ KERNEL_OF = {
     "bdsv2": "bdsv_rows_kernel<float, 14,",
     "pcg2_f64": "pcg_batched_kernel<double, 14,",
     "grid4_f32": "pcg_grid_kernel<float, 12,",
+    "pcg2_pd": "pcg_batched_kernel<float, 14, 1, 3>",
 }
 # Workload inputs: the five configurations; bdsv2 is the direct solve of the
 # same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
 # are the precision variants of pcg2 and grid4 (same recipe and seeds).
 CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2,
-             "pcg2_f64": 2, "grid4_f32": 4}
+             "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2}
+# Workloads run with GLASS_PCG_PINV_BLOCK_DIAGONAL (their Pinv is block-Jacobi,
+# so the assertion holds): pcg2_pd is the ss=14 workload with the hint.
+PINV_DIAG = {"pcg2_pd"}
 VARIANT_OF = {
+    "pcg2_pd": dict(name="pcg_ss14_kp32_b4096_f32_pinv_blockdiag"),
     "pcg2_f64": dict(name="pcg_ss14_kp32_b4096_f64", dtype=np.float64),
     "grid4_f32": dict(name="grid_pcg_ss12_kp8192_f32", dtype=np.float32, rel_tol=1e-7),
 }
@@ -95,13 +100,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes_pcg(w, iters: np.ndarray, resident: bool) -> float:
+def algorithmic_bytes_pcg(w, iters: np.ndarray, resident: bool, pinv_diag=False) -> float:
     """Bytes one solve must move between HBM and the chip, by the algorithm:
-    S and Pinv (n*3ss each) once if they stay on chip, else once per pass
-    (the initial S x0 / Pinv r pass plus one per iteration); x read, b read,
-    x written (n each); iters (4 bytes)."""
+    S and Pinv (n*3ss each; Pinv n*ss when only its D blocks are read) once
+    if they stay on chip, else once per pass (the initial S x0 / Pinv r pass
+    plus one per iteration); x read, b read, x written (n each); iters
+    (4 bytes)."""
     es = np.dtype(w.dtype).itemsize
-    mat = 2 * w.n * 3 * w.ss * es
+    mat = (w.n * 3 * w.ss + w.n * (w.ss if pinv_diag else 3 * w.ss)) * es
     vec = 3 * w.n * es + 4
     passes = np.ones_like(iters, dtype=np.float64) if resident else (iters.astype(np.float64) + 1)
     return float(np.sum(passes * mat + vec))
@@ -318,12 +324,15 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
 
     # The grid solve is timed with the exclusive launch (this process is the
     # only user of the device); the cooperative launch is timed after it.
+    pd = key in PINV_DIAG
+
     def run(x, exclusive=True):
         if grid:
             glass.pcg_grid(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters, ws,
                            exclusive=exclusive)
         else:
-            glass.pcg_batched(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters)
+            glass.pcg_batched(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters,
+                              pinv_block_diagonal=pd)
 
     for k in range(warmup):
         run(xs[steps + k])
@@ -341,8 +350,9 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     avg_ms = float(np.mean(launch_ms))
     # S and Pinv count once if they stay on chip (the grid solve and the
     # batched resident placement), else once per pass.
-    resident = grid or glass.pcg_batched_placement(w.ss, w.kp, S.dtype) == glass.PLACEMENT_RESIDENT
-    nbytes = algorithmic_bytes_pcg(w, it, resident)
+    resident = grid or glass.pcg_batched_placement(
+        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd) == glass.PLACEMENT_RESIDENT
+    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd and resident)
     for k in range(min(10, len(xs))):
         xs[k].zero_()
     iso = isolated_ms(torch, lambda k: run(xs[k]), reps=min(10, len(xs)))

@@ -21,6 +21,7 @@ __all__ = [
     "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "bdsv_workspace_bytes",
     "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
+    "PCG_PINV_BLOCK_DIAGONAL",
     "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED",
 ]
@@ -36,6 +37,7 @@ GLASS_F32, GLASS_F64 = 0, 1
 CONVERGED, MAX_ITERS, BREAKDOWN, GRID_TIMEOUT = 0, 1, 2, 3
 BDSV_OK, BDSV_NOT_SPD = 0, 1
 GRID_EXCLUSIVE = 1  # glass_pcg_grid_ex flag: ordinary dispatch on the stream's queue
+PCG_PINV_BLOCK_DIAGONAL = 1  # glass_pcg_batched_ex flag: Pinv's L and R blocks are zero
 
 
 class GlassError(RuntimeError):
@@ -63,10 +65,10 @@ def load():
         sigs = {
             "glass_bdmv_batched": ([P, P, P, I, I, I, I, P], I),
             "glass_pcg_batched": ([P, P, P, P, I, I, I, I, D, D, P, I, P], I),
-            "glass_pcg_batched_ex": ([P, P, P, P, I, I, I, I, D, D, P, P, P, I, P], I),
+            "glass_pcg_batched_ex": ([P, P, P, P, I, I, I, I, D, D, P, P, P, I, U, P], I),
             "glass_bdsv_batched": ([P, P, P, I, I, I, P, P, Z, I, P], I),
             "glass_bdsv_workspace_bytes": ([I, I, I, I], Z),
-            "glass_pcg_batched_placement": ([I, I, I, I], I),
+            "glass_pcg_batched_placement": ([I, I, I, I, U], I),
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
@@ -141,10 +143,12 @@ def bdmv_batched(y, S, v, state_size: int, knot_points: int, stream=None):
 
 def pcg_batched(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
                 rel_tol: float, abs_tol: float, iters_out, status_out=None,
-                rho_out=None, stream=None):
+                rho_out=None, stream=None, pinv_block_diagonal=False):
     """Batched PCG (page "Block-tridiagonal Solves", section "Solve --
     glass::pcg").  x: [B, kp*ss] initial guess in, solution out; iters_out
-    (and status_out) int32 [B]; rho_out dtype [B, 2]."""
+    (and status_out) int32 [B]; rho_out dtype [B, 2].
+    ``pinv_block_diagonal=True`` passes GLASS_PCG_PINV_BLOCK_DIAGONAL: the
+    caller asserts that Pinv's L and R blocks are zero."""
     import torch
     ss, kp = int(state_size), int(knot_points)
     B = _problems(S, ss, kp)
@@ -157,6 +161,7 @@ def pcg_batched(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int
     rh = _dev(rho_out, "rho_out", 2 * B, dt) if rho_out is not None else None
     rc = load().glass_pcg_batched_ex(*a, ss, kp, B, int(max_iters), float(rel_tol),
                                      float(abs_tol), it, st, rh, _dtype_code(S),
+                                     PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0,
                                      _stream(stream))
     _check(rc, "glass_pcg_batched_ex")
 
@@ -194,14 +199,16 @@ def bdsv_batched(x, S, b, state_size: int, knot_points: int, status_out=None,
 PLACEMENT_RESIDENT, PLACEMENT_STREAMED_PREFETCH, PLACEMENT_STREAMED = 0, 1, 2
 
 
-def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=True) -> int:
+def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=True,
+                          pinv_block_diagonal=False) -> int:
     """Where pcg_batched keeps S and Pinv on the current device for this shape:
     PLACEMENT_RESIDENT (read once per solve) or PLACEMENT_STREAMED[_PREFETCH]
     (read once per matvec pass).  Raises for shapes the solve rejects."""
     import torch
     code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
     rc = load().glass_pcg_batched_placement(int(state_size), int(knot_points), code,
-                                            1 if aligned16 else 0)
+                                            1 if aligned16 else 0,
+                                            PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0)
     if rc < 0:
         _check(rc, "glass_pcg_batched_placement")
     return rc

@@ -122,8 +122,10 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
                          const void* b, int state_size, int knot_points,
                          int n_problems, int max_iters, double rel_tol,
                          double abs_tol, int* iters_out, int* status_out,
-                         void* rho_out, glass_dtype dtype, void* hip_stream) {
+                         void* rho_out, glass_dtype dtype, unsigned flags,
+                         void* hip_stream) {
   if (int rc = check_common(dtype, state_size, knot_points, n_problems)) return rc;
+  if (flags & ~(unsigned)GLASS_PCG_PINV_BLOCK_DIAGONAL) return fail(GLASS_EINVAL, "unknown pcg flags");
   if (int rc = check_tols(max_iters, rel_tol, abs_tol)) return rc;
   if ((long long)knot_points * state_size > 8192)
     return fail(GLASS_EUNSUPPORTED, "knot_points*state_size above 8192 (use glass_pcg_grid)");
@@ -139,6 +141,7 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
   return glass::launch_pcg_batched(dtype, x, S, Pinv, b, state_size, knot_points,
                                    n_problems, max_iters, rel_tol, abs_tol,
                                    iters_out, status_out, rho_out,
+                                   (flags & GLASS_PCG_PINV_BLOCK_DIAGONAL) != 0,
                                    (hipStream_t)hip_stream);
 }
 
@@ -148,15 +151,17 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
                       int* iters_out, glass_dtype dtype, void* hip_stream) {
   return glass_pcg_batched_ex(x, S, Pinv, b, state_size, knot_points,
                               n_problems, max_iters, rel_tol, abs_tol,
-                              iters_out, nullptr, nullptr, dtype, hip_stream);
+                              iters_out, nullptr, nullptr, dtype, 0u, hip_stream);
 }
 
 int glass_pcg_batched_placement(int state_size, int knot_points,
-                                glass_dtype dtype, int aligned16) {
+                                glass_dtype dtype, int aligned16, unsigned flags) {
   if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
+  if (flags & ~(unsigned)GLASS_PCG_PINV_BLOCK_DIAGONAL) return fail(GLASS_EINVAL, "unknown pcg flags");
   if ((long long)knot_points * state_size > 8192)
     return fail(GLASS_EUNSUPPORTED, "knot_points*state_size above 8192 (use glass_pcg_grid)");
-  return glass::pcg_batched_placement(dtype, state_size, knot_points, aligned16 != 0);
+  return glass::pcg_batched_placement(dtype, state_size, knot_points, aligned16 != 0,
+                                      (flags & GLASS_PCG_PINV_BLOCK_DIAGONAL) != 0);
 }
 
 size_t glass_bdsv_workspace_bytes(int state_size, int knot_points, int n_problems,

@@ -34,6 +34,12 @@
 //   dots and the workgroup barriers (matrix loads never depend on the
 //   vectors).
 // Barriers per iteration: 4 (p^T Sp, r publish, r^T z, p publish).
+//
+// RESIDENT with a block-diagonal Pinv (the caller asserts its L and R blocks
+// are zero): each lane holds only the D part of its Pinv row and multiplies
+// it with its own block-row of r.  The skipped terms are exact zeros that the
+// general contraction adds after and before the D terms, so the result has
+// the same value; fewer registers let more workgroups share a CU.
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -71,7 +77,7 @@ struct PcgArgs {
 };
 
 // Placements of the matrices (see the header).
-enum Mode { kResident = 0, kStreamPrefetch = 1, kStream = 2 };
+enum Mode { kResident = 0, kStreamPrefetch = 1, kStream = 2, kResidentPD = 3 };
 
 // Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for the
 // prefetching placement (two chunk buffers per lane) and for 3-4 rows per
@@ -84,7 +90,8 @@ constexpr int max_threads_for(int rpt, int mode) {
 template <typename T, int SS, int RPT, int MODE>
 __global__ void __launch_bounds__(max_threads_for(RPT, MODE))
 pcg_batched_kernel(PcgArgs<T> a) {
-  constexpr bool RES = MODE == kResident;
+  constexpr bool RES = MODE == kResident || MODE == kResidentPD;
+  constexpr bool PD = MODE == kResidentPD;  // Pinv rows: D part only
   constexpr bool PFM = MODE == kStreamPrefetch;
   constexpr int WC = SS > 0 ? 3 * SS : 1;  // compile-time width
   const int ss = SS > 0 ? SS : a.ss;
@@ -154,22 +161,25 @@ pcg_batched_kernel(PcgArgs<T> a) {
 
   // RESIDENT: each lane's S and Pinv rows in registers for the whole solve,
   // loaded straight from HBM with every load of both rows in flight.
-  T mS[RES ? RPT : 1][WC], mP[RES ? RPT : 1][WC];
+  constexpr int WCP = PD ? (SS > 0 ? SS : 1) : WC;  // Pinv row width held
+  T mS[RES ? RPT : 1][WC], mP[RES ? RPT : 1][WCP];
   if constexpr (RES) {
     static_assert(!RES || RPT == 1, "resident placement deals one row per lane");
 #pragma unroll
-    for (int c = 0; c < WC; ++c) {
-      mS[0][c] = T(0);
-      mP[0][c] = T(0);
-    }
+    for (int c = 0; c < WC; ++c) mS[0][c] = T(0);
+#pragma unroll
+    for (int c = 0; c < WCP; ++c) mP[0][c] = T(0);
     if (valid[0]) {
       const long long off = (long long)row[0] * WC;
+      // The D part starts ss elements into the row: at (3*row + 1) times its
+      // own byte size, so the widths load_row_regs picks stay aligned.
+      const long long offP = off + (PD ? SS : 0);
       if (vec) {
         load_row_regs<T, WC, true>(mS[0], gS + off);
-        load_row_regs<T, WC, true>(mP[0], gP + off);
+        load_row_regs<T, WCP, true>(mP[0], gP + offP);
       } else {
         load_row_regs<T, WC, false>(mS[0], gS + off);
-        load_row_regs<T, WC, false>(mP[0], gP + off);
+        load_row_regs<T, WCP, false>(mP[0], gP + offP);
       }
     }
   }
@@ -199,8 +209,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
 
   // out[k] = (M * vpad)[row k]: one lane, one row, serial 3*ss contraction.
   // MI selects the matrix: 0 = S, 1 = Pinv.
-  auto matvec = [&](auto mi_tag, T (&out)[RPT], T (&mreg)[RES ? RPT : 1][WC],
-                    const T* __restrict__ vpad) {
+  auto matvec = [&](auto mi_tag, T (&out)[RPT], auto& mreg, const T* __restrict__ vpad) {
     constexpr int MI = decltype(mi_tag)::value;
     const T* __restrict__ gM = MI == 0 ? gS : gP;
 #pragma unroll
@@ -209,8 +218,13 @@ pcg_batched_kernel(PcgArgs<T> a) {
       if constexpr (RES) {
         if (valid[k]) {
           const T* __restrict__ w = vpad + wstart[k];
+          if constexpr (PD && MI == 1) {
 #pragma unroll
-          for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], w[c], acc);
+            for (int c = 0; c < WCP; ++c) acc = fma(mreg[k][c], w[SS + c], acc);
+          } else {
+#pragma unroll
+            for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], w[c], acc);
+          }
         }
       } else {
         const int r0 = chunk_r0(k);
@@ -389,6 +403,7 @@ struct Plan {
   int NW = 0;
   int RPT = 0;
   bool res = false;
+  bool pd = false;  // resident with Pinv's D blocks only
   bool prefetch = false;
   int stage_elems = 0;
   size_t lds = 0;
@@ -409,6 +424,11 @@ template <typename T>
 constexpr bool kResidentFits(int ss) {
   return 6 * ss * (int)sizeof(T) / 4 <= 96;
 }
+// The same budget when Pinv is block-diagonal (its rows hold ss values).
+template <typename T>
+constexpr bool kResidentFitsPD(int ss) {
+  return 4 * ss * (int)sizeof(T) / 4 <= 96;
+}
 
 // Streamed with prefetch: specialised sizes whose 64-row chunk is at most 16
 // 16-byte vectors per lane.
@@ -428,18 +448,20 @@ int prefetch_stage_elems(int ss) {
 // res_available: specialised size (resident rows possible); prefetch: the
 // prefetching streamed placement is allowed (specialised, 16-byte aligned).
 template <typename T>
-bool make_plan(int ss, int kp, bool res_available, bool prefetch, size_t lds_max,
-               Plan* plan) {
+bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag,
+               size_t lds_max, Plan* plan) {
   const int n = kp * ss;
   const int W = 3 * ss;
   const int nchunks = (n + 63) / 64;
   // Register-resident rows when they fit comfortably in 128 VGPRs per lane.
-  const bool res_fits = res_available && kResidentFits<T>(ss) && nchunks <= 16;
+  const bool res_fits = res_available && nchunks <= 16 &&
+                        (pinv_diag ? kResidentFitsPD<T>(ss) : kResidentFits<T>(ss));
   if (res_fits) {
     Plan p;
     p.NW = nchunks;
     p.RPT = 1;
     p.res = true;
+    p.pd = pinv_diag;
     p.stage_elems = 0;
     p.lds = lds_bytes<T>(ss, kp, p.NW, 0);
     if (p.lds <= lds_max) {
@@ -524,8 +546,11 @@ int launch_rpt(const PcgArgs<T>& a, int n_problems, const Plan& pl,
 template <typename T, int SS>
 int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
               hipStream_t st) {
+  if constexpr (SS > 0 && kResidentFitsPD<T>(SS)) {
+    if (pl.res && pl.pd) return launch_one<T, SS, 1, kResidentPD>(a, n_problems, pl, st);
+  }
   if constexpr (SS > 0 && kResidentFits<T>(SS)) {
-    if (pl.res) return launch_one<T, SS, 1, kResident>(a, n_problems, pl, st);
+    if (pl.res && !pl.pd) return launch_one<T, SS, 1, kResident>(a, n_problems, pl, st);
   }
   if constexpr (SS > 0 && kPrefetchFits<T>(SS)) {
     if (pl.prefetch) return launch_rpt<T, SS, kStreamPrefetch>(a, n_problems, pl, st);
@@ -536,7 +561,7 @@ int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
 template <typename T>
 int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
                  int n_problems, int max_iters, double rel_tol, double abs_tol,
-                 int* iters, int* status, T* rho, hipStream_t st) {
+                 int* iters, int* status, T* rho, bool pinv_diag, hipStream_t st) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
@@ -546,12 +571,12 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
                         std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
   Plan pl;
-  if (!make_plan<T>(ss, kp, specialised, prefetch, dev.max_lds_per_block, &pl))
+  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, dev.max_lds_per_block, &pl))
     return fail(GLASS_EUNSUPPORTED,
                 "pcg: problem too large for one workgroup (rows or LDS)");
   if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl.res) {
     Plan alt;
-    if (make_plan<T>(ss, kp, false, prefetch, dev.max_lds_per_block, &alt)) pl = alt;
+    if (make_plan<T>(ss, kp, false, prefetch, false, dev.max_lds_per_block, &alt)) pl = alt;
   }
   PcgArgs<T> a;
   a.x = x;
@@ -578,18 +603,18 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
 }
 
 template <typename T>
-int placement_typed(int ss, int kp, bool vec) {
+int placement_typed(int ss, int kp, bool vec, bool pinv_diag) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
   const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
                         std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
   Plan pl;
-  if (!make_plan<T>(ss, kp, specialised, prefetch, dev.max_lds_per_block, &pl))
+  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, dev.max_lds_per_block, &pl))
     return fail(GLASS_EUNSUPPORTED, "pcg: problem too large for one workgroup (rows or LDS)");
   if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl.res) {
     Plan alt;
-    if (make_plan<T>(ss, kp, false, prefetch, dev.max_lds_per_block, &alt)) pl = alt;
+    if (make_plan<T>(ss, kp, false, prefetch, false, dev.max_lds_per_block, &alt)) pl = alt;
   }
   return pl.res ? GLASS_PLACEMENT_RESIDENT
                 : (pl.prefetch ? GLASS_PLACEMENT_STREAMED_PREFETCH : GLASS_PLACEMENT_STREAMED);
@@ -597,25 +622,25 @@ int placement_typed(int ss, int kp, bool vec) {
 
 }  // namespace
 
-int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16) {
-  return dt == GLASS_F32 ? placement_typed<float>(ss, kp, aligned16)
-                         : placement_typed<double>(ss, kp, aligned16);
+int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag) {
+  return dt == GLASS_F32 ? placement_typed<float>(ss, kp, aligned16, pinv_diag)
+                         : placement_typed<double>(ss, kp, aligned16, pinv_diag);
 }
 
 int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
                        const void* Pinv, const void* b, int ss, int kp,
                        int n_problems, int max_iters, double rel_tol,
                        double abs_tol, int* iters, int* status, void* rho,
-                       hipStream_t stream) {
+                       bool pinv_diag, hipStream_t stream) {
   if (dt == GLASS_F32)
     return launch_typed<float>((float*)x, (const float*)S, (const float*)Pinv,
                                (const float*)b, ss, kp, n_problems, max_iters,
                                rel_tol, abs_tol, iters, status, (float*)rho,
-                               stream);
+                               pinv_diag, stream);
   return launch_typed<double>((double*)x, (const double*)S,
                               (const double*)Pinv, (const double*)b, ss, kp,
                               n_problems, max_iters, rel_tol, abs_tol, iters,
-                              status, (double*)rho, stream);
+                              status, (double*)rho, pinv_diag, stream);
 }
 
 }  // namespace glass

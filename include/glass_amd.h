@@ -126,26 +126,39 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
                       int* iters_out, glass_dtype dtype, void* hip_stream);
 
 /* As glass_pcg_batched, plus optional per-problem outputs (either may be
- * NULL): status_out (GLASS_PCG_*) and rho_out (see conventions). */
+ * NULL): status_out (GLASS_PCG_*) and rho_out (see conventions), and flags:
+ *   GLASS_PCG_PINV_BLOCK_DIAGONAL  the caller asserts that the L and R blocks
+ *     of every block-row of Pinv are zero (a block-Jacobi preconditioner,
+ *     one of the choices the same page names).  Pinv keeps its [L|D|R]
+ *     layout; where each lane keeps its rows in registers only the D blocks
+ *     are read and held, which lets more workgroups share a CU and reads a
+ *     third of Pinv's bytes.  When the assertion holds the results are the
+ *     same as without the flag (the skipped terms are exact zeros, added in
+ *     the same order); when it does not, the L and R blocks of Pinv may or
+ *     may not be used.
+ * Other flag bits return GLASS_EINVAL. */
+enum { GLASS_PCG_PINV_BLOCK_DIAGONAL = 1u };
 int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
                          const void* b, int state_size, int knot_points,
                          int n_problems, int max_iters, double rel_tol,
                          double abs_tol, int* iters_out, int* status_out,
-                         void* rho_out, glass_dtype dtype, void* hip_stream);
+                         void* rho_out, glass_dtype dtype, unsigned flags,
+                         void* hip_stream);
 
-/* Where glass_pcg_batched keeps S and Pinv for a problem shape on the
- * current device: GLASS_PLACEMENT_RESIDENT (each lane's rows in registers,
- * read from HBM once per solve) or GLASS_PLACEMENT_STREAMED[_PREFETCH]
- * (re-read from memory for every matvec).  aligned16: whether S and Pinv
- * will be 16-byte aligned.  Returns a negative GLASS_E* code for shapes the
- * solve rejects.  Enqueues nothing. */
+/* Where glass_pcg_batched_ex keeps S and Pinv for a problem shape and flags
+ * on the current device: GLASS_PLACEMENT_RESIDENT (each lane's rows in
+ * registers, read from HBM once per solve) or
+ * GLASS_PLACEMENT_STREAMED[_PREFETCH] (re-read from memory for every
+ * matvec).  aligned16: whether S and Pinv will be 16-byte aligned.  flags:
+ * as glass_pcg_batched_ex (0 for glass_pcg_batched).  Returns a negative
+ * GLASS_E* code for shapes the solve rejects.  Enqueues nothing. */
 enum {
   GLASS_PLACEMENT_RESIDENT = 0,
   GLASS_PLACEMENT_STREAMED_PREFETCH = 1,
   GLASS_PLACEMENT_STREAMED = 2
 };
 int glass_pcg_batched_placement(int state_size, int knot_points,
-                                glass_dtype dtype, int aligned16);
+                                glass_dtype dtype, int aligned16, unsigned flags);
 
 /*
  * One PCG solve (same steps and outputs as glass_pcg_batched with

@@ -51,7 +51,7 @@ def assert_bdmv_close(y_gpu, S, v, ss, kp, nthreads=8):
         bad.sum(), float((err / np.maximum(scale[:, ss:-ss], 1e-300)).max()))
 
 
-def pcg_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, x0=None):
+def pcg_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, x0=None, pinv_block_diagonal=False):
     t = {k: to_dev(v) for k, v in inp.items() if k in ("S", "Pinv", "b")}
     B = inp["b"].shape[0]
     x = to_dev(inp["x0"] if x0 is None else x0).clone()
@@ -59,7 +59,7 @@ def pcg_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, x0=None):
     status = torch.full((B,), -1, dtype=torch.int32, device="cuda")
     rho = torch.zeros((B, 2), dtype=x.dtype, device="cuda")
     glass.pcg_batched(x, t["S"], t["Pinv"], t["b"], ss, kp, max_iters, rel_tol,
-                      abs_tol, iters, status, rho)
+                      abs_tol, iters, status, rho, pinv_block_diagonal=pinv_block_diagonal)
     torch.cuda.synchronize()
     return x.cpu().numpy(), iters.cpu().numpy(), status.cpu().numpy(), rho.cpu().numpy()
 

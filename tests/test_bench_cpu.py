@@ -26,6 +26,8 @@ def test_pcg_bytes_resident_and_streamed():
     assert bench.algorithmic_bytes_pcg(w, it, resident=True) == 2 * (288 + 76)
     # streamed: S and Pinv once per pass, iterations + 1 passes
     assert bench.algorithmic_bytes_pcg(w, it, resident=False) == (5 * 288 + 76) + (1 * 288 + 76)
+    # only Pinv's D blocks: S 6*6*4 = 144 B plus Pinv 6*2*4 = 48 B
+    assert bench.algorithmic_bytes_pcg(w, it, resident=True, pinv_diag=True) == 2 * (192 + 76)
 
 
 def test_bdmv_bytes():

@@ -233,3 +233,52 @@ def test_empty_batches_are_no_ops(gpu):
     gpu.pcg_batched(z, z, z, z, 6, 32, 10, 1e-6, 0.0, zi)
     gpu.bdsv_batched(z, z, z, 6, 32, zi)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("ss,kp,B,dtype,resident_only_with_flag", [
+    (14, 32, 96, np.float32, False),   # the resident ss=14 workload shape
+    (6, 32, 40, np.float32, False),
+    (12, 60, 9, np.float32, False),
+    (21, 40, 7, np.float32, True),     # 840 rows: resident only with the flag
+    (6, 20, 9, np.float64, False),
+    (21, 64, 5, np.float32, False),    # streamed either way: the flag is ignored
+])
+def test_pcg_pinv_block_diagonal_hint(gpu, ss, kp, B, dtype, resident_only_with_flag):
+    """GLASS_PCG_PINV_BLOCK_DIAGONAL on block-Jacobi preconditioners: the
+    same values as the general contraction (the skipped terms are exact
+    zeros added in the same order) and oracle parity; the placement query
+    reports where the rows go."""
+    rng = np.random.default_rng(ss * 100 + kp)
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.2, dtype)
+    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
+           "b": rng.standard_normal((B, kp * ss)).astype(dtype),
+           "x0": np.zeros((B, kp * ss), dtype)}
+    rel = 1e-6 if dtype == np.float32 else 1e-10
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    plain = gpu.pcg_batched_placement(ss, kp, tdt)
+    hinted = gpu.pcg_batched_placement(ss, kp, tdt, pinv_block_diagonal=True)
+    if resident_only_with_flag:
+        assert plain != gpu.PLACEMENT_RESIDENT and hinted == gpu.PLACEMENT_RESIDENT
+    elif plain == gpu.PLACEMENT_RESIDENT:
+        assert hinted == gpu.PLACEMENT_RESIDENT
+    say("pcg Pinv block-diagonal ss=%d kp=%d B=%d %s placement %d -> %d"
+        % (ss, kp, B, np.dtype(dtype).name, plain, hinted))
+    ref = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0)
+    got = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0, pinv_block_diagonal=True)
+    for u, v in zip(ref, got):
+        np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, got, dtype)
+
+
+def test_pcg_pinv_block_diagonal_full_workload(gpu):
+    """The full 4096-problem ss=14 workload with the hint, against the
+    general run and the oracle."""
+    w = workloads.WORKLOADS[2]
+    inp = workloads.generate(w)
+    say("pcg cfg2 full with the block-diagonal Pinv hint")
+    ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    got = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol,
+                  pinv_block_diagonal=True)
+    for u, v in zip(ref, got):
+        np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, got, np.float32)
