@@ -64,17 +64,20 @@ KERNEL_OF = {
     "pcg2_f64": "pcg_batched_kernel<double, 14,",
     "grid4_f32": "pcg_grid_kernel<float, 12,",
     "pcg2_pd": "pcg_batched_kernel<float, 14, 1, 3>",
+    "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 4>",
 }
 # Workload inputs: the five configurations; bdsv2 is the direct solve of the
 # same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
 # are the precision variants of pcg2 and grid4 (same recipe and seeds).
 CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2,
-             "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2}
+             "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3}
 # Workloads run with GLASS_PCG_PINV_BLOCK_DIAGONAL (their Pinv is block-Jacobi,
-# so the assertion holds): pcg2_pd is the ss=14 workload with the hint.
-PINV_DIAG = {"pcg2_pd"}
+# so the assertion holds): pcg2_pd and pcg3_pd are the ss=14 and ss=21
+# workloads with the hint.
+PINV_DIAG = {"pcg2_pd", "pcg3_pd"}
 VARIANT_OF = {
     "pcg2_pd": dict(name="pcg_ss14_kp32_b4096_f32_pinv_blockdiag"),
+    "pcg3_pd": dict(name="pcg_ss21_kp64_b2048_f32_pinv_blockdiag"),
     "pcg2_f64": dict(name="pcg_ss14_kp32_b4096_f64", dtype=np.float64),
     "grid4_f32": dict(name="grid_pcg_ss12_kp8192_f32", dtype=np.float32, rel_tol=1e-7),
 }
@@ -352,7 +355,7 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     # batched resident placement), else once per pass.
     resident = grid or glass.pcg_batched_placement(
         w.ss, w.kp, S.dtype, pinv_block_diagonal=pd) == glass.PLACEMENT_RESIDENT
-    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd and resident)
+    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd)
     for k in range(min(10, len(xs))):
         xs[k].zero_()
     iso = isolated_ms(torch, lambda k: run(xs[k]), reps=min(10, len(xs)))

@@ -39,7 +39,11 @@
 // are zero): each lane holds only the D part of its Pinv row and multiplies
 // it with its own block-row of r.  The skipped terms are exact zeros that the
 // general contraction adds after and before the D terms, so the result has
-// the same value; fewer registers let more workgroups share a CU.
+// the same value; fewer registers let more workgroups share a CU.  STREAMED
+// with PREFETCH and a block-diagonal Pinv: a Pinv chunk's 16-byte vectors
+// that touch no row's D block are given an offset past the buffer's end, so
+// they read zeros and are not fetched (about 2/5 of the vectors remain at
+// ss=21).
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -77,14 +81,21 @@ struct PcgArgs {
 };
 
 // Placements of the matrices (see the header).
-enum Mode { kResident = 0, kStreamPrefetch = 1, kStream = 2, kResidentPD = 3 };
+enum Mode {
+  kResident = 0,
+  kStreamPrefetch = 1,
+  kStream = 2,
+  kResidentPD = 3,        // resident, Pinv's D blocks only
+  kStreamPrefetchPD = 4,  // streamed with prefetch, Pinv vectors touching D only
+};
 
 // Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for the
 // prefetching placement (two chunk buffers per lane) and for 3-4 rows per
 // lane; 16 waves otherwise (rows beyond 4096 need them, at the cost of
 // spills).
 constexpr int max_threads_for(int rpt, int mode) {
-  return (mode == kStreamPrefetch || rpt == 3 || rpt == 4) ? 512 : 1024;
+  return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || rpt == 3 || rpt == 4) ? 512
+                                                                                       : 1024;
 }
 
 template <typename T, int SS, int RPT, int MODE>
@@ -92,7 +103,7 @@ __global__ void __launch_bounds__(max_threads_for(RPT, MODE))
 pcg_batched_kernel(PcgArgs<T> a) {
   constexpr bool RES = MODE == kResident || MODE == kResidentPD;
   constexpr bool PD = MODE == kResidentPD;  // Pinv rows: D part only
-  constexpr bool PFM = MODE == kStreamPrefetch;
+  constexpr bool PFM = MODE == kStreamPrefetch || MODE == kStreamPrefetchPD;
   constexpr int WC = SS > 0 ? 3 * SS : 1;  // compile-time width
   const int ss = SS > 0 ? SS : a.ss;
   const int W = 3 * ss;
@@ -143,13 +154,24 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // offset register serves every load.  A chunk this wave does not have
   // (r0 >= n) becomes an empty resource: the loads return zeros.
   constexpr int NV = (WC * (int)sizeof(T) + 15) / 16;  // vectors per lane
-  auto load_chunk = [&](vec16_t (&buf)[NV], const T* __restrict__ gM, int k) {
+  auto load_chunk = [&](vec16_t (&buf)[NV], const T* __restrict__ gM, int k, bool dpart) {
     const int r0 = chunk_r0(k);
     const bool has = r0 < n;
     const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gM + (long long)r0 * W : gM, nbytes);
+    constexpr int RB = WC * (int)sizeof(T);                  // row bytes
+    constexpr int D0 = (SS > 0 ? SS : 1) * (int)sizeof(T);  // D block bytes [D0, 2*D0)
 #pragma unroll
-    for (int u = 0; u < NV; ++u) buf[u] = buffer_load16(rs, (lane + u * kWave) * 16);
+    for (int u = 0; u < NV; ++u) {
+      int off = (lane + u * kWave) * 16;
+      if (dpart) {
+        // Does [off, off+16) touch the D block of its row or of the next?
+        const int q = off / RB, in = off - q * RB;
+        const bool touch = (in < 2 * D0 && in + 16 > D0) || (in + 16 - RB > D0);
+        off = touch ? off : 0x7ffffff0;  // past the end: zeros, no fetch
+      }
+      buf[u] = buffer_load16(rs, off);
+    }
   };
   // Write a loaded chunk into the wave's LDS stage (same layout as in HBM; the
   // stage holds NV*64 vectors, so every store is in bounds).
@@ -198,11 +220,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
     if constexpr (PFM) {
       const int m = pos / RPT, k = pos % RPT;
       const T* gM = m == 0 ? gS : gP;
+      const bool dpart = MODE == kStreamPrefetchPD && m == 1;
       if constexpr (kRingDepth == 1) {
-        load_chunk(pf0, gM, k);
+        load_chunk(pf0, gM, k, dpart);
       } else {
-        if (pos % 2 == 0) load_chunk(pf0, gM, k);
-        else load_chunk(pf1, gM, k);
+        if (pos % 2 == 0) load_chunk(pf0, gM, k, dpart);
+        else load_chunk(pf1, gM, k, dpart);
       }
     }
   };
@@ -403,7 +426,7 @@ struct Plan {
   int NW = 0;
   int RPT = 0;
   bool res = false;
-  bool pd = false;  // resident with Pinv's D blocks only
+  bool pd = false;  // Pinv's D blocks only (resident, or streamed with prefetch)
   bool prefetch = false;
   int stage_elems = 0;
   size_t lds = 0;
@@ -493,6 +516,7 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
         best.NW = NW;
         best.RPT = rpt;
         best.res = false;
+        best.pd = pinv_diag && pf != 0;  // only the prefetching placement uses it
         best.prefetch = pf != 0;
         best.stage_elems = stage;
         best.lds = lds;
@@ -553,7 +577,9 @@ int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
     if (pl.res && !pl.pd) return launch_one<T, SS, 1, kResident>(a, n_problems, pl, st);
   }
   if constexpr (SS > 0 && kPrefetchFits<T>(SS)) {
-    if (pl.prefetch) return launch_rpt<T, SS, kStreamPrefetch>(a, n_problems, pl, st);
+    if (pl.prefetch)
+      return pl.pd ? launch_rpt<T, SS, kStreamPrefetchPD>(a, n_problems, pl, st)
+                   : launch_rpt<T, SS, kStreamPrefetch>(a, n_problems, pl, st);
   }
   return launch_rpt<T, SS, kStream>(a, n_problems, pl, st);
 }

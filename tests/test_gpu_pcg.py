@@ -282,3 +282,29 @@ def test_pcg_pinv_block_diagonal_full_workload(gpu):
     for u, v in zip(ref, got):
         np.testing.assert_array_equal(u, v)
     assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, got, np.float32)
+
+
+def test_pcg_pinv_block_diagonal_streamed_prefetch(gpu, monkeypatch):
+    """The streamed placement with prefetch fetches only the Pinv vectors
+    that touch a D block under the hint: the same values as the general run
+    for the full ss=21 workload, and at 1, 2 and 4 rows per lane for ss=14."""
+    w = workloads.WORKLOADS[3]
+    inp = workloads.generate(w)
+    say("pcg cfg3 full with the block-diagonal Pinv hint")
+    ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    got = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol,
+                  pinv_block_diagonal=True)
+    for u, v in zip(ref, got):
+        np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, got, np.float32)
+    w2 = workloads.WORKLOADS[2]
+    inp2 = workloads.generate(w2, n_problems=20)
+    monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
+    for rpt in ("1", "2", "4"):
+        monkeypatch.setenv("GLASS_AMD_PCG_RPT", rpt)
+        say("pcg cfg2 streamed prefetch rows/lane=%s with the hint" % rpt)
+        ref = pcg_gpu(gpu, inp2, w2.ss, w2.kp, w2.max_iters, w2.rel_tol, w2.abs_tol)
+        got = pcg_gpu(gpu, inp2, w2.ss, w2.kp, w2.max_iters, w2.rel_tol, w2.abs_tol,
+                      pinv_block_diagonal=True)
+        for u, v in zip(ref, got):
+            np.testing.assert_array_equal(u, v)
