@@ -55,13 +55,13 @@ METRIC = "PCG solves/sec (batched) and bdmv HBM GB/s as fraction of MI355X peak"
 # The kernel each workload spends its time in (a substring of the demangled
 # name rocprofv3 reports).
 KERNEL_OF = {
-    "pcg0": "pcg_batched_kernel<float, 6,",
+    "pcg0": "pcg_batched_kernel<float, 6, 1, 0>",
     "bdmv1": "bdmv_kernel<float, 14>",
-    "pcg2": "pcg_batched_kernel<float, 14,",
-    "pcg3": "pcg_batched_kernel<float, 21,",
+    "pcg2": "pcg_batched_kernel<float, 14, 1, 0>",
+    "pcg3": "pcg_batched_kernel<float, 21, 3, 1>",
     "grid4": "pcg_grid_kernel<double, 12,",
     "bdsv2": "bdsv_rows_kernel<float, 14,",
-    "pcg2_f64": "pcg_batched_kernel<double, 14,",
+    "pcg2_f64": "pcg_batched_kernel<double, 14, 1, 2>",
     "grid4_f32": "pcg_grid_kernel<float, 12,",
     "pcg2_pd": "pcg_batched_kernel<float, 14, 1, 3>",
     "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 4>",
