@@ -130,9 +130,11 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
  *   GLASS_PCG_PINV_BLOCK_DIAGONAL  the caller asserts that the L and R blocks
  *     of every block-row of Pinv are zero (a block-Jacobi preconditioner,
  *     one of the choices the same page names).  Pinv keeps its [L|D|R]
- *     layout; where each lane keeps its rows in registers only the D blocks
- *     are read and held, which lets more workgroups share a CU and reads a
- *     third of Pinv's bytes.  When the assertion holds the results are the
+ *     layout.  Where each lane keeps its rows in registers only the D blocks
+ *     are requested and held (fewer registers, a third of Pinv's
+ *     multiply-adds); where rows are streamed, 16-byte pieces that touch no
+ *     D block are not requested.  Memory traffic shrinks only where whole
+ *     cache lines lie outside the D blocks.  When the assertion holds the results are the
  *     same as without the flag (the skipped terms are exact zeros, added in
  *     the same order); when it does not, the L and R blocks of Pinv may or
  *     may not be used.
