@@ -94,8 +94,11 @@ enum Mode {
 // lane; 16 waves otherwise (rows beyond 4096 need them, at the cost of
 // spills).
 constexpr int max_threads_for(int rpt, int mode) {
-  return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || rpt == 3 || rpt == 4) ? 512
-                                                                                       : 1024;
+  const bool resident = mode == kResident || mode == kResidentPD;
+  return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || rpt == 3 || rpt == 4 ||
+          (resident && rpt > 1))
+             ? 512
+             : 1024;
 }
 
 template <typename T, int SS, int RPT, int MODE>
@@ -186,22 +189,24 @@ pcg_batched_kernel(PcgArgs<T> a) {
   constexpr int WCP = PD ? (SS > 0 ? SS : 1) : WC;  // Pinv row width held
   T mS[RES ? RPT : 1][WC], mP[RES ? RPT : 1][WCP];
   if constexpr (RES) {
-    static_assert(!RES || RPT == 1, "resident placement deals one row per lane");
 #pragma unroll
-    for (int c = 0; c < WC; ++c) mS[0][c] = T(0);
+    for (int k = 0; k < RPT; ++k) {
 #pragma unroll
-    for (int c = 0; c < WCP; ++c) mP[0][c] = T(0);
-    if (valid[0]) {
-      const long long off = (long long)row[0] * WC;
-      // The D part starts ss elements into the row: at (3*row + 1) times its
-      // own byte size, so the widths load_row_regs picks stay aligned.
-      const long long offP = off + (PD ? SS : 0);
-      if (vec) {
-        load_row_regs<T, WC, true>(mS[0], gS + off);
-        load_row_regs<T, WCP, true>(mP[0], gP + offP);
-      } else {
-        load_row_regs<T, WC, false>(mS[0], gS + off);
-        load_row_regs<T, WCP, false>(mP[0], gP + offP);
+      for (int c = 0; c < WC; ++c) mS[k][c] = T(0);
+#pragma unroll
+      for (int c = 0; c < WCP; ++c) mP[k][c] = T(0);
+      if (valid[k]) {
+        const long long off = (long long)row[k] * WC;
+        // The D part starts ss elements into the row: at (3*row + 1) times
+        // its own byte size, so the widths load_row_regs picks stay aligned.
+        const long long offP = off + (PD ? SS : 0);
+        if (vec) {
+          load_row_regs<T, WC, true>(mS[k], gS + off);
+          load_row_regs<T, WCP, true>(mP[k], gP + offP);
+        } else {
+          load_row_regs<T, WC, false>(mS[k], gS + off);
+          load_row_regs<T, WCP, false>(mP[k], gP + offP);
+        }
       }
     }
   }
@@ -427,6 +432,7 @@ struct Plan {
   int RPT = 0;
   bool res = false;
   bool pd = false;  // Pinv's D blocks only (resident, or streamed with prefetch)
+  bool res_auto = false;  // resident rows per lane left to the occupancy choice
   bool prefetch = false;
   int stage_elems = 0;
   size_t lds = 0;
@@ -452,6 +458,12 @@ template <typename T>
 constexpr bool kResidentFitsPD(int ss) {
   return 4 * ss * (int)sizeof(T) / 4 <= 96;
 }
+// Several resident rows per lane (workgroups of at most 8 waves, so up to
+// 256 VGPRs per lane): rpt rows of S and Pinv within 176 registers.
+template <typename T>
+constexpr bool kResidentRowsFit(int ss, int rpt, bool pd) {
+  return rpt * (pd ? 4 : 6) * ss * (int)sizeof(T) / 4 <= (rpt == 1 ? 96 : 176);
+}
 
 // Streamed with prefetch: specialised sizes whose 64-row chunk is at most 16
 // 16-byte vectors per lane.
@@ -476,14 +488,21 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
   const int n = kp * ss;
   const int W = 3 * ss;
   const int nchunks = (n + 63) / 64;
-  // Register-resident rows when they fit comfortably in 128 VGPRs per lane.
-  const bool res_fits = res_available && nchunks <= 16 &&
-                        (pinv_diag ? kResidentFitsPD<T>(ss) : kResidentFits<T>(ss));
+  // Register-resident rows when they fit comfortably in the VGPR budget:
+  // one row per lane (up to 16 waves), or GLASS_AMD_PCG_RES_RPT rows per lane
+  // (up to 8 waves; 2..4).
+  const int forced_res_rpt = env_int("GLASS_AMD_PCG_RES_RPT", 0);
+  const int res_rpt = forced_res_rpt > 0 ? forced_res_rpt : 1;
+  const int res_nw = (nchunks + res_rpt - 1) / res_rpt;
+  const bool res_fits = res_available && res_rpt >= 1 && res_rpt <= 4 &&
+                        res_nw * 64 <= max_threads_for(res_rpt, kResident) &&
+                        kResidentRowsFit<T>(ss, res_rpt, pinv_diag);
   if (res_fits) {
     Plan p;
-    p.NW = nchunks;
-    p.RPT = 1;
+    p.NW = res_nw;
+    p.RPT = res_rpt;
     p.res = true;
+    p.res_auto = forced_res_rpt == 0;
     p.pd = pinv_diag;
     p.stage_elems = 0;
     p.lds = lds_bytes<T>(ss, kp, p.NW, 0);
@@ -567,14 +586,59 @@ int launch_rpt(const PcgArgs<T>& a, int n_problems, const Plan& pl,
   }
 }
 
+// Resident placement: one instantiation per rows-per-lane count that fits.
+// Left to itself (no GLASS_AMD_PCG_RES_RPT), a batch with more problems than
+// CUs takes two rows per lane instead of one when that kernel fits more
+// workgroups per CU (more problems in flight); a smaller batch keeps one row
+// per lane (the most waves per problem, the shortest solve).
+template <typename T, int SS, bool PD>
+int launch_res(const PcgArgs<T>& a, int n_problems, const Plan& pl_in, hipStream_t st) {
+  constexpr int M = PD ? kResidentPD : kResident;
+  Plan pl = pl_in;
+  if constexpr (kResidentRowsFit<T>(SS, 1, PD) && kResidentRowsFit<T>(SS, 2, PD)) {
+    DeviceInfo dev;
+    const int nchunks = (a.kp * SS + 63) / 64;
+    const int nw2 = (nchunks + 1) / 2;
+    if (pl.res_auto && pl.RPT == 1 && nw2 * 64 <= max_threads_for(2, M) &&
+        current_device_info(&dev) == GLASS_OK && n_problems > dev.cu_count) {
+      int per1 = 0, per2 = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per1, pcg_batched_kernel<T, SS, 1, M>,
+                                                       pl.NW * 64, pl.lds) == hipSuccess &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per2, pcg_batched_kernel<T, SS, 2, M>,
+                                                       nw2 * 64, pl.lds) == hipSuccess &&
+          per2 > per1) {
+        pl.RPT = 2;
+        pl.NW = nw2;
+      }
+    }
+  }
+  switch (pl.RPT) {
+    case 1:
+      if constexpr (kResidentRowsFit<T>(SS, 1, PD)) return launch_one<T, SS, 1, M>(a, n_problems, pl, st);
+      break;
+    case 2:
+      if constexpr (kResidentRowsFit<T>(SS, 2, PD)) return launch_one<T, SS, 2, M>(a, n_problems, pl, st);
+      break;
+    case 3:
+      if constexpr (kResidentRowsFit<T>(SS, 3, PD)) return launch_one<T, SS, 3, M>(a, n_problems, pl, st);
+      break;
+    case 4:
+      if constexpr (kResidentRowsFit<T>(SS, 4, PD)) return launch_one<T, SS, 4, M>(a, n_problems, pl, st);
+      break;
+    default:
+      break;
+  }
+  return fail(GLASS_EUNSUPPORTED, "pcg: internal plan error (resident rows per lane)");
+}
+
 template <typename T, int SS>
 int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
               hipStream_t st) {
-  if constexpr (SS > 0 && kResidentFitsPD<T>(SS)) {
-    if (pl.res && pl.pd) return launch_one<T, SS, 1, kResidentPD>(a, n_problems, pl, st);
-  }
-  if constexpr (SS > 0 && kResidentFits<T>(SS)) {
-    if (pl.res && !pl.pd) return launch_one<T, SS, 1, kResident>(a, n_problems, pl, st);
+  if constexpr (SS > 0) {
+    if (pl.res) {
+      return pl.pd ? launch_res<T, SS, true>(a, n_problems, pl, st)
+                   : launch_res<T, SS, false>(a, n_problems, pl, st);
+    }
   }
   if constexpr (SS > 0 && kPrefetchFits<T>(SS)) {
     if (pl.prefetch)

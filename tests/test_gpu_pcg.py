@@ -308,3 +308,33 @@ def test_pcg_pinv_block_diagonal_streamed_prefetch(gpu, monkeypatch):
                       pinv_block_diagonal=True)
         for u, v in zip(ref, got):
             np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("rpt", ["2", "3", "4"])
+def test_pcg_resident_rows_per_lane_bit_identical(gpu, monkeypatch, rpt):
+    """Resident rows at 2, 3 and 4 rows per lane (GLASS_AMD_PCG_RES_RPT; for
+    the ss=6 kp=32 workload 3 rows per lane is one wave per problem) give the
+    same bits as one row per lane, with and without the block-diagonal Pinv
+    hint, and meet the oracle."""
+    w = workloads.WORKLOADS[0]
+    inp = workloads.generate(w)
+    ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    monkeypatch.setenv("GLASS_AMD_PCG_RES_RPT", rpt)
+    assert gpu.pcg_batched_placement(w.ss, w.kp, torch.float32) == gpu.PLACEMENT_RESIDENT
+    for pd in (False, True):
+        say("pcg cfg0 resident rows/lane=%s pinv_diag=%s" % (rpt, pd))
+        got = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol,
+                      pinv_block_diagonal=pd)
+        for u, v in zip(ref, got):
+            np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, got, np.float32)
+    if rpt == "2":
+        w2 = workloads.WORKLOADS[2]
+        inp2 = workloads.generate(w2, n_problems=64)
+        monkeypatch.delenv("GLASS_AMD_PCG_RES_RPT")
+        ref2 = pcg_gpu(gpu, inp2, w2.ss, w2.kp, w2.max_iters, w2.rel_tol, w2.abs_tol)
+        monkeypatch.setenv("GLASS_AMD_PCG_RES_RPT", "2")
+        say("pcg cfg2 resident rows/lane=2")
+        got2 = pcg_gpu(gpu, inp2, w2.ss, w2.kp, w2.max_iters, w2.rel_tol, w2.abs_tol)
+        for u, v in zip(ref2, got2):
+            np.testing.assert_array_equal(u, v)
