@@ -65,17 +65,24 @@ KERNEL_OF = {
     "grid4_f32": "pcg_grid_kernel<float, 12,",
     "pcg2_pd": "pcg_batched_kernel<float, 14, 1, 3>",
     "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 4>",
+    "grid4_sr": "pcg_grid_cg1_kernel<double, 12,",
+    "grid4_f32_sr": "pcg_grid_cg1_kernel<float, 12,",
 }
 # Workload inputs: the five configurations; bdsv2 is the direct solve of the
 # same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
 # are the precision variants of pcg2 and grid4 (same recipe and seeds).
 CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2,
-             "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3}
+             "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3, "grid4_sr": 4, "grid4_f32_sr": 4}
 # Workloads run with GLASS_PCG_PINV_BLOCK_DIAGONAL (their Pinv is block-Jacobi,
 # so the assertion holds): pcg2_pd and pcg3_pd are the ss=14 and ss=21
 # workloads with the hint.
 PINV_DIAG = {"pcg2_pd", "pcg3_pd"}
+# Grid workloads run in the single-reduction form (GLASS_GRID_SINGLE_REDUCTION).
+SINGLE_RED = {"grid4_sr", "grid4_f32_sr"}
 VARIANT_OF = {
+    "grid4_sr": dict(name="grid_pcg_ss12_kp8192_f64_single_reduction"),
+    "grid4_f32_sr": dict(name="grid_pcg_ss12_kp8192_f32_single_reduction", dtype=np.float32,
+                         rel_tol=1e-7),
     "pcg2_pd": dict(name="pcg_ss14_kp32_b4096_f32_pinv_blockdiag"),
     "pcg3_pd": dict(name="pcg_ss21_kp64_b2048_f32_pinv_blockdiag"),
     "pcg2_f64": dict(name="pcg_ss14_kp32_b4096_f64", dtype=np.float64),
@@ -328,11 +335,12 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     # The grid solve is timed with the exclusive launch (this process is the
     # only user of the device); the cooperative launch is timed after it.
     pd = key in PINV_DIAG
+    single = key in SINGLE_RED
 
     def run(x, exclusive=True):
         if grid:
             glass.pcg_grid(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters, ws,
-                           exclusive=exclusive)
+                           exclusive=exclusive, single_reduction=single)
         else:
             glass.pcg_batched(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters,
                               pinv_block_diagonal=pd)

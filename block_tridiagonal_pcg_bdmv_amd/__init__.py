@@ -21,7 +21,7 @@ __all__ = [
     "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "bdsv_workspace_bytes",
     "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
-    "PCG_PINV_BLOCK_DIAGONAL",
+    "PCG_PINV_BLOCK_DIAGONAL", "GRID_SINGLE_REDUCTION",
     "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED",
 ]
@@ -37,6 +37,7 @@ GLASS_F32, GLASS_F64 = 0, 1
 CONVERGED, MAX_ITERS, BREAKDOWN, GRID_TIMEOUT = 0, 1, 2, 3
 BDSV_OK, BDSV_NOT_SPD = 0, 1
 GRID_EXCLUSIVE = 1  # glass_pcg_grid_ex flag: ordinary dispatch on the stream's queue
+GRID_SINGLE_REDUCTION = 2  # glass_pcg_grid_ex flag: one grid reduction per iteration
 PCG_PINV_BLOCK_DIAGONAL = 1  # glass_pcg_batched_ex flag: Pinv's L and R blocks are zero
 
 
@@ -222,13 +223,16 @@ def pcg_grid_workspace_bytes(state_size: int, knot_points: int, dtype) -> int:
 
 def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
              rel_tol: float, abs_tol: float, iters_out, workspace,
-             status_out=None, rho_out=None, stream=None, exclusive=False):
+             status_out=None, rho_out=None, stream=None, exclusive=False,
+             single_reduction=False):
     """One PCG solve over a cooperative grid.  Same arguments as
     ``pcg_batched`` with one problem, plus a device ``workspace`` tensor of at
     least ``pcg_grid_workspace_bytes`` bytes (any dtype, 256-byte aligned).
     ``exclusive=True`` passes GLASS_GRID_EXCLUSIVE: an ordinary dispatch on
     the stream's queue, for callers that know no other kernel occupies the
-    device during the solve."""
+    device during the solve.  ``single_reduction=True`` passes
+    GLASS_GRID_SINGLE_REDUCTION: the single-reduction form of PCG (one grid
+    reduction per iteration; same iterates in exact arithmetic)."""
     import torch
     ss, kp = int(state_size), int(knot_points)
     if _problems(S, ss, kp) != 1:
@@ -246,6 +250,8 @@ def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
     rc = load().glass_pcg_grid_ex(*a, ss, kp, int(max_iters), float(rel_tol),
                                   float(abs_tol), it, st, rh,
                                   ctypes.c_void_p(workspace.data_ptr()), wbytes,
-                                  _dtype_code(S), GRID_EXCLUSIVE if exclusive else 0,
+                                  _dtype_code(S),
+                                  (GRID_EXCLUSIVE if exclusive else 0)
+                                  | (GRID_SINGLE_REDUCTION if single_reduction else 0),
                                   _stream(stream))
     _check(rc, "glass_pcg_grid_ex")

@@ -209,7 +209,8 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
                       size_t workspace_bytes, glass_dtype dtype,
                       unsigned flags, void* hip_stream) {
   if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
-  if (flags & ~(unsigned)GLASS_GRID_EXCLUSIVE) return fail(GLASS_EINVAL, "unknown grid flags");
+  if (flags & ~(unsigned)(GLASS_GRID_EXCLUSIVE | GLASS_GRID_SINGLE_REDUCTION))
+    return fail(GLASS_EINVAL, "unknown grid flags");
   if (knot_points < 4) return fail(GLASS_EINVAL, "grid pcg needs knot_points >= 4");
   if (int rc = check_ptr(x, dtype, "x")) return rc;
   if (int rc = check_ptr(S, dtype, "S")) return rc;
@@ -228,6 +229,7 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
                                 max_iters, rel_tol, abs_tol, iters_out,
                                 status_out, rho_out, workspace, workspace_bytes,
                                 (flags & GLASS_GRID_EXCLUSIVE) != 0,
+                                (flags & GLASS_GRID_SINGLE_REDUCTION) != 0,
                                 (hipStream_t)hip_stream);
 }
 

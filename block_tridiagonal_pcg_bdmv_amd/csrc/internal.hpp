@@ -51,7 +51,7 @@ int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     const void* b, int ss, int kp, int max_iters,
                     double rel_tol, double abs_tol, int* iters, int* status,
                     void* rho, void* workspace, size_t workspace_bytes,
-                    bool exclusive, hipStream_t stream);
+                    bool exclusive, bool single, hipStream_t stream);
 
 inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;

@@ -31,12 +31,13 @@
 //   stopping decisions.  One store and about one load round trip per dot,
 //   against the five dependent round trips of a counter-based two-level
 //   barrier (measured 2.2 us against 4.4 us per barrier at 256 workgroups).
-// * Reuse rules.  Partials alternate between two buffers by barrier parity:
-//   a workgroup writes the buffer of barrier n+2 only after it has seen every
-//   partial of barrier n+1, and each of those was stored after its writer had
-//   finished reading barrier n.  Edge values use one buffer: a workgroup
-//   overwrites its edges (at the next r^T z barrier) only after seeing its
-//   neighbours' p^T S p partials, which they store after reading the edges.
+// * Reuse rules.  Partials and edge values alternate between two buffers by
+//   barrier parity: a workgroup writes the buffers of barrier n+2 only after
+//   it has seen every partial of barrier n+1, and each of those was stored
+//   after its writer had finished reading barrier n (its edge loads
+//   included).  One buffer would do for edges published every other barrier
+//   (the standard steps), not for the single-reduction form, which publishes
+//   them at every barrier.
 //   A reset kernel zeroes every tag word before the solve, so tags start at 1
 //   and stale words from an earlier solve never match.
 // * Matrices: for the specialised state sizes each thread keeps its S row
@@ -70,8 +71,9 @@ struct GridArgs {
   T rel_tol;
   T abs_tol;
   unsigned int* flags;       // [0]: a poll timed out (zeroed before the launch)
-  unsigned long long* part;  // [2][G][kTagWords<T>] tagged partials, by barrier parity
-  unsigned long long* edges; // [G][4*ss][kTagWords<T>] tagged z of block-rows A, A+1, B-2, B-1
+  unsigned long long* part;  // [2][G][kDotValues][kTagWords<T>] tagged partials, by barrier parity
+  unsigned long long* edges; // [2][G][4*ss][kTagWords<T>] tagged edge values (block-rows
+                             // A, A+1, B-2, B-1), by barrier parity
   int G;
   int nb_max;
   int wide;               // matrix bases 16-byte aligned: vector row loads
@@ -82,6 +84,10 @@ typedef unsigned long long u64;
 // 64-bit exchange words per value: one for float, two for double.
 template <typename T>
 constexpr int kTagWords = (int)sizeof(T) / 4;
+
+// Values one grid dot can reduce at once (the single-reduction variant
+// reduces two).
+constexpr int kDotValues = 2;
 
 struct WorkspaceLayout {
   size_t flags, part, edges, total;
@@ -95,8 +101,8 @@ WorkspaceLayout layout(int ss, int kp, size_t elem) {
   WorkspaceLayout w;
   w.flags = 0;
   w.part = 256;
-  w.edges = w.part + round256(2 * gmax * words * sizeof(u64));
-  w.total = w.edges + round256(gmax * 4 * (size_t)ss * words * sizeof(u64));
+  w.edges = w.part + round256(2 * gmax * kDotValues * words * sizeof(u64));
+  w.total = w.edges + round256(2 * gmax * 4 * (size_t)ss * words * sizeof(u64));
   return w;
 }
 
@@ -159,38 +165,59 @@ __device__ __forceinline__ bool keep_polling(unsigned& spins, unsigned int* flag
 // Partials one lane loads per poll round.
 constexpr int kSumBatch = 4;
 
-// Where a workgroup's exchange buffers are.
+// Where a workgroup's exchange buffers are (edge pointers for parity 0; the
+// parity-1 buffers follow at edge_parity words).
 struct GridXchg {
-  u64* part;         // [2][G][kTagWords]
+  u64* part;         // [2][G][kDotValues][kTagWords]
   u64* my_edges;     // this workgroup's [4*ss][kTagWords]
   const u64* left;   // left neighbour's edges, or null (first partition)
   const u64* right;  // right neighbour's edges, or null (last partition)
+  size_t edge_parity;
   unsigned int* flags;
   int G, g;
 };
 
-// Grid-wide sum of the per-thread values v; every thread of every workgroup
-// must call it and gets the same bits.  `bar` is the barrier number
-// (1-based, the same sequence in every workgroup).  With edge_lds, wave 0
-// also publishes this workgroup's n_edge = 4*ss edge z values staged there
-// and fills ghost_lds with the neighbours' ones: [0, 2ss) z of block-rows
-// A-2, A-1 and [2ss, 4ss) z of B, B+1 (zero off the chain).  GP bounds the
-// ghost values per lane (GP*64 >= n_edge).  Contains two __syncthreads().
-template <typename T, int GP>
-__device__ __forceinline__ T grid_dot(T v, const T* edge_lds, T* ghost_lds, int n_edge,
-                                      const GridXchg& xc, unsigned bar, T* wsl, T* bcast,
-                                      int NW, int wave, int lane) {
+// Grid-wide sums of NV per-thread values v[0..NV); every thread of every
+// workgroup must call it and gets the same bits in out[0..NV).  `bar` is the
+// barrier number (1-based, the same sequence in every workgroup).  With
+// edge_lds, wave 0 also publishes this workgroup's n_edge = 4*ss edge values
+// staged there and fills ghost_lds with the neighbours' ones: [0, 2ss) of
+// block-rows A-2, A-1 and [2ss, 4ss) of B, B+1 (zero off the chain).  GP
+// bounds the ghost values per lane (GP*64 >= n_edge).  Contains two
+// __syncthreads().
+template <typename T, int GP, int NV>
+__device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const T* edge_lds,
+                                           T* ghost_lds, int n_edge, const GridXchg& xc,
+                                           unsigned bar, T* wsl, T* bcast, int NW, int wave,
+                                           int lane) {
+  static_assert(NV >= 1 && NV <= kDotValues, "values per grid dot");
   constexpr int WD = kTagWords<T>;
-  v = wave_sum(v);
-  if (lane == 0) wsl[wave] = v;
+  T vs[NV];
+#pragma unroll
+  for (int q = 0; q < NV; ++q) vs[q] = wave_sum(v[q]);
+  if (lane == 0) {
+#pragma unroll
+    for (int q = 0; q < NV; ++q) wsl[q * NW + wave] = vs[q];
+  }
   __syncthreads();
   if (wave == 0) {
-    T part = wsl[0];
-    for (int w = 1; w < NW; ++w) part = part + wsl[w];
-    u64* slots = xc.part + (size_t)(bar & 1u) * xc.G * WD;
+    T part[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) {
+      part[q] = wsl[q * NW];
+      for (int w = 1; w < NW; ++w) part[q] = part[q] + wsl[q * NW + w];
+    }
+    u64* slots = xc.part + (size_t)(bar & 1u) * xc.G * NV * WD;
+    const size_t epar = (bar & 1u) ? xc.edge_parity : 0;
+    const u64* left = xc.left ? xc.left + epar : nullptr;
+    const u64* right = xc.right ? xc.right + epar : nullptr;
     if (edge_lds)
-      for (int j = lane; j < n_edge; j += kWave) put_tagged(xc.my_edges + j * WD, edge_lds[j], bar);
-    if (lane == 0) put_tagged(slots + xc.g * WD, part, bar);
+      for (int j = lane; j < n_edge; j += kWave)
+        put_tagged(xc.my_edges + epar + j * WD, edge_lds[j], bar);
+    if (lane == 0) {
+#pragma unroll
+      for (int q = 0; q < NV; ++q) put_tagged(slots + (xc.g * NV + q) * WD, part[q], bar);
+    }
 
     // Neighbour edges: loaded now, checked after the partials, so both
     // share one round trip when the neighbours are on time.
@@ -203,7 +230,7 @@ __device__ __forceinline__ T grid_dot(T v, const T* edge_lds, T* ghost_lds, int 
         const int q = lane + k * kWave;
         gv[k] = T(0);
         if (q < n_edge) {
-          const u64* src = q < half ? xc.left : xc.right;
+          const u64* src = q < half ? left : right;
           if (src) gok &= get_tagged(src + (q < half ? q + half : q - half) * WD, bar, gv[k]);
         }
       }
@@ -211,26 +238,35 @@ __device__ __forceinline__ T grid_dot(T v, const T* edge_lds, T* ghost_lds, int 
 
     // All G partials, polled in batches until every tag is current, added in
     // a fixed order: lane-strided within the batch sequence, then the tree.
-    T s = T(0);
+    T sum[NV];
+#pragma unroll
+    for (int q = 0; q < NV; ++q) sum[q] = T(0);
     for (int base = 0; base < xc.G; base += kSumBatch * kWave) {
-      T val[kSumBatch];
+      T val[kSumBatch][NV];
       unsigned spins = 0;
       for (;;) {
         bool ok = true;
 #pragma unroll
         for (int k = 0; k < kSumBatch; ++k) {
           const int j = base + lane + k * kWave;
-          val[k] = T(0);
-          if (j < xc.G) ok &= get_tagged(slots + j * WD, bar, val[k]);
+#pragma unroll
+          for (int q = 0; q < NV; ++q) {
+            val[k][q] = T(0);
+            if (j < xc.G) ok &= get_tagged(slots + (j * NV + q) * WD, bar, val[k][q]);
+          }
         }
         if (__all(ok)) break;
         if (!keep_polling(spins, xc.flags, lane)) break;
       }
 #pragma unroll
       for (int k = 0; k < kSumBatch; ++k)
-        if (base + lane + k * kWave < xc.G) s = s + val[k];
+        if (base + lane + k * kWave < xc.G) {
+#pragma unroll
+          for (int q = 0; q < NV; ++q) sum[q] = sum[q] + val[k][q];
+        }
     }
-    s = wave_sum(s);
+#pragma unroll
+    for (int q = 0; q < NV; ++q) sum[q] = wave_sum(sum[q]);
 
     if (edge_lds) {
       unsigned spins = 0;
@@ -241,7 +277,7 @@ __device__ __forceinline__ T grid_dot(T v, const T* edge_lds, T* ghost_lds, int 
         for (int k = 0; k < GP; ++k) {
           const int q = lane + k * kWave;
           if (q < n_edge) {
-            const u64* src = q < half ? xc.left : xc.right;
+            const u64* src = q < half ? left : right;
             if (src) gok &= get_tagged(src + (q < half ? q + half : q - half) * WD, bar, gv[k]);
           }
         }
@@ -250,10 +286,14 @@ __device__ __forceinline__ T grid_dot(T v, const T* edge_lds, T* ghost_lds, int 
       for (int k = 0; k < GP; ++k)
         if (lane + k * kWave < n_edge) ghost_lds[lane + k * kWave] = gv[k];
     }
-    if (lane == 0) *bcast = s;
+    if (lane == 0) {
+#pragma unroll
+      for (int q = 0; q < NV; ++q) bcast[q] = sum[q];
+    }
   }
   __syncthreads();
-  return *bcast;
+#pragma unroll
+  for (int q = 0; q < NV; ++q) out[q] = bcast[q];
 }
 
 template <typename T, int SS, bool RES>
@@ -282,8 +322,8 @@ pcg_grid_kernel(GridArgs<T> a) {
   T* r_loc = p_loc + loc_len;                 // same indexing
   T* edge_lds = r_loc + loc_len;              // [4*ss] z of A, A+1, B-2, B-1
   T* ghost_lds = edge_lds + n_edge;           // [4*ss] z of A-2, A-1, B, B+1
-  T* wsl = ghost_lds + n_edge;                // [NW]
-  T* bcast = wsl + NW;                        // [1]
+  T* wsl = ghost_lds + n_edge;                // [kDotValues][NW]
+  T* bcast = wsl + kDotValues * NW;           // [kDotValues]
 
   // This thread's extended row.
   const int e = tid;
@@ -313,14 +353,17 @@ pcg_grid_kernel(GridArgs<T> a) {
   xc.my_edges = a.edges + (size_t)g * n_edge * WD;
   xc.left = g > 0 ? a.edges + (size_t)(g - 1) * n_edge * WD : nullptr;
   xc.right = g + 1 < G ? a.edges + (size_t)(g + 1) * n_edge * WD : nullptr;
+  xc.edge_parity = (size_t)G * n_edge * WD;
   xc.flags = a.flags;
   xc.G = G;
   xc.g = g;
   unsigned int barriers = 0;
   auto dot = [&](T v, bool with_edges) {
     ++barriers;
-    return grid_dot<T, GP>(v, with_edges ? edge_lds : (const T*)nullptr, ghost_lds, n_edge, xc,
-                           barriers, wsl, bcast, NW, wave, lane);
+    T in[1] = {v}, out[1];
+    grid_dot_n<T, GP, 1>(in, out, with_edges ? edge_lds : (const T*)nullptr, ghost_lds, n_edge,
+                         xc, barriers, wsl, bcast, NW, wave, lane);
+    return out[0];
   };
 
   // Matrix rows in registers (specialised sizes): S for every valid extended
@@ -438,10 +481,219 @@ pcg_grid_kernel(GridArgs<T> a) {
   }
 }
 
+// Single-reduction PCG over the same placement (the communication-reducing
+// form of Chronopoulos and Gear, preconditioned as written out by Ghysels and
+// Vanroose): in exact arithmetic the same iterates, stopping rule and
+// iteration count as the standard steps, with r^T u and w^T u reduced in one
+// grid dot, so one grid barrier per iteration instead of two (the rounding
+// differs).  u = Pinv r, w = S u, and further recurrence vectors replace the
+// second dot:
+//   r0 = b - S x0; u0 = Pinv r0; w0 = S u0
+//   for i = 0, 1, ...:  gamma = r^T u; delta = w^T u       (one reduction)
+//     stop when |gamma| < thresh (i updates done) or i = max_iters
+//     m = Pinv w; n = S m
+//     beta = gamma / gamma_prev (0 at i = 0)
+//     d = delta - beta gamma / alpha_prev (delta at i = 0)  [= p^T S p]
+//     d not positive: breakdown; alpha = gamma / d
+//     z = n + beta z; q = m + beta q; s = w + beta s; p = u + beta p
+//     x += alpha p; r -= alpha s; u -= alpha q; w -= alpha z
+// Each workgroup keeps Pinv rows for its extended rows A-1 .. B as well, so
+// m is computed there and n = S m needs no exchange; the reduction carries the
+// owners' w of their two edge block-rows on each side.  One more exchange at
+// the start carries u0's edges for w0.
+template <typename T, int SS, bool RES>
+__global__ void __launch_bounds__(RES ? 512 : 1024)
+pcg_grid_cg1_kernel(GridArgs<T> a) {
+  constexpr int WC = SS > 0 ? 3 * SS : 1;
+  const int ss = SS > 0 ? SS : a.ss;
+  const int W = 3 * ss;
+  const int kp = a.kp;
+  const int G = a.G;
+  const int NT = blockDim.x;
+  const int NW = NT >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bid = blockIdx.x;
+  const int g = (G % 8 == 0) ? (bid % 8) * (G / 8) + bid / 8 : bid;
+  const int A = (int)((long long)g * kp / G);
+  const int B = (int)((long long)(g + 1) * kp / G);
+  const int nb = B - A;
+  const int next = (nb + 2) * ss;  // extended rows: block-rows A-1 .. B
+  const int loc_len = (a.nb_max + 4) * ss;
+  const int n_edge = 4 * ss;
+
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  T* w_loc = reinterpret_cast<T*>(smem_raw);  // block-rows A-2 .. B+1
+  T* m_loc = w_loc + loc_len;                 // same indexing
+  T* edge_lds = m_loc + loc_len;              // [4*ss] values of A, A+1, B-2, B-1
+  T* ghost_lds = edge_lds + n_edge;           // [4*ss] values of A-2, A-1, B, B+1
+  T* wsl = ghost_lds + n_edge;                // [kDotValues][NW]
+  T* bcast = wsl + kDotValues * NW;           // [kDotValues]
+
+  const int e = tid;
+  const int br = A - 1 + (e < next ? e / ss : 0);
+  const int i = e < next ? e % ss : 0;
+  const bool valid = e < next && br >= 0 && br < kp;
+  const bool own = valid && br >= A && br < B;
+  const long long grow = (long long)br * ss + i;
+  const int wstart = (e < next ? e / ss : 0) * ss;
+
+  auto ghost = [&](int gbr, int gi) -> T {
+    return gbr < A ? ghost_lds[(gbr - (A - 2)) * ss + gi] : ghost_lds[2 * ss + (gbr - B) * ss + gi];
+  };
+  auto stage_edges = [&](T val) {
+    if (!own) return;
+    if (br < A + 2) edge_lds[(br - A) * ss + i] = val;
+    if (br >= B - 2) edge_lds[2 * ss + (br - (B - 2)) * ss + i] = val;
+  };
+  // Fill a window vector on block-rows A-2 .. B+1 from this workgroup's own
+  // values and the neighbours' edges.
+  auto fill_window = [&](T* loc, T own_val) {
+    if (e < next) loc[e + ss] = valid ? (own ? own_val : ghost(br, i)) : T(0);
+    if (tid < ss) loc[tid] = ghost(A - 2, tid);
+    else if (tid < 2 * ss) loc[(nb + 3) * ss + tid - ss] = ghost(B + 1, tid - ss);
+  };
+  constexpr int GP = SS > 0 ? (4 * SS + kWave - 1) / kWave : (4 * 64 + kWave - 1) / kWave;
+  constexpr int WD = kTagWords<T>;
+  GridXchg xc;
+  xc.part = a.part;
+  xc.my_edges = a.edges + (size_t)g * n_edge * WD;
+  xc.left = g > 0 ? a.edges + (size_t)(g - 1) * n_edge * WD : nullptr;
+  xc.right = g + 1 < G ? a.edges + (size_t)(g + 1) * n_edge * WD : nullptr;
+  xc.edge_parity = (size_t)G * n_edge * WD;
+  xc.flags = a.flags;
+  xc.G = G;
+  xc.g = g;
+  unsigned int barriers = 0;
+  auto dot2 = [&](T v0, T v1, T (&out)[2]) {
+    ++barriers;
+    T in[2] = {v0, v1};
+    grid_dot_n<T, GP, 2>(in, out, edge_lds, ghost_lds, n_edge, xc, barriers, wsl, bcast, NW,
+                         wave, lane);
+  };
+
+  // S and Pinv rows of every valid extended row.
+  T mS[WC], mP[WC];
+  if constexpr (RES) {
+#pragma unroll
+    for (int c = 0; c < WC; ++c) {
+      mS[c] = T(0);
+      mP[c] = T(0);
+    }
+    if (valid) {
+      if (a.wide) {
+        load_row_regs<T, WC, true>(mS, a.S + grow * WC);
+        load_row_regs<T, WC, true>(mP, a.P + grow * WC);
+      } else {
+        load_row_regs<T, WC, false>(mS, a.S + grow * WC);
+        load_row_regs<T, WC, false>(mP, a.P + grow * WC);
+      }
+    }
+  }
+  auto row_dot = [&](const T* __restrict__ gM, const T* __restrict__ mreg,
+                     const T* __restrict__ vloc) -> T {
+    T acc = T(0);
+    const T* __restrict__ w = vloc + wstart;
+    if constexpr (RES) {
+#pragma unroll
+      for (int c = 0; c < WC; ++c) acc = fma(mreg[c], w[c], acc);
+    } else {
+      const T* __restrict__ m = gM + grow * W;
+      for (int c = 0; c < W; ++c) acc = fma(m[c], w[c], acc);
+    }
+    return acc;
+  };
+
+  // r0 on the extended rows from x0 on A-2 .. B+1 (w_loc), u0 on own rows.
+  for (int j = tid; j < (nb + 4) * ss; j += NT) {
+    const int gbr = A - 2 + j / ss;
+    w_loc[j] = (gbr >= 0 && gbr < kp) ? a.x[(long long)gbr * ss + j % ss] : T(0);
+    m_loc[j] = T(0);
+  }
+  T xr = own ? a.x[grow] : T(0);
+  const T bb = valid ? a.b[grow] : T(0);
+  __syncthreads();
+  T rr = valid ? bb - row_dot(a.S, mS, w_loc) : T(0);
+  if (e < next) m_loc[e + ss] = rr;
+  __syncthreads();
+  T uu = own ? row_dot(a.P, mP, m_loc) : T(0);
+  // Exchange u0's edges (the sums are not used), then w0 = S u0.
+  stage_edges(uu);
+  T red[2];
+  dot2(own ? rr * uu : T(0), T(0), red);
+  fill_window(w_loc, uu);
+  __syncthreads();
+  T ww = own ? row_dot(a.S, mS, w_loc) : T(0);
+
+  T zz = T(0), qq = T(0), sv = T(0), pp = T(0);
+  T rho0 = T(0), rho_last = T(0), thresh = T(0);
+  T gamma_prev = T(1), alpha_prev = T(1);
+  int iters = 0;
+  int status = GLASS_PCG_MAX_ITERS;
+  for (int it = 0;; ++it) {
+    stage_edges(ww);
+    dot2(own ? rr * uu : T(0), own ? ww * uu : T(0), red);
+    const T gamma = red[0], delta = red[1];
+    rho_last = gamma;
+    if (it == 0) {
+      rho0 = gamma;
+      const T rho_init = fabs(gamma);
+      thresh = mul_add_unfused(a.rel_tol, rho_init, a.abs_tol);
+      if (rho_init == T(0) || rho_init < thresh) {
+        status = GLASS_PCG_CONVERGED;
+        break;
+      }
+    } else if (fabs(gamma) < thresh) {
+      status = GLASS_PCG_CONVERGED;
+      break;
+    }
+    if (it >= a.max_iters) break;  // GLASS_PCG_MAX_ITERS
+    // m = Pinv w on the extended rows, n = S m on own rows.
+    fill_window(w_loc, ww);
+    __syncthreads();
+    const T mm = valid ? row_dot(a.P, mP, w_loc) : T(0);
+    if (e < next) m_loc[e + ss] = mm;
+    __syncthreads();
+    const T nn = own ? row_dot(a.S, mS, m_loc) : T(0);
+    const T beta = it == 0 ? T(0) : gamma / gamma_prev;
+    const T d = it == 0 ? delta : delta - beta * gamma / alpha_prev;
+    if (!(d > T(0)) || !is_finite_val(d)) {
+      status = GLASS_PCG_BREAKDOWN;
+      break;
+    }
+    const T alpha = gamma / d;
+    if (own) {
+      zz = fma(beta, zz, nn);
+      qq = fma(beta, qq, mm);
+      sv = fma(beta, sv, ww);
+      pp = fma(beta, pp, uu);
+      xr = fma(alpha, pp, xr);
+      rr = fma(-alpha, sv, rr);
+      uu = fma(-alpha, qq, uu);
+      ww = fma(-alpha, zz, ww);
+    }
+    gamma_prev = gamma;
+    alpha_prev = alpha;
+    iters = it + 1;
+  }
+
+  if (iters > 0 && own) a.x[grow] = xr;
+  if (g == 0 && tid == 0) {
+    const bool timed_out =
+        __hip_atomic_load(a.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+    if (a.iters) a.iters[0] = iters;
+    if (a.status) a.status[0] = timed_out ? GLASS_PCG_GRID_TIMEOUT : status;
+    if (a.rho) {
+      a.rho[0] = rho0;
+      a.rho[1] = rho_last;
+    }
+  }
+}
+
 template <typename T, int SS, bool RES>
 int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
-                      bool exclusive, hipStream_t st) {
-  auto kern = pcg_grid_kernel<T, SS, RES>;
+                      bool exclusive, bool single, hipStream_t st) {
+  auto kern = single ? pcg_grid_cg1_kernel<T, SS, RES> : pcg_grid_kernel<T, SS, RES>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -454,8 +706,8 @@ int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
   if ((long long)per_cu * dev.cu_count < a.G)
     return fail(GLASS_ECOOP, "grid pcg: workgroups cannot all be co-resident");
   // Tag words this grid reads: both partial buffers and the edges.
-  const int n_part = 2 * a.G * kTagWords<T>;
-  const int n_edge = a.G * 4 * a.ss * kTagWords<T>;
+  const int n_part = 2 * a.G * kDotValues * kTagWords<T>;
+  const int n_edge = 2 * a.G * 4 * a.ss * kTagWords<T>;
   const int reset_blocks = std::min(256, (std::max(n_part, n_edge) + 255) / 256);
   hipLaunchKernelGGL(grid_reset_kernel, dim3(reset_blocks), dim3(256), 0, st, a.flags, a.part,
                      n_part, a.edges, n_edge);
@@ -488,9 +740,9 @@ constexpr bool kGridResidentFits(int ss) {
 
 template <typename T, int SS>
 int launch_grid_res(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
-                    bool exclusive, hipStream_t st) {
+                    bool exclusive, bool single, hipStream_t st) {
   if constexpr (kGridResidentFits<T>(SS))
-    return launch_grid_typed<T, SS, true>(a, NT, lds, dev, exclusive, st);
+    return launch_grid_typed<T, SS, true>(a, NT, lds, dev, exclusive, single, st);
   return fail(GLASS_EUNSUPPORTED, "grid pcg: internal plan error");
 }
 
@@ -498,7 +750,7 @@ template <typename T>
 int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
                 int max_iters, double rel_tol, double abs_tol, int* iters,
                 int* status, T* rho, void* workspace, size_t ws_bytes,
-                bool exclusive, hipStream_t st) {
+                bool exclusive, bool single, hipStream_t st) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   if (!dev.cooperative)
@@ -528,7 +780,7 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   }
   const int NW = NT / 64;
   const size_t loc_len = (size_t)(nb_max + 4) * ss;
-  const size_t lds = (2 * loc_len + 8 * (size_t)ss + NW + 1) * sizeof(T);
+  const size_t lds = (2 * loc_len + 8 * (size_t)ss + (size_t)kDotValues * (NW + 1)) * sizeof(T);
   if (lds > dev.max_lds_per_block)
     return fail(GLASS_EUNSUPPORTED, "grid pcg: partition does not fit in LDS");
 
@@ -554,13 +806,13 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.wide = aligned(S, 16) && aligned(P, 16);
   if (res) {
     switch (ss) {
-      case 6: return launch_grid_res<T, 6>(a, NT, lds, dev, exclusive, st);
-      case 12: return launch_grid_res<T, 12>(a, NT, lds, dev, exclusive, st);
-      case 14: return launch_grid_res<T, 14>(a, NT, lds, dev, exclusive, st);
-      default: return launch_grid_res<T, 21>(a, NT, lds, dev, exclusive, st);
+      case 6: return launch_grid_res<T, 6>(a, NT, lds, dev, exclusive, single, st);
+      case 12: return launch_grid_res<T, 12>(a, NT, lds, dev, exclusive, single, st);
+      case 14: return launch_grid_res<T, 14>(a, NT, lds, dev, exclusive, single, st);
+      default: return launch_grid_res<T, 21>(a, NT, lds, dev, exclusive, single, st);
     }
   }
-  return launch_grid_typed<T, 0, false>(a, NT, lds, dev, exclusive, st);
+  return launch_grid_typed<T, 0, false>(a, NT, lds, dev, exclusive, single, st);
 }
 
 }  // namespace
@@ -573,16 +825,16 @@ int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     const void* b, int ss, int kp, int max_iters,
                     double rel_tol, double abs_tol, int* iters, int* status,
                     void* rho, void* workspace, size_t workspace_bytes,
-                    bool exclusive, hipStream_t stream) {
+                    bool exclusive, bool single, hipStream_t stream) {
   if (dt == GLASS_F32)
     return launch_grid<float>((float*)x, (const float*)S, (const float*)Pinv,
                               (const float*)b, ss, kp, max_iters, rel_tol,
                               abs_tol, iters, status, (float*)rho, workspace,
-                              workspace_bytes, exclusive, stream);
+                              workspace_bytes, exclusive, single, stream);
   return launch_grid<double>((double*)x, (const double*)S, (const double*)Pinv,
                              (const double*)b, ss, kp, max_iters, rel_tol,
                              abs_tol, iters, status, (double*)rho, workspace,
-                             workspace_bytes, exclusive, stream);
+                             workspace_bytes, exclusive, single, stream);
 }
 
 }  // namespace glass

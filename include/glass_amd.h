@@ -186,9 +186,17 @@ int glass_pcg_batched_placement(int state_size, int knot_points,
  *     cannot all start, the bounded barrier waits expire and the solve
  *     reports GLASS_PCG_GRID_TIMEOUT (after up to a few seconds) instead of
  *     hanging; x is then unspecified.
+ *   GLASS_GRID_SINGLE_REDUCTION  the single-reduction form of PCG
+ *     (Chronopoulos and Gear, preconditioned): u = Pinv r and w = S u are
+ *     carried by recurrences, so r^T u and w^T u are reduced together and
+ *     each iteration needs one grid-wide reduction instead of two.  In exact
+ *     arithmetic it has the same iterates, stopping rule, iteration count,
+ *     breakdown test (its step denominator equals p^T S p) and outputs as the
+ *     steps above; in floating point it rounds differently.  It holds S and
+ *     Pinv rows for one more block-row on each side of a workgroup's range.
  * Other flag bits return GLASS_EINVAL.
  */
-enum { GLASS_GRID_EXCLUSIVE = 1u };
+enum { GLASS_GRID_EXCLUSIVE = 1u, GLASS_GRID_SINGLE_REDUCTION = 2u };
 size_t glass_pcg_grid_workspace_bytes(int state_size, int knot_points,
                                       glass_dtype dtype);
 int glass_pcg_grid(void* x, const void* S, const void* Pinv, const void* b,

@@ -107,7 +107,8 @@ def test_grid_argument_errors_and_workspace_size(lib):
         return lib.glass_pcg_grid_ex(FAKE, FAKE, FAKE, FAKE, 12, 8192, 10, 1e-10, 0.0,
                                      FAKE, None, None, ctypes.c_void_p(0x100000), ws, 1,
                                      flags, None)
-    assert grid_ex(2) == EINVAL  # unknown flag bit
+    assert grid_ex(4) == EINVAL  # unknown flag bit
+    assert grid_ex(1 | 2 | 8) == EINVAL
     assert grid_ex(0x80000000) == EINVAL
 
 

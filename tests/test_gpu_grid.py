@@ -14,7 +14,15 @@ from gpu_common import X_REL, assert_pcg_parity, say, to_dev
 pytestmark = pytest.mark.gpu
 
 
-def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, exclusive=False):
+@pytest.fixture(params=["standard", "single"])
+def variant(request):
+    """The standard steps (two grid reductions per iteration) or the
+    single-reduction form (GLASS_GRID_SINGLE_REDUCTION); both are held to
+    the same oracle bar."""
+    return request.param == "single"
+
+
+def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, exclusive=False, single=False):
     t = {k: to_dev(v) for k, v in inp.items()}
     x = t["x0"].clone()
     iters = torch.full((1,), -1, dtype=torch.int32, device="cuda")
@@ -23,18 +31,18 @@ def grid_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, exclusive=False):
     nbytes = glass.pcg_grid_workspace_bytes(ss, kp, x.dtype)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     glass.pcg_grid(x, t["S"], t["Pinv"], t["b"], ss, kp, max_iters, rel_tol, abs_tol,
-                   iters, ws, status, rho, exclusive=exclusive)
+                   iters, ws, status, rho, exclusive=exclusive, single_reduction=single)
     torch.cuda.synchronize()
     return (x.cpu().numpy(), iters.cpu().numpy(), status.cpu().numpy(),
             rho.cpu().numpy().reshape(1, 2))
 
 
-def test_grid_full_chain_fp64(gpu):
+def test_grid_full_chain_fp64(gpu, variant):
     """The kp=8192, ss=12 fp64 chain, every entry of x checked."""
     w = workloads.WORKLOADS[4]
     inp = workloads.generate(w)
-    say("grid ss=12 kp=8192 fp64")
-    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    say("grid ss=12 kp=8192 fp64 single=%s" % variant)
+    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, single=variant)
     assert res[2][0] == gpu.CONVERGED, res[2]
     its = assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float64)
     say("  iterations: %d" % its[0])
@@ -44,7 +52,7 @@ def test_grid_full_chain_fp64(gpu):
                                          (14, 97, np.float32), (21, 40, np.float32),
                                          (5, 33, np.float64), (3, 4, np.float64),
                                          (12, 5000, np.float32)])
-def test_grid_matches_oracle_and_batched(gpu, ss, kp, dtype):
+def test_grid_matches_oracle_and_batched(gpu, ss, kp, dtype, variant):
     """Specialised and runtime state sizes, partitions of uneven length, the
     minimum chain (kp = 4).  Also cross-checked with the batched solve of the
     same single problem."""
@@ -54,8 +62,8 @@ def test_grid_matches_oracle_and_batched(gpu, ss, kp, dtype):
            "b": rng.standard_normal((1, kp * ss)).astype(dtype),
            "x0": np.zeros((1, kp * ss), dtype)}
     rel = 1e-10 if dtype == np.float64 else 1e-7
-    say("grid ss=%d kp=%d %s" % (ss, kp, np.dtype(dtype).name))
-    res = grid_gpu(gpu, inp, ss, kp, 500, rel, 0.0)
+    say("grid ss=%d kp=%d %s single=%s" % (ss, kp, np.dtype(dtype).name, variant))
+    res = grid_gpu(gpu, inp, ss, kp, 500, rel, 0.0, single=variant)
     assert res[2][0] == gpu.CONVERGED
     assert_pcg_parity(inp, ss, kp, 500, rel, 0.0, res, dtype)
     if kp * ss <= 8192:
@@ -69,7 +77,7 @@ def test_grid_matches_oracle_and_batched(gpu, ss, kp, dtype):
 
 
 @pytest.mark.parametrize("wgs", [2, 8, 24, 64, 512])
-def test_grid_partition_count_does_not_change_the_answer(gpu, monkeypatch, wgs):
+def test_grid_partition_count_does_not_change_the_answer(gpu, monkeypatch, wgs, variant):
     """Different grid sizes change only the summation tree of the dots."""
     rng = np.random.default_rng(77)
     ss, kp = 12, 2048
@@ -77,13 +85,13 @@ def test_grid_partition_count_does_not_change_the_answer(gpu, monkeypatch, wgs):
     inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D), "b": rng.standard_normal((1, kp * ss)),
            "x0": np.zeros((1, kp * ss))}
     monkeypatch.setenv("GLASS_AMD_GRID_WGS", str(wgs))
-    say("grid wgs=%d" % wgs)
-    res = grid_gpu(gpu, inp, ss, kp, 200, 1e-10, 0.0)
+    say("grid wgs=%d single=%s" % (wgs, variant))
+    res = grid_gpu(gpu, inp, ss, kp, 200, 1e-10, 0.0, single=variant)
     assert res[2][0] == gpu.CONVERGED
     assert_pcg_parity(inp, ss, kp, 200, 1e-10, 0.0, res, np.float64)
 
 
-def test_grid_status_cases(gpu):
+def test_grid_status_cases(gpu, variant):
     rng = np.random.default_rng(5)
     ss, kp = 6, 64
     S, D = workloads.random_spd_strips(rng, 1, ss, kp, 0.3, np.float64)
@@ -91,28 +99,29 @@ def test_grid_status_cases(gpu):
     b = rng.standard_normal((1, kp * ss))
     x0 = rng.standard_normal((1, kp * ss))
     base = {"S": S, "Pinv": P, "b": b, "x0": x0}
-    say("grid max_iters=3")
-    x, it, st, _ = grid_gpu(gpu, base, ss, kp, 3, 1e-12, 0.0)
+    say("grid max_iters=3 single=%s" % variant)
+    x, it, st, _ = grid_gpu(gpu, base, ss, kp, 3, 1e-12, 0.0, single=variant)
     assert it[0] == 3 and st[0] == gpu.MAX_ITERS
     xo, _, _, _ = oracle.pcg(x0, S, P, b, ss, kp, 3, 1e-12, 0.0, "f64")
     assert np.linalg.norm(x - xo) <= 1e-10 * np.linalg.norm(xo)
     say("grid breakdown")
-    x, it, st, _ = grid_gpu(gpu, dict(base, S=-S), ss, kp, 20, 1e-8, 0.0)
+    x, it, st, _ = grid_gpu(gpu, dict(base, S=-S), ss, kp, 20, 1e-8, 0.0, single=variant)
     assert st[0] == gpu.BREAKDOWN and it[0] == 0
     np.testing.assert_array_equal(x, x0)
     say("grid b=0, x0=0")
-    x, it, st, _ = grid_gpu(gpu, dict(base, b=0 * b, x0=0 * x0), ss, kp, 20, 1e-8, 0.0)
+    x, it, st, _ = grid_gpu(gpu, dict(base, b=0 * b, x0=0 * x0), ss, kp, 20, 1e-8, 0.0,
+                            single=variant)
     assert st[0] == gpu.CONVERGED and it[0] == 0 and np.all(x == 0)
 
 
-def test_grid_full_chain_fp32_variant(gpu):
+def test_grid_full_chain_fp32_variant(gpu, variant):
     """The float32 variant of the kp=8192 chain as bench.py times it
     (rel_tol 1e-7), every entry of x checked."""
     from dataclasses import replace
     w = replace(workloads.WORKLOADS[4], dtype=np.float32, rel_tol=1e-7)
     inp = workloads.generate(w)
-    say("grid ss=12 kp=8192 fp32")
-    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    say("grid ss=12 kp=8192 fp32 single=%s" % variant)
+    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, single=variant)
     assert res[2][0] == gpu.CONVERGED, res[2]
     assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float32)
 
@@ -143,3 +152,23 @@ def test_grid_exclusive_launch_is_bit_identical(gpu, ss, kp, dtype):
         assert excl[2][0] == gpu.CONVERGED
         for a, b in zip(coop, excl):
             np.testing.assert_array_equal(a, b)
+
+
+def test_grid_single_reduction_agrees_with_standard_and_repeats(gpu):
+    """The single-reduction form against the standard steps on the fp64
+    chain: the same iteration count and status, x within 1e-12 relative
+    (rounding only), rho_init equal to rounding; and bit-identical repeats,
+    also with the exclusive launch."""
+    w = workloads.WORKLOADS[4]
+    inp = workloads.generate(w)
+    say("grid single vs standard fp64")
+    std = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    one = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, single=True)
+    assert one[1][0] == std[1][0] and one[2][0] == std[2][0]
+    rel = np.linalg.norm(one[0] - std[0]) / np.linalg.norm(std[0])
+    assert rel <= 1e-12, rel
+    np.testing.assert_allclose(one[3][0, 0], std[3][0, 0], rtol=1e-12)
+    again = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, single=True,
+                     exclusive=True)
+    for u, v in zip(one, again):
+        np.testing.assert_array_equal(u, v)
