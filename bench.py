@@ -63,7 +63,7 @@ KERNEL_OF = {
     "bdsv2": "bdsv_rows_kernel<float, 14,",
     "pcg2_f64": "pcg_batched_kernel<double, 14, 1, 2>",
     "grid4_f32": "pcg_grid_kernel<float, 12,",
-    "pcg2_pd": "pcg_batched_kernel<float, 14, 1, 3>",
+    "pcg2_pd": "pcg_batched_kernel<float, 14, 2, 3>",
     "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 4>",
     "grid4_sr": "pcg_grid_cg1_kernel<double, 12,",
     "grid4_f32_sr": "pcg_grid_cg1_kernel<float, 12,",
