@@ -47,6 +47,8 @@
 // * Bounded polls: a poll that exceeds its spin limit sets a flag, every
 //   other poll stops as soon as it sees the flag, the kernel runs to its end,
 //   and the status output reports the timeout instead of the device hanging.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -54,6 +56,8 @@ namespace glass {
 namespace {
 
 constexpr int kGridMaxWorkgroups = 2048;
+// Poll rounds before a wait gives up (GLASS_AMD_GRID_SPIN_LIMIT overrides it,
+// which lets tests drive the timeout path from the host).
 constexpr unsigned kSpinLimit = 1u << 21;
 
 template <typename T>
@@ -77,6 +81,7 @@ struct GridArgs {
   int G;
   int nb_max;
   int wide;               // matrix bases 16-byte aligned: vector row loads
+  unsigned spin_limit;    // poll rounds before a wait gives up
 };
 
 typedef unsigned long long u64;
@@ -149,13 +154,14 @@ __device__ __forceinline__ bool get_tagged(const u64* src, unsigned tag, double&
 
 // One more round of a bounded poll by a whole wave (see the timeout rule at
 // the top of the file); false when the poll must stop.
-__device__ __forceinline__ bool keep_polling(unsigned& spins, unsigned int* flags, int lane) {
+__device__ __forceinline__ bool keep_polling(unsigned& spins, unsigned int* flags, int lane,
+                                             unsigned limit) {
   __builtin_amdgcn_s_sleep(1);
   ++spins;
   if ((spins & 63u) == 0u &&
       __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
     return false;  // another workgroup already gave up: do not wait again
-  if (spins > kSpinLimit) {
+  if (spins > limit) {
     if (lane == 0) __hip_atomic_store(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
   }
@@ -174,6 +180,7 @@ struct GridXchg {
   const u64* right;  // right neighbour's edges, or null (last partition)
   size_t edge_parity;
   unsigned int* flags;
+  unsigned spin_limit;
   int G, g;
 };
 
@@ -256,7 +263,7 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
           }
         }
         if (__all(ok)) break;
-        if (!keep_polling(spins, xc.flags, lane)) break;
+        if (!keep_polling(spins, xc.flags, lane, xc.spin_limit)) break;
       }
 #pragma unroll
       for (int k = 0; k < kSumBatch; ++k)
@@ -271,7 +278,7 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
     if (edge_lds) {
       unsigned spins = 0;
       while (!__all(gok)) {
-        if (!keep_polling(spins, xc.flags, lane)) break;
+        if (!keep_polling(spins, xc.flags, lane, xc.spin_limit)) break;
         gok = true;
 #pragma unroll
         for (int k = 0; k < GP; ++k) {
@@ -354,6 +361,7 @@ pcg_grid_kernel(GridArgs<T> a) {
   xc.left = g > 0 ? a.edges + (size_t)(g - 1) * n_edge * WD : nullptr;
   xc.right = g + 1 < G ? a.edges + (size_t)(g + 1) * n_edge * WD : nullptr;
   xc.edge_parity = (size_t)G * n_edge * WD;
+  xc.spin_limit = a.spin_limit;
   xc.flags = a.flags;
   xc.G = G;
   xc.g = g;
@@ -561,6 +569,7 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
   xc.left = g > 0 ? a.edges + (size_t)(g - 1) * n_edge * WD : nullptr;
   xc.right = g + 1 < G ? a.edges + (size_t)(g + 1) * n_edge * WD : nullptr;
   xc.edge_parity = (size_t)G * n_edge * WD;
+  xc.spin_limit = a.spin_limit;
   xc.flags = a.flags;
   xc.G = G;
   xc.g = g;
@@ -804,6 +813,12 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.G = G;
   a.nb_max = nb_max;
   a.wide = aligned(S, 16) && aligned(P, 16);
+  a.spin_limit = kSpinLimit;
+  if (const char* sl = std::getenv("GLASS_AMD_GRID_SPIN_LIMIT"); sl && *sl) {
+    char* end = nullptr;
+    const unsigned long v = std::strtoul(sl, &end, 10);
+    if (end != sl && *end == '\0' && v <= kSpinLimit) a.spin_limit = (unsigned)v;
+  }
   if (res) {
     switch (ss) {
       case 6: return launch_grid_res<T, 6>(a, NT, lds, dev, exclusive, single, st);

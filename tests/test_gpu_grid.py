@@ -172,3 +172,21 @@ def test_grid_single_reduction_agrees_with_standard_and_repeats(gpu):
                      exclusive=True)
     for u, v in zip(one, again):
         np.testing.assert_array_equal(u, v)
+
+
+def test_grid_timeout_path_reports_and_drains(gpu, monkeypatch, variant):
+    """The bounded-poll path, forced from the host: with a spin limit of 0
+    the first poll that finds a partial missing gives up (workgroups reach
+    the first barrier microseconds apart after their row loads).  The solve
+    reports GLASS_PCG_GRID_TIMEOUT, every workgroup leaves (the call
+    returns), and the next solve on the same workspace is normal."""
+    w = workloads.WORKLOADS[4]
+    inp = workloads.generate(w)
+    monkeypatch.setenv("GLASS_AMD_GRID_SPIN_LIMIT", "0")
+    say("grid forced timeout single=%s" % variant)
+    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, single=variant)
+    assert res[2][0] == gpu.GRID_TIMEOUT, res[2]
+    monkeypatch.delenv("GLASS_AMD_GRID_SPIN_LIMIT")
+    res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, single=variant)
+    assert res[2][0] == gpu.CONVERGED
+    assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float64)
