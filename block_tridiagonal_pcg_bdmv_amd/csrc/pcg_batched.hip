@@ -24,8 +24,8 @@
 //   every placement (number of waves, rows per lane, resident or streamed).
 //   Two slot arrays alternate so one barrier per dot suffices.
 // * matrices: RESIDENT -- each lane holds its S row and Pinv row in VGPRs,
-//   loaded once: coalesced 16-byte loads of the wave's 64-row chunks (all in
-//   flight), transposed into rows through a per-wave LDS stage;
+//   loaded once straight from memory with every load of both rows in flight
+//   (the widest loads the row alignment allows);
 //   STREAMED -- every matvec re-stages the wave's 64-row chunk of S or
 //   Pinv HBM/L2 -> LDS (coalesced 16-byte loads) and each lane multiplies its
 //   row from there.  With PREFETCH, the wave's next two chunks in the fixed
