@@ -65,6 +65,8 @@ KERNEL_OF = {
     "grid4_f32": "pcg_grid_kernel<float, 12,",
     "pcg2_pd": "pcg_batched_kernel<float, 14, 2, 3>",
     "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 4>",
+    "pcg2_pdp": "pcg_batched_kernel<float, 14, 2, 6>",
+    "pcg3_pdp": "pcg_batched_kernel<float, 21, 3, 5>",
     "grid4_sr": "pcg_grid_cg1_kernel<double, 12,",
     "grid4_f32_sr": "pcg_grid_cg1_kernel<float, 12,",
 }
@@ -72,11 +74,15 @@ KERNEL_OF = {
 # same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
 # are the precision variants of pcg2 and grid4 (same recipe and seeds).
 CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2,
-             "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3, "grid4_sr": 4, "grid4_f32_sr": 4}
+             "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3, "pcg2_pdp": 2,
+             "pcg3_pdp": 3, "grid4_sr": 4, "grid4_f32_sr": 4}
 # Workloads run with GLASS_PCG_PINV_BLOCK_DIAGONAL (their Pinv is block-Jacobi,
 # so the assertion holds): pcg2_pd and pcg3_pd are the ss=14 and ss=21
 # workloads with the hint.
 PINV_DIAG = {"pcg2_pd", "pcg3_pd"}
+# Workloads run with GLASS_PCG_PINV_DIAGONAL_BLOCKS: the same systems with
+# Pinv passed as its packed D blocks [B, kp, ss, ss].
+PINV_PACKED = {"pcg2_pdp", "pcg3_pdp"}
 # Grid workloads run in the single-reduction form (GLASS_GRID_SINGLE_REDUCTION).
 SINGLE_RED = {"grid4_sr", "grid4_f32_sr"}
 VARIANT_OF = {
@@ -85,6 +91,8 @@ VARIANT_OF = {
                          rel_tol=1e-7),
     "pcg2_pd": dict(name="pcg_ss14_kp32_b4096_f32_pinv_blockdiag"),
     "pcg3_pd": dict(name="pcg_ss21_kp64_b2048_f32_pinv_blockdiag"),
+    "pcg2_pdp": dict(name="pcg_ss14_kp32_b4096_f32_pinv_diagonal_blocks"),
+    "pcg3_pdp": dict(name="pcg_ss21_kp64_b2048_f32_pinv_diagonal_blocks"),
     "pcg2_f64": dict(name="pcg_ss14_kp32_b4096_f64", dtype=np.float64),
     "grid4_f32": dict(name="grid_pcg_ss12_kp8192_f32", dtype=np.float32, rel_tol=1e-7),
 }
@@ -321,10 +329,13 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     w = workload_of(key)
     inp = workloads.generate(w)
     dev = torch.device("cuda:0")
+    packed = key in PINV_PACKED
     S = torch.from_numpy(inp["S"]).to(dev)
     P = torch.from_numpy(inp["Pinv"]).to(dev)
-    b = torch.from_numpy(inp["b"]).to(dev)
     B = w.n_problems
+    if packed:  # the D blocks alone, [B, kp, ss, ss]
+        P = P.reshape(B, w.kp, w.ss, 3 * w.ss)[:, :, :, w.ss:2 * w.ss].contiguous()
+    b = torch.from_numpy(inp["b"]).to(dev)
     xs = [torch.zeros((B, w.n), dtype=S.dtype, device=dev) for _ in range(steps + warmup)]
     iters = torch.zeros(B, dtype=torch.int32, device=dev)
     grid = w.kind == "grid"
@@ -343,7 +354,7 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
                            exclusive=exclusive, single_reduction=single)
         else:
             glass.pcg_batched(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters,
-                              pinv_block_diagonal=pd)
+                              pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
 
     for k in range(warmup):
         run(xs[steps + k])
@@ -362,8 +373,9 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     # S and Pinv count once if they stay on chip (the grid solve and the
     # batched resident placement), else once per pass.
     resident = grid or glass.pcg_batched_placement(
-        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd) == glass.PLACEMENT_RESIDENT
-    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd)
+        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd,
+        pinv_diagonal_blocks=packed) == glass.PLACEMENT_RESIDENT
+    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed)
     for k in range(min(10, len(xs))):
         xs[k].zero_()
     iso = isolated_ms(torch, lambda k: run(xs[k]), reps=min(10, len(xs)))

@@ -21,7 +21,7 @@ __all__ = [
     "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "bdsv_workspace_bytes",
     "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
-    "PCG_PINV_BLOCK_DIAGONAL", "GRID_SINGLE_REDUCTION",
+    "PCG_PINV_BLOCK_DIAGONAL", "PCG_PINV_DIAGONAL_BLOCKS", "GRID_SINGLE_REDUCTION",
     "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED",
 ]
@@ -39,6 +39,7 @@ BDSV_OK, BDSV_NOT_SPD = 0, 1
 GRID_EXCLUSIVE = 1  # glass_pcg_grid_ex flag: ordinary dispatch on the stream's queue
 GRID_SINGLE_REDUCTION = 2  # glass_pcg_grid_ex flag: one grid reduction per iteration
 PCG_PINV_BLOCK_DIAGONAL = 1  # glass_pcg_batched_ex flag: Pinv's L and R blocks are zero
+PCG_PINV_DIAGONAL_BLOCKS = 2  # glass_pcg_batched_ex flag: Pinv is packed D blocks [B, kp, ss, ss]
 
 
 class GlassError(RuntimeError):
@@ -144,26 +145,31 @@ def bdmv_batched(y, S, v, state_size: int, knot_points: int, stream=None):
 
 def pcg_batched(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
                 rel_tol: float, abs_tol: float, iters_out, status_out=None,
-                rho_out=None, stream=None, pinv_block_diagonal=False):
+                rho_out=None, stream=None, pinv_block_diagonal=False,
+                pinv_diagonal_blocks=False):
     """Batched PCG (page "Block-tridiagonal Solves", section "Solve --
     glass::pcg").  x: [B, kp*ss] initial guess in, solution out; iters_out
     (and status_out) int32 [B]; rho_out dtype [B, 2].
     ``pinv_block_diagonal=True`` passes GLASS_PCG_PINV_BLOCK_DIAGONAL: the
-    caller asserts that Pinv's L and R blocks are zero."""
+    caller asserts that Pinv's L and R blocks are zero.
+    ``pinv_diagonal_blocks=True`` passes GLASS_PCG_PINV_DIAGONAL_BLOCKS: Pinv
+    holds only the D blocks, packed as [B, kp, ss, ss]."""
     import torch
     ss, kp = int(state_size), int(knot_points)
     B = _problems(S, ss, kp)
     dt = S.dtype
     n = kp * ss
+    p_numel = B * n * ss if pinv_diagonal_blocks else S.numel()
     a = (_dev(x, "x", B * n, dt), _dev(S, "S", S.numel(), dt),
-         _dev(Pinv, "Pinv", S.numel(), dt), _dev(b, "b", B * n, dt))
+         _dev(Pinv, "Pinv", p_numel, dt), _dev(b, "b", B * n, dt))
+    flags = (PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0) | \
+        (PCG_PINV_DIAGONAL_BLOCKS if pinv_diagonal_blocks else 0)
     it = _dev(iters_out, "iters_out", B, torch.int32)
     st = _dev(status_out, "status_out", B, torch.int32) if status_out is not None else None
     rh = _dev(rho_out, "rho_out", 2 * B, dt) if rho_out is not None else None
     rc = load().glass_pcg_batched_ex(*a, ss, kp, B, int(max_iters), float(rel_tol),
                                      float(abs_tol), it, st, rh, _dtype_code(S),
-                                     PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0,
-                                     _stream(stream))
+                                     flags, _stream(stream))
     _check(rc, "glass_pcg_batched_ex")
 
 
@@ -201,7 +207,7 @@ PLACEMENT_RESIDENT, PLACEMENT_STREAMED_PREFETCH, PLACEMENT_STREAMED = 0, 1, 2
 
 
 def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=True,
-                          pinv_block_diagonal=False) -> int:
+                          pinv_block_diagonal=False, pinv_diagonal_blocks=False) -> int:
     """Where pcg_batched keeps S and Pinv on the current device for this shape:
     PLACEMENT_RESIDENT (read once per solve) or PLACEMENT_STREAMED[_PREFETCH]
     (read once per matvec pass).  Raises for shapes the solve rejects."""
@@ -209,7 +215,9 @@ def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=Tr
     code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
     rc = load().glass_pcg_batched_placement(int(state_size), int(knot_points), code,
                                             1 if aligned16 else 0,
-                                            PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0)
+                                            (PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0)
+                                            | (PCG_PINV_DIAGONAL_BLOCKS
+                                               if pinv_diagonal_blocks else 0))
     if rc < 0:
         _check(rc, "glass_pcg_batched_placement")
     return rc

@@ -118,6 +118,10 @@ int glass_bdmv_batched(void* y, const void* S, const void* v, int state_size,
                             (hipStream_t)hip_stream);
 }
 
+// Flags of the batched PCG; packed diagonal blocks imply block-diagonal.
+constexpr unsigned kPcgFlags = GLASS_PCG_PINV_BLOCK_DIAGONAL | GLASS_PCG_PINV_DIAGONAL_BLOCKS;
+constexpr unsigned kPinvDiag = GLASS_PCG_PINV_BLOCK_DIAGONAL | GLASS_PCG_PINV_DIAGONAL_BLOCKS;
+
 int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
                          const void* b, int state_size, int knot_points,
                          int n_problems, int max_iters, double rel_tol,
@@ -125,7 +129,7 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
                          void* rho_out, glass_dtype dtype, unsigned flags,
                          void* hip_stream) {
   if (int rc = check_common(dtype, state_size, knot_points, n_problems)) return rc;
-  if (flags & ~(unsigned)GLASS_PCG_PINV_BLOCK_DIAGONAL) return fail(GLASS_EINVAL, "unknown pcg flags");
+  if (flags & ~kPcgFlags) return fail(GLASS_EINVAL, "unknown pcg flags");
   if (int rc = check_tols(max_iters, rel_tol, abs_tol)) return rc;
   if ((long long)knot_points * state_size > 8192)
     return fail(GLASS_EUNSUPPORTED, "knot_points*state_size above 8192 (use glass_pcg_grid)");
@@ -141,7 +145,8 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
   return glass::launch_pcg_batched(dtype, x, S, Pinv, b, state_size, knot_points,
                                    n_problems, max_iters, rel_tol, abs_tol,
                                    iters_out, status_out, rho_out,
-                                   (flags & GLASS_PCG_PINV_BLOCK_DIAGONAL) != 0,
+                                   (flags & kPinvDiag) != 0,
+                                   (flags & GLASS_PCG_PINV_DIAGONAL_BLOCKS) != 0,
                                    (hipStream_t)hip_stream);
 }
 
@@ -157,11 +162,12 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
 int glass_pcg_batched_placement(int state_size, int knot_points,
                                 glass_dtype dtype, int aligned16, unsigned flags) {
   if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
-  if (flags & ~(unsigned)GLASS_PCG_PINV_BLOCK_DIAGONAL) return fail(GLASS_EINVAL, "unknown pcg flags");
+  if (flags & ~kPcgFlags) return fail(GLASS_EINVAL, "unknown pcg flags");
   if ((long long)knot_points * state_size > 8192)
     return fail(GLASS_EUNSUPPORTED, "knot_points*state_size above 8192 (use glass_pcg_grid)");
   return glass::pcg_batched_placement(dtype, state_size, knot_points, aligned16 != 0,
-                                      (flags & GLASS_PCG_PINV_BLOCK_DIAGONAL) != 0);
+                                      (flags & kPinvDiag) != 0,
+                                      (flags & GLASS_PCG_PINV_DIAGONAL_BLOCKS) != 0);
 }
 
 size_t glass_bdsv_workspace_bytes(int state_size, int knot_points, int n_problems,

@@ -36,10 +36,12 @@ int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
                        const void* Pinv, const void* b, int ss, int kp,
                        int n_problems, int max_iters, double rel_tol,
                        double abs_tol, int* iters, int* status, void* rho,
-                       bool pinv_diag, hipStream_t stream);
+                       bool pinv_diag, bool pinv_packed, hipStream_t stream);
 
 // Placement glass_pcg_batched_ex would choose (GLASS_PLACEMENT_*), or an error.
-int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag);
+// pinv_packed: Pinv given as packed D blocks (implies pinv_diag).
+int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
+                          bool pinv_packed);
 
 size_t bdsv_workspace_bytes(int ss, int kp, long long n_problems, glass_dtype dt);
 int launch_bdsv(glass_dtype dt, void* x, const void* S, const void* b, int ss,

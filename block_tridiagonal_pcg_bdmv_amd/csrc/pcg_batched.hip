@@ -44,6 +44,13 @@
 // that touch no row's D block are given an offset past the buffer's end, so
 // they read zeros and are not fetched (about 2/5 of the vectors remain at
 // ss=21).
+//
+// Pinv as packed D blocks ([kp*ss][ss] per problem, the same block-Jacobi
+// preconditioner stored without its zero blocks): resident lanes load their
+// ss values from row*ss, and streamed chunks are 64 rows of ss values,
+// multiplied with the middle third of the window.  The terms and their order
+// are those of the D-only rows above, so the results are the same; every
+// byte fetched is a D byte.
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -78,6 +85,8 @@ struct PcgArgs {
   T abs_tol;
   int vec;          // 16-byte staging allowed (alignment checked on the host)
   int stage_elems;  // per-wave LDS stage, elements
+  int ppacked;      // Pinv is packed D blocks, [kp*ss][ss] per problem (read
+                    // by kStream; the other modes fix it at compile time)
 };
 
 // Placements of the matrices (see the header).
@@ -87,6 +96,8 @@ enum Mode {
   kStream = 2,
   kResidentPD = 3,        // resident, Pinv's D blocks only
   kStreamPrefetchPD = 4,  // streamed with prefetch, Pinv vectors touching D only
+  kStreamPrefetchPDP = 5,  // streamed with prefetch, Pinv as packed D blocks
+  kResidentPDP = 6,        // resident, Pinv as packed D blocks
 };
 
 // Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for the
@@ -94,8 +105,9 @@ enum Mode {
 // lane; 16 waves otherwise (rows beyond 4096 need them, at the cost of
 // spills).
 constexpr int max_threads_for(int rpt, int mode) {
-  const bool resident = mode == kResident || mode == kResidentPD;
-  return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || rpt == 3 || rpt == 4 ||
+  const bool resident = mode == kResident || mode == kResidentPD || mode == kResidentPDP;
+  return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || mode == kStreamPrefetchPDP ||
+          rpt == 3 || rpt == 4 ||
           (resident && rpt > 1))
              ? 512
              : 1024;
@@ -104,9 +116,13 @@ constexpr int max_threads_for(int rpt, int mode) {
 template <typename T, int SS, int RPT, int MODE>
 __global__ void __launch_bounds__(max_threads_for(RPT, MODE))
 pcg_batched_kernel(PcgArgs<T> a) {
-  constexpr bool RES = MODE == kResident || MODE == kResidentPD;
-  constexpr bool PD = MODE == kResidentPD;  // Pinv rows: D part only
-  constexpr bool PFM = MODE == kStreamPrefetch || MODE == kStreamPrefetchPD;
+  constexpr bool RES = MODE == kResident || MODE == kResidentPD || MODE == kResidentPDP;
+  constexpr bool PD = MODE == kResidentPD || MODE == kResidentPDP;  // Pinv rows: D part only
+  constexpr bool PFM =
+      MODE == kStreamPrefetch || MODE == kStreamPrefetchPD || MODE == kStreamPrefetchPDP;
+  // Pinv chunks of packed D blocks in the prefetch ring (compile time, so the
+  // ring keeps one load pattern per position).
+  constexpr bool PFP = MODE == kStreamPrefetchPDP;
   constexpr int WC = SS > 0 ? 3 * SS : 1;  // compile-time width
   const int ss = SS > 0 ? SS : a.ss;
   const int W = 3 * ss;
@@ -121,8 +137,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const long long prob = blockIdx.x;
   const long long mstride = (long long)n * W;
+  // Pinv as packed D blocks: fixed by the mode, except for plain staging.
+  const bool packed = MODE == kResidentPDP || MODE == kStreamPrefetchPDP ||
+                      (MODE == kStream && a.ppacked != 0);
   const T* __restrict__ gS = a.S + prob * mstride;
-  const T* __restrict__ gP = a.P + prob * mstride;
+  const T* __restrict__ gP = a.P + prob * (packed ? (long long)n * ss : mstride);
   const bool vec = a.vec != 0;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -157,11 +176,20 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // offset register serves every load.  A chunk this wave does not have
   // (r0 >= n) becomes an empty resource: the loads return zeros.
   constexpr int NV = (WC * (int)sizeof(T) + 15) / 16;  // vectors per lane
-  auto load_chunk = [&](vec16_t (&buf)[NV], const T* __restrict__ gM, int k, bool dpart) {
+  // A chunk of packed D blocks (rows of ss elements) is NVD vectors per lane.
+  constexpr int NVD = ((SS > 0 ? SS : 1) * (int)sizeof(T) + 15) / 16;
+  auto load_chunk = [&](vec16_t (&buf)[NV], const T* __restrict__ gM, int k, bool dpart,
+                        bool dpacked) {
     const int r0 = chunk_r0(k);
     const bool has = r0 < n;
-    const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gM + (long long)r0 * W : gM, nbytes);
+    const int rw = dpacked ? ss : W;  // elements per row in gM
+    const int nbytes = has ? min(64, n - r0) * rw * (int)sizeof(T) : 0;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gM + (long long)r0 * rw : gM, nbytes);
+    if (dpacked) {
+#pragma unroll
+      for (int u = 0; u < NVD; ++u) buf[u] = buffer_load16(rs, (lane + u * kWave) * 16);
+      return;
+    }
     constexpr int RB = WC * (int)sizeof(T);                  // row bytes
     constexpr int D0 = (SS > 0 ? SS : 1) * (int)sizeof(T);  // D block bytes [D0, 2*D0)
 #pragma unroll
@@ -178,10 +206,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
   };
   // Write a loaded chunk into the wave's LDS stage (same layout as in HBM; the
   // stage holds NV*64 vectors, so every store is in bounds).
-  auto stage_chunk = [&](const vec16_t (&buf)[NV]) {
+  auto stage_chunk = [&](const vec16_t (&buf)[NV], bool dpacked) {
     vec16_t* __restrict__ d4 = reinterpret_cast<vec16_t*>(stage);
 #pragma unroll
-    for (int u = 0; u < NV; ++u) d4[lane + u * kWave] = buf[u];
+    for (int u = 0; u < NV; ++u)
+      if (!dpacked || u < NVD) d4[lane + u * kWave] = buf[u];
   };
 
   // RESIDENT: each lane's S and Pinv rows in registers for the whole solve,
@@ -199,7 +228,9 @@ pcg_batched_kernel(PcgArgs<T> a) {
         const long long off = (long long)row[k] * WC;
         // The D part starts ss elements into the row: at (3*row + 1) times
         // its own byte size, so the widths load_row_regs picks stay aligned.
-        const long long offP = off + (PD ? SS : 0);
+        // Packed D blocks: the row's ss values start at row * ss.
+        const long long offP =
+            MODE == kResidentPDP ? (long long)row[k] * SS : off + (PD ? SS : 0);
         if (vec) {
           load_row_regs<T, WC, true>(mS[k], gS + off);
           load_row_regs<T, WCP, true>(mP[k], gP + offP);
@@ -226,11 +257,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
       const int m = pos / RPT, k = pos % RPT;
       const T* gM = m == 0 ? gS : gP;
       const bool dpart = MODE == kStreamPrefetchPD && m == 1;
+      const bool dpacked = PFP && m == 1;
       if constexpr (kRingDepth == 1) {
-        load_chunk(pf0, gM, k, dpart);
+        load_chunk(pf0, gM, k, dpart, dpacked);
       } else {
-        if (pos % 2 == 0) load_chunk(pf0, gM, k, dpart);
-        else load_chunk(pf1, gM, k, dpart);
+        if (pos % 2 == 0) load_chunk(pf0, gM, k, dpart, dpacked);
+        else load_chunk(pf1, gM, k, dpart, dpacked);
       }
     }
   };
@@ -240,6 +272,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
   auto matvec = [&](auto mi_tag, T (&out)[RPT], auto& mreg, const T* __restrict__ vpad) {
     constexpr int MI = decltype(mi_tag)::value;
     const T* __restrict__ gM = MI == 0 ? gS : gP;
+    // Streamed Pinv as packed D blocks: rows of ss values, multiplied with
+    // the middle third of the window (the terms and order of a D-only row).
+    // Prefetching placements know it at compile time.
+    const bool mpacked = MI == 1 && (PFM ? PFP : packed);
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       T acc = T(0);
@@ -260,10 +296,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
           constexpr int pos = MI * RPT;  // + k, below
           if (r0 < n) {  // wave-uniform
             if constexpr (kRingDepth == 1) {
-              stage_chunk(pf0);
+              stage_chunk(pf0, mpacked);
             } else {
-              if ((pos + k) % 2 == 0) stage_chunk(pf0);
-              else stage_chunk(pf1);
+              if ((pos + k) % 2 == 0) stage_chunk(pf0, mpacked);
+              else stage_chunk(pf1, mpacked);
             }
           }
           // Keep the next loads after these LDS stores, so the emptied
@@ -277,10 +313,20 @@ pcg_batched_kernel(PcgArgs<T> a) {
         if (r0 < n) {  // wave-uniform
           if constexpr (!PFM) {
             const int nrows = min(64, n - r0);
-            copy_to_lds<false>(stage, gM + (long long)r0 * W, nrows * W, lane, kWave, vec);
+            const int rw = mpacked ? ss : W;
+            copy_to_lds<false>(stage, gM + (long long)r0 * rw, nrows * rw, lane, kWave, vec);
           }
           wave_lds_sync();
-          if (valid[k]) {
+          if (valid[k] && mpacked) {
+            const T* __restrict__ m = stage + lane * ss;
+            const T* __restrict__ w = vpad + wstart[k] + ss;
+            if constexpr (SS > 0) {
+#pragma unroll
+              for (int c = 0; c < SS; ++c) acc = fma(m[c], w[c], acc);
+            } else {
+              for (int c = 0; c < ss; ++c) acc = fma(m[c], w[c], acc);
+            }
+          } else if (valid[k]) {
             const T* __restrict__ m = stage + lane * W;
             const T* __restrict__ w = vpad + wstart[k];
             if constexpr (SS > 0) {
@@ -432,6 +478,7 @@ struct Plan {
   int RPT = 0;
   bool res = false;
   bool pd = false;  // Pinv's D blocks only (resident, or streamed with prefetch)
+  bool packed = false;  // Pinv given as packed D blocks
   bool res_auto = false;  // resident rows per lane left to the occupancy choice
   bool prefetch = false;
   int stage_elems = 0;
@@ -591,9 +638,9 @@ int launch_rpt(const PcgArgs<T>& a, int n_problems, const Plan& pl,
 // CUs takes two rows per lane instead of one when that kernel fits more
 // workgroups per CU (more problems in flight); a smaller batch keeps one row
 // per lane (the most waves per problem, the shortest solve).
-template <typename T, int SS, bool PD>
+template <typename T, int SS, bool PD, bool PACKED>
 int launch_res(const PcgArgs<T>& a, int n_problems, const Plan& pl_in, hipStream_t st) {
-  constexpr int M = PD ? kResidentPD : kResident;
+  constexpr int M = PACKED ? kResidentPDP : (PD ? kResidentPD : kResident);
   Plan pl = pl_in;
   if constexpr (kResidentRowsFit<T>(SS, 1, PD) && kResidentRowsFit<T>(SS, 2, PD)) {
     DeviceInfo dev;
@@ -636,38 +683,62 @@ int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
               hipStream_t st) {
   if constexpr (SS > 0) {
     if (pl.res) {
-      return pl.pd ? launch_res<T, SS, true>(a, n_problems, pl, st)
-                   : launch_res<T, SS, false>(a, n_problems, pl, st);
+      if (!pl.pd) return launch_res<T, SS, false, false>(a, n_problems, pl, st);
+      return pl.packed ? launch_res<T, SS, true, true>(a, n_problems, pl, st)
+                       : launch_res<T, SS, true, false>(a, n_problems, pl, st);
     }
   }
   if constexpr (SS > 0 && kPrefetchFits<T>(SS)) {
     if (pl.prefetch)
-      return pl.pd ? launch_rpt<T, SS, kStreamPrefetchPD>(a, n_problems, pl, st)
+      return pl.pd ? (pl.packed ? launch_rpt<T, SS, kStreamPrefetchPDP>(a, n_problems, pl, st)
+                                : launch_rpt<T, SS, kStreamPrefetchPD>(a, n_problems, pl, st))
                    : launch_rpt<T, SS, kStreamPrefetch>(a, n_problems, pl, st);
   }
   return launch_rpt<T, SS, kStream>(a, n_problems, pl, st);
 }
 
+// 16-byte vector paths: S and Pinv 16-byte aligned and every problem's
+// matrices starting on a 16-byte boundary.
+template <typename T>
+bool vector_ok(const void* S, const void* P, int ss, int kp, bool pinv_packed) {
+  const long long n = (long long)kp * ss, es = (long long)sizeof(T);
+  return aligned(S, 16) && aligned(P, 16) && (n * 3 * ss * es) % 16 == 0 &&
+         (!pinv_packed || (n * ss * es) % 16 == 0);
+}
+
+// The plan for a shape.  GLASS_AMD_PCG_STREAMED=1 replaces a resident plan
+// by a streamed one (tests and measurement); it keeps the D-block hint only
+// for packed D blocks, which the general streamed modes cannot read.  A
+// packed Pinv is only ever given to the D-block modes or kStream.
+template <typename T>
+bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, size_t lds_max,
+                 Plan* pl) {
+  const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
+  const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
+                        std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
+  pinv_diag = pinv_diag || pinv_packed;
+  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, lds_max, pl)) return false;
+  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl->res) {
+    Plan alt;
+    if (make_plan<T>(ss, kp, false, prefetch, pinv_packed, lds_max, &alt)) *pl = alt;
+  }
+  if (pinv_packed && !pl->pd && (pl->res || pl->prefetch)) return false;  // not reached
+  pl->packed = pinv_packed;
+  return true;
+}
+
 template <typename T>
 int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
                  int n_problems, int max_iters, double rel_tol, double abs_tol,
-                 int* iters, int* status, T* rho, bool pinv_diag, hipStream_t st) {
+                 int* iters, int* status, T* rho, bool pinv_diag, bool pinv_packed,
+                 hipStream_t st) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
-  const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
-  const long long n = (long long)kp * ss;
-  const bool vec = aligned(S, 16) && aligned(P, 16) &&
-                   ((n * 3 * ss * (long long)sizeof(T)) % 16 == 0);
-  const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
-                        std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
+  const bool vec = vector_ok<T>(S, P, ss, kp, pinv_packed);
   Plan pl;
-  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, dev.max_lds_per_block, &pl))
+  if (!choose_plan<T>(ss, kp, vec, pinv_diag, pinv_packed, dev.max_lds_per_block, &pl))
     return fail(GLASS_EUNSUPPORTED,
                 "pcg: problem too large for one workgroup (rows or LDS)");
-  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl.res) {
-    Plan alt;
-    if (make_plan<T>(ss, kp, false, prefetch, false, dev.max_lds_per_block, &alt)) pl = alt;
-  }
   PcgArgs<T> a;
   a.x = x;
   a.S = S;
@@ -683,6 +754,7 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.abs_tol = (T)abs_tol;
   a.vec = vec;
   a.stage_elems = pl.stage_elems;
+  a.ppacked = pinv_packed ? 1 : 0;
   switch (ss) {
     case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
     case 12: return launch_ss<T, 12>(a, n_problems, pl, st);
@@ -693,44 +765,41 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
 }
 
 template <typename T>
-int placement_typed(int ss, int kp, bool vec, bool pinv_diag) {
+int placement_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_packed) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
-  const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
-  const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
-                        std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
+  const long long n = (long long)kp * ss, es = (long long)sizeof(T);
+  const bool vec = aligned16 && (n * 3 * ss * es) % 16 == 0 &&
+                   (!pinv_packed || (n * ss * es) % 16 == 0);
   Plan pl;
-  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, dev.max_lds_per_block, &pl))
+  if (!choose_plan<T>(ss, kp, vec, pinv_diag, pinv_packed, dev.max_lds_per_block, &pl))
     return fail(GLASS_EUNSUPPORTED, "pcg: problem too large for one workgroup (rows or LDS)");
-  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl.res) {
-    Plan alt;
-    if (make_plan<T>(ss, kp, false, prefetch, false, dev.max_lds_per_block, &alt)) pl = alt;
-  }
   return pl.res ? GLASS_PLACEMENT_RESIDENT
                 : (pl.prefetch ? GLASS_PLACEMENT_STREAMED_PREFETCH : GLASS_PLACEMENT_STREAMED);
 }
 
 }  // namespace
 
-int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag) {
-  return dt == GLASS_F32 ? placement_typed<float>(ss, kp, aligned16, pinv_diag)
-                         : placement_typed<double>(ss, kp, aligned16, pinv_diag);
+int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
+                          bool pinv_packed) {
+  return dt == GLASS_F32 ? placement_typed<float>(ss, kp, aligned16, pinv_diag, pinv_packed)
+                         : placement_typed<double>(ss, kp, aligned16, pinv_diag, pinv_packed);
 }
 
 int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
                        const void* Pinv, const void* b, int ss, int kp,
                        int n_problems, int max_iters, double rel_tol,
                        double abs_tol, int* iters, int* status, void* rho,
-                       bool pinv_diag, hipStream_t stream) {
+                       bool pinv_diag, bool pinv_packed, hipStream_t stream) {
   if (dt == GLASS_F32)
     return launch_typed<float>((float*)x, (const float*)S, (const float*)Pinv,
                                (const float*)b, ss, kp, n_problems, max_iters,
                                rel_tol, abs_tol, iters, status, (float*)rho,
-                               pinv_diag, stream);
+                               pinv_diag, pinv_packed, stream);
   return launch_typed<double>((double*)x, (const double*)S,
                               (const double*)Pinv, (const double*)b, ss, kp,
                               n_problems, max_iters, rel_tol, abs_tol, iters,
-                              status, (double*)rho, pinv_diag, stream);
+                              status, (double*)rho, pinv_diag, pinv_packed, stream);
 }
 
 }  // namespace glass

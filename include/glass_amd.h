@@ -138,8 +138,16 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
  *     same as without the flag (the skipped terms are exact zeros, added in
  *     the same order); when it does not, the L and R blocks of Pinv may or
  *     may not be used.
+ *   GLASS_PCG_PINV_DIAGONAL_BLOCKS  Pinv holds only the D blocks, packed:
+ *     [n_problems][kp][ss][ss] row-major (row i of block-row br starts at
+ *     element (br*ss + i)*ss of its problem), kp*ss*ss elements per problem
+ *     instead of kp*ss*3ss.  The same block-Jacobi preconditioner as
+ *     GLASS_PCG_PINV_BLOCK_DIAGONAL (which it implies), with every placement
+ *     reading a third of Pinv's bytes.  The results are the same as for the
+ *     [L|D|R] layout with zero L and R blocks (the same terms in the same
+ *     order).  Pinv must be 16-byte aligned like S.
  * Other flag bits return GLASS_EINVAL. */
-enum { GLASS_PCG_PINV_BLOCK_DIAGONAL = 1u };
+enum { GLASS_PCG_PINV_BLOCK_DIAGONAL = 1u, GLASS_PCG_PINV_DIAGONAL_BLOCKS = 2u };
 int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
                          const void* b, int state_size, int knot_points,
                          int n_problems, int max_iters, double rel_tol,

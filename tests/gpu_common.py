@@ -51,15 +51,26 @@ def assert_bdmv_close(y_gpu, S, v, ss, kp, nthreads=8):
         bad.sum(), float((err / np.maximum(scale[:, ss:-ss], 1e-300)).max()))
 
 
-def pcg_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, x0=None, pinv_block_diagonal=False):
-    t = {k: to_dev(v) for k, v in inp.items() if k in ("S", "Pinv", "b")}
+def pack_diagonal_blocks(P, ss, kp):
+    """The D blocks of [L|D|R] Pinv strips, packed as [B, kp, ss, ss] (the
+    GLASS_PCG_PINV_DIAGONAL_BLOCKS layout); a copy, no arithmetic."""
+    B = P.shape[0]
+    return np.ascontiguousarray(P.reshape(B, kp, ss, 3 * ss)[:, :, :, ss:2 * ss])
+
+
+def pcg_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, x0=None, pinv_block_diagonal=False,
+            pinv_diagonal_blocks=False):
+    t = {k: to_dev(v) for k, v in inp.items() if k in ("S", "b")}
+    P = pack_diagonal_blocks(inp["Pinv"], ss, kp) if pinv_diagonal_blocks else inp["Pinv"]
+    t["Pinv"] = to_dev(P)
     B = inp["b"].shape[0]
     x = to_dev(inp["x0"] if x0 is None else x0).clone()
     iters = torch.full((B,), -1, dtype=torch.int32, device="cuda")
     status = torch.full((B,), -1, dtype=torch.int32, device="cuda")
     rho = torch.zeros((B, 2), dtype=x.dtype, device="cuda")
     glass.pcg_batched(x, t["S"], t["Pinv"], t["b"], ss, kp, max_iters, rel_tol,
-                      abs_tol, iters, status, rho, pinv_block_diagonal=pinv_block_diagonal)
+                      abs_tol, iters, status, rho, pinv_block_diagonal=pinv_block_diagonal,
+                      pinv_diagonal_blocks=pinv_diagonal_blocks)
     torch.cuda.synchronize()
     return x.cpu().numpy(), iters.cpu().numpy(), status.cpu().numpy(), rho.cpu().numpy()
 

@@ -134,13 +134,14 @@ def test_placement_query_argument_errors(lib):
     assert lib.glass_pcg_batched_placement(0, 32, 0, 1, 0) == EINVAL
     assert lib.glass_pcg_batched_placement(6, 32, 5, 1, 0) == EINVAL
     assert lib.glass_pcg_batched_placement(64, 200, 0, 1, 0) == EUNSUPPORTED
-    assert lib.glass_pcg_batched_placement(6, 32, 0, 1, 2) == EINVAL  # unknown flag
+    assert lib.glass_pcg_batched_placement(6, 32, 0, 1, 4) == EINVAL  # unknown flag
 
 
 def test_pcg_ex_flag_errors(lib):
     def ex(flags):
         return lib.glass_pcg_batched_ex(FAKE, FAKE, FAKE, FAKE, 6, 32, 1, 20, 1e-6, 0.0, FAKE,
                                         None, None, 0, flags, None)
-    assert ex(2) == EINVAL
+    assert ex(4) == EINVAL
     assert ex(0x80000000) == EINVAL
     assert ex(1 | 4) == EINVAL
+    assert ex(2 | 8) == EINVAL

@@ -310,6 +310,87 @@ def test_pcg_pinv_block_diagonal_streamed_prefetch(gpu, monkeypatch):
             np.testing.assert_array_equal(u, v)
 
 
+@pytest.mark.parametrize("ss,kp,B,dtype", [
+    (14, 32, 96, np.float32),   # resident (D blocks only)
+    (6, 32, 40, np.float32),
+    (12, 60, 9, np.float32),
+    (21, 40, 7, np.float32),    # 840 rows: resident with D blocks
+    (21, 64, 5, np.float32),    # streamed with prefetch
+    (6, 20, 9, np.float64),
+    (14, 32, 6, np.float64),    # plain streamed staging, specialised size
+    (9, 32, 5, np.float32),     # plain streamed staging, generic size, 16-byte paths
+    (9, 23, 5, np.float32),     # generic size, ragged last chunk, element paths
+])
+def test_pcg_pinv_packed_diagonal_blocks(gpu, ss, kp, B, dtype):
+    """GLASS_PCG_PINV_DIAGONAL_BLOCKS: Pinv passed as packed D blocks
+    [B, kp, ss, ss] gives the same bits as the [L|D|R] layout with zero L
+    and R blocks (the same terms in the same order) in every placement, and
+    meets the oracle; the placement query reports the hinted placement."""
+    rng = np.random.default_rng(ss * 1000 + kp)
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.2, dtype)
+    inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
+           "b": rng.standard_normal((B, kp * ss)).astype(dtype),
+           "x0": np.zeros((B, kp * ss), dtype)}
+    rel = 1e-6 if dtype == np.float32 else 1e-10
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    hinted = gpu.pcg_batched_placement(ss, kp, tdt, pinv_block_diagonal=True)
+    packed = gpu.pcg_batched_placement(ss, kp, tdt, pinv_diagonal_blocks=True)
+    assert packed == hinted
+    say("pcg Pinv packed D blocks ss=%d kp=%d B=%d %s placement %d"
+        % (ss, kp, B, np.dtype(dtype).name, packed))
+    ref = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0)
+    got = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0, pinv_diagonal_blocks=True)
+    for u, v in zip(ref, got):
+        np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, got, dtype)
+
+
+def test_pcg_pinv_packed_diagonal_blocks_workloads(gpu, monkeypatch):
+    """Packed D blocks on both full workloads (ss=14 resident, ss=21
+    streamed with prefetch) against the [L|D|R] runs, then the other
+    streamed forms: prefetch at 1, 2 and 4 rows per lane, and plain
+    staging."""
+    for cfg in (2, 3):
+        w = workloads.WORKLOADS[cfg]
+        inp = workloads.generate(w)
+        say("pcg cfg%d full with packed Pinv D blocks" % cfg)
+        ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+        got = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol,
+                      pinv_diagonal_blocks=True)
+        for u, v in zip(ref, got):
+            np.testing.assert_array_equal(u, v)
+        assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, got, np.float32)
+    w2 = workloads.WORKLOADS[2]
+    inp2 = workloads.generate(w2, n_problems=20)
+    ref2 = pcg_gpu(gpu, inp2, w2.ss, w2.kp, w2.max_iters, w2.rel_tol, w2.abs_tol)
+    monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
+    assert gpu.pcg_batched_placement(w2.ss, w2.kp, torch.float32, pinv_diagonal_blocks=True) \
+        == gpu.PLACEMENT_STREAMED_PREFETCH
+    for rpt in ("1", "2", "4"):
+        monkeypatch.setenv("GLASS_AMD_PCG_RPT", rpt)
+        say("pcg cfg2 streamed prefetch rows/lane=%s, packed Pinv D blocks" % rpt)
+        got = pcg_gpu(gpu, inp2, w2.ss, w2.kp, w2.max_iters, w2.rel_tol, w2.abs_tol,
+                      pinv_diagonal_blocks=True)
+        for u, v in zip(ref2, got):
+            np.testing.assert_array_equal(u, v)
+    monkeypatch.delenv("GLASS_AMD_PCG_RPT")
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_PREFETCH", "1")
+    assert gpu.pcg_batched_placement(w2.ss, w2.kp, torch.float32, pinv_diagonal_blocks=True) \
+        == gpu.PLACEMENT_STREAMED
+    w3 = workloads.WORKLOADS[3]
+    inp3 = workloads.generate(w3, n_problems=12)
+    for w, inp, ref in ((w2, inp2, ref2), (w3, inp3, None)):
+        say("pcg ss=%d plain streamed staging, packed Pinv D blocks" % w.ss)
+        if ref is None:
+            monkeypatch.delenv("GLASS_AMD_PCG_NO_PREFETCH")
+            ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+            monkeypatch.setenv("GLASS_AMD_PCG_NO_PREFETCH", "1")
+        got = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol,
+                      pinv_diagonal_blocks=True)
+        for u, v in zip(ref, got):
+            np.testing.assert_array_equal(u, v)
+
+
 @pytest.mark.parametrize("rpt", ["2", "3", "4"])
 def test_pcg_resident_rows_per_lane_bit_identical(gpu, monkeypatch, rpt):
     """Resident rows at 2, 3 and 4 rows per lane (GLASS_AMD_PCG_RES_RPT; for
