@@ -145,7 +145,8 @@ int glass_pcg_batched(void* x, const void* S, const void* Pinv, const void* b,
  *     GLASS_PCG_PINV_BLOCK_DIAGONAL (which it implies), with every placement
  *     reading a third of Pinv's bytes.  The results are the same as for the
  *     [L|D|R] layout with zero L and R blocks (the same terms in the same
- *     order).  Pinv must be 16-byte aligned like S.
+ *     order).  Alignment as for S: the element size, 16 bytes for the
+ *     vector paths.
  * Other flag bits return GLASS_EINVAL. */
 enum { GLASS_PCG_PINV_BLOCK_DIAGONAL = 1u, GLASS_PCG_PINV_DIAGONAL_BLOCKS = 2u };
 int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,

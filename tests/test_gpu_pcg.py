@@ -9,7 +9,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_common import assert_pcg_parity, pcg_gpu, say
+from gpu_common import assert_pcg_parity, pack_diagonal_blocks, pcg_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -343,6 +343,35 @@ def test_pcg_pinv_packed_diagonal_blocks(gpu, ss, kp, B, dtype):
     for u, v in zip(ref, got):
         np.testing.assert_array_equal(u, v)
     assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, got, dtype)
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_pcg_pinv_packed_element_aligned_pointer(gpu, cfg):
+    """Packed D blocks at an address aligned to the element size only: the
+    element-load paths (the 16-byte ones need 16-byte alignment) give the
+    same bits as the aligned call."""
+    w = workloads.WORKLOADS[cfg]
+    inp = workloads.generate(w, n_problems=24)
+    B = inp["b"].shape[0]
+    packed = pack_diagonal_blocks(inp["Pinv"], w.ss, w.kp)
+    ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol,
+                  pinv_diagonal_blocks=True)
+    store = torch.zeros(packed.size + 1, dtype=torch.float32, device="cuda")
+    P = store[1:]
+    P.copy_(torch.from_numpy(packed.reshape(-1)))
+    assert P.data_ptr() % 16 == 4
+    x = torch.from_numpy(inp["x0"]).cuda()
+    it = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    st = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    rho = torch.zeros((B, 2), dtype=torch.float32, device="cuda")
+    say("pcg cfg%d packed Pinv at a 4-byte-aligned address" % cfg)
+    gpu.pcg_batched(x, torch.from_numpy(inp["S"]).cuda(), P, torch.from_numpy(inp["b"]).cuda(),
+                    w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, it, st, rho,
+                    pinv_diagonal_blocks=True)
+    torch.cuda.synchronize()
+    got = (x.cpu().numpy(), it.cpu().numpy(), st.cpu().numpy(), rho.cpu().numpy())
+    for u, v in zip(ref, got):
+        np.testing.assert_array_equal(u, v)
 
 
 def test_pcg_pinv_packed_diagonal_blocks_workloads(gpu, monkeypatch):
