@@ -231,6 +231,7 @@ def test_empty_batches_are_no_ops(gpu):
     z = torch.zeros(0, dtype=torch.float32, device="cuda")
     zi = torch.zeros(0, dtype=torch.int32, device="cuda")
     gpu.pcg_batched(z, z, z, z, 6, 32, 10, 1e-6, 0.0, zi)
+    gpu.pcg_batched(z, z, z, z, 6, 32, 10, 1e-6, 0.0, zi, pinv_diagonal_blocks=True)
     gpu.bdsv_batched(z, z, z, 6, 32, zi)
     torch.cuda.synchronize()
 
@@ -320,6 +321,8 @@ def test_pcg_pinv_block_diagonal_streamed_prefetch(gpu, monkeypatch):
     (14, 32, 6, np.float64),    # plain streamed staging, specialised size
     (9, 32, 5, np.float32),     # plain streamed staging, generic size, 16-byte paths
     (9, 23, 5, np.float32),     # generic size, ragged last chunk, element paths
+    (14, 1, 3, np.float32),     # one block-row (Pinv is exactly inv(S))
+    (21, 2, 4, np.float32),     # two block-rows
 ])
 def test_pcg_pinv_packed_diagonal_blocks(gpu, ss, kp, B, dtype):
     """GLASS_PCG_PINV_DIAGONAL_BLOCKS: Pinv passed as packed D blocks
