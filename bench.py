@@ -58,10 +58,11 @@ KERNEL_OF = {
     "pcg0": "pcg_batched_kernel<float, 6, 1, 0>",
     "bdmv1": "bdmv_kernel<float, 14>",
     "pcg2": "pcg_batched_kernel<float, 14, 1, 0>",
-    "pcg3": "pcg_batched_kernel<float, 21, 3, 1>",
+    "pcg3": "pcg_batched_kernel<float, 21, 3, 7>",
+    "pcg3_stream": "pcg_batched_kernel<float, 21, 3, 1>",
     "grid4": "pcg_grid_kernel<double, 12,",
     "bdsv2": "bdsv_rows_kernel<float, 14,",
-    "pcg2_f64": "pcg_batched_kernel<double, 14, 1, 2>",
+    "pcg2_f64": "pcg_batched_kernel<double, 14, 1, 7>",
     "grid4_f32": "pcg_grid_kernel<float, 12,",
     "pcg2_pd": "pcg_batched_kernel<float, 14, 2, 3>",
     "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 4>",
@@ -73,7 +74,7 @@ KERNEL_OF = {
 # Workload inputs: the five configurations; bdsv2 is the direct solve of the
 # same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
 # are the precision variants of pcg2 and grid4 (same recipe and seeds).
-CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "grid4": 4, "bdsv2": 2,
+CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "pcg3_stream": 3, "grid4": 4, "bdsv2": 2,
              "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3, "pcg2_pdp": 2,
              "pcg3_pdp": 3, "grid4_sr": 4, "grid4_f32_sr": 4}
 # Workloads run with GLASS_PCG_PINV_BLOCK_DIAGONAL (their Pinv is block-Jacobi,
@@ -83,6 +84,10 @@ PINV_DIAG = {"pcg2_pd", "pcg3_pd"}
 # Workloads run with GLASS_PCG_PINV_DIAGONAL_BLOCKS: the same systems with
 # Pinv passed as its packed D blocks [B, kp, ss, ss].
 PINV_PACKED = {"pcg2_pdp", "pcg3_pdp"}
+# Workloads run with the S-resident placement switched off
+# (GLASS_AMD_PCG_NO_HYBRID=1): pcg3_stream is the ss=21 workload with S and
+# Pinv both streamed, the placement the S-resident one replaced.
+NO_HYBRID = {"pcg3_stream"}
 # Grid workloads run in the single-reduction form (GLASS_GRID_SINGLE_REDUCTION).
 SINGLE_RED = {"grid4_sr", "grid4_f32_sr"}
 VARIANT_OF = {
@@ -91,6 +96,7 @@ VARIANT_OF = {
                          rel_tol=1e-7),
     "pcg2_pd": dict(name="pcg_ss14_kp32_b4096_f32_pinv_blockdiag"),
     "pcg3_pd": dict(name="pcg_ss21_kp64_b2048_f32_pinv_blockdiag"),
+    "pcg3_stream": dict(name="pcg_ss21_kp64_b2048_f32_streamed"),
     "pcg2_pdp": dict(name="pcg_ss14_kp32_b4096_f32_pinv_diagonal_blocks"),
     "pcg3_pdp": dict(name="pcg_ss21_kp64_b2048_f32_pinv_diagonal_blocks"),
     "pcg2_f64": dict(name="pcg_ss14_kp32_b4096_f64", dtype=np.float64),
@@ -118,17 +124,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes_pcg(w, iters: np.ndarray, resident: bool, pinv_diag=False) -> float:
+def algorithmic_bytes_pcg(w, iters: np.ndarray, resident, pinv_diag=False) -> float:
     """Bytes one solve must move between HBM and the chip, by the algorithm:
     S and Pinv (n*3ss each; Pinv n*ss when only its D blocks are read) once
     if they stay on chip, else once per pass (the initial S x0 / Pinv r pass
     plus one per iteration); x read, b read, x written (n each); iters
-    (4 bytes)."""
+    (4 bytes).  resident: True (both on chip), False (both streamed) or "S"
+    (S on chip, Pinv streamed)."""
     es = np.dtype(w.dtype).itemsize
-    mat = (w.n * 3 * w.ss + w.n * (w.ss if pinv_diag else 3 * w.ss)) * es
+    s_bytes = w.n * 3 * w.ss * es
+    p_bytes = w.n * (w.ss if pinv_diag else 3 * w.ss) * es
     vec = 3 * w.n * es + 4
-    passes = np.ones_like(iters, dtype=np.float64) if resident else (iters.astype(np.float64) + 1)
-    return float(np.sum(passes * mat + vec))
+    passes = iters.astype(np.float64) + 1
+    if resident == "S":
+        return float(np.sum(s_bytes + passes * p_bytes + vec))
+    if resident:
+        passes = np.ones_like(passes)
+    return float(np.sum(passes * (s_bytes + p_bytes) + vec))
 
 
 def algorithmic_bytes_bdmv(w, B: int) -> float:
@@ -347,6 +359,10 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     # only user of the device); the cooperative launch is timed after it.
     pd = key in PINV_DIAG
     single = key in SINGLE_RED
+    if key in NO_HYBRID:
+        os.environ["GLASS_AMD_PCG_NO_HYBRID"] = "1"
+    else:
+        os.environ.pop("GLASS_AMD_PCG_NO_HYBRID", None)
 
     def run(x, exclusive=True):
         if grid:
@@ -372,9 +388,10 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     avg_ms = float(np.mean(launch_ms))
     # S and Pinv count once if they stay on chip (the grid solve and the
     # batched resident placement), else once per pass.
-    resident = grid or glass.pcg_batched_placement(
-        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd,
-        pinv_diagonal_blocks=packed) == glass.PLACEMENT_RESIDENT
+    placement = None if grid else glass.pcg_batched_placement(
+        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
+    resident = grid or placement == glass.PLACEMENT_RESIDENT or (
+        "S" if placement == glass.PLACEMENT_S_RESIDENT else False)
     nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed)
     for k in range(min(10, len(xs))):
         xs[k].zero_()
@@ -582,8 +599,10 @@ def main():
         else:
             # the headline workload gets the larger CPU budget (10 s)
             budget = max(args.cpu_budget, 10.0) if name == "pcg3" else args.cpu_budget
+            # pcg3_stream runs pcg3's inputs in another placement: no second
+            # CPU baseline
             res[name] = bench_pcg(torch, glass, name, args.steps, args.warmup, budget,
-                                  with_cpu, traffic)
+                                  with_cpu and name not in NO_HYBRID, traffic)
         print("[bench] %s done: %s" % (name, json.dumps(res[name])[:300]), file=sys.stderr,
               flush=True)
     if args.calibration_copy:

@@ -23,7 +23,7 @@ __all__ = [
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
     "PCG_PINV_BLOCK_DIAGONAL", "PCG_PINV_DIAGONAL_BLOCKS", "GRID_SINGLE_REDUCTION",
     "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
-    "PLACEMENT_STREAMED",
+    "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -203,14 +203,15 @@ def bdsv_batched(x, S, b, state_size: int, knot_points: int, status_out=None,
     _check(rc, "glass_bdsv_batched")
 
 
-PLACEMENT_RESIDENT, PLACEMENT_STREAMED_PREFETCH, PLACEMENT_STREAMED = 0, 1, 2
+PLACEMENT_RESIDENT, PLACEMENT_STREAMED_PREFETCH, PLACEMENT_STREAMED, PLACEMENT_S_RESIDENT = 0, 1, 2, 3
 
 
 def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=True,
                           pinv_block_diagonal=False, pinv_diagonal_blocks=False) -> int:
     """Where pcg_batched keeps S and Pinv on the current device for this shape:
-    PLACEMENT_RESIDENT (read once per solve) or PLACEMENT_STREAMED[_PREFETCH]
-    (read once per matvec pass).  Raises for shapes the solve rejects."""
+    PLACEMENT_RESIDENT (read once per solve), PLACEMENT_STREAMED[_PREFETCH]
+    (read once per matvec pass) or PLACEMENT_S_RESIDENT (S read once, Pinv once
+    per pass).  Raises for shapes the solve rejects."""
     import torch
     code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
     rc = load().glass_pcg_batched_placement(int(state_size), int(knot_points), code,

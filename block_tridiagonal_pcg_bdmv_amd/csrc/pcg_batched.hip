@@ -98,6 +98,7 @@ enum Mode {
   kStreamPrefetchPD = 4,  // streamed with prefetch, Pinv vectors touching D only
   kStreamPrefetchPDP = 5,  // streamed with prefetch, Pinv as packed D blocks
   kResidentPDP = 6,        // resident, Pinv as packed D blocks
+  kHybrid = 7,             // S resident, Pinv streamed by direct loads into LDS
 };
 
 // Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for the
@@ -107,7 +108,7 @@ enum Mode {
 constexpr int max_threads_for(int rpt, int mode) {
   const bool resident = mode == kResident || mode == kResidentPD || mode == kResidentPDP;
   return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || mode == kStreamPrefetchPDP ||
-          rpt == 3 || rpt == 4 ||
+          mode == kHybrid || rpt == 3 || rpt == 4 ||
           (resident && rpt > 1))
              ? 512
              : 1024;
@@ -120,6 +121,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
   constexpr bool PD = MODE == kResidentPD || MODE == kResidentPDP;  // Pinv rows: D part only
   constexpr bool PFM =
       MODE == kStreamPrefetch || MODE == kStreamPrefetchPD || MODE == kStreamPrefetchPDP;
+  // HYBRID: S rows resident in registers, Pinv chunks streamed into the
+  // wave's LDS stage by direct buffer -> LDS loads.
+  constexpr bool HYB = MODE == kHybrid;
+  constexpr bool SRES = RES || HYB;  // S rows held in registers
   // Pinv chunks of packed D blocks in the prefetch ring (compile time, so the
   // ring keeps one load pattern per position).
   constexpr bool PFP = MODE == kStreamPrefetchPDP;
@@ -216,14 +221,16 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // RESIDENT: each lane's S and Pinv rows in registers for the whole solve,
   // loaded straight from HBM with every load of both rows in flight.
   constexpr int WCP = PD ? (SS > 0 ? SS : 1) : WC;  // Pinv row width held
-  T mS[RES ? RPT : 1][WC], mP[RES ? RPT : 1][WCP];
-  if constexpr (RES) {
+  T mS[SRES ? RPT : 1][WC], mP[RES ? RPT : 1][WCP];
+  if constexpr (SRES) {
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
 #pragma unroll
       for (int c = 0; c < WC; ++c) mS[k][c] = T(0);
+      if constexpr (RES) {
 #pragma unroll
-      for (int c = 0; c < WCP; ++c) mP[k][c] = T(0);
+        for (int c = 0; c < WCP; ++c) mP[k][c] = T(0);
+      }
       if (valid[k]) {
         const long long off = (long long)row[k] * WC;
         // The D part starts ss elements into the row: at (3*row + 1) times
@@ -233,14 +240,50 @@ pcg_batched_kernel(PcgArgs<T> a) {
             MODE == kResidentPDP ? (long long)row[k] * SS : off + (PD ? SS : 0);
         if (vec) {
           load_row_regs<T, WC, true>(mS[k], gS + off);
-          load_row_regs<T, WCP, true>(mP[k], gP + offP);
+          if constexpr (RES) load_row_regs<T, WCP, true>(mP[k], gP + offP);
         } else {
           load_row_regs<T, WC, false>(mS[k], gS + off);
-          load_row_regs<T, WCP, false>(mP[k], gP + offP);
+          if constexpr (RES) load_row_regs<T, WCP, false>(mP[k], gP + offP);
         }
       }
     }
   }
+
+  // HYBRID: Pinv chunk k of this wave, loaded straight into the wave's LDS
+  // stage in the coalesced order (lane l's 16-byte vectors l, l+64, ...
+  // land at the same offsets as in memory, so the stage has the chunk's
+  // layout).  The resource spans exactly the chunk; vectors past its end, or
+  // every vector of a chunk the wave does not have, write zeros without a
+  // fetch.  The loads use no registers once issued, so the next chunk is in
+  // flight while the wave multiplies, reduces and waits at barriers.
+  auto dma_chunk = [&](int k) {
+    if constexpr (HYB) {
+      const int r0 = chunk_r0(k);
+      const bool has = r0 < n;
+      const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gP + (long long)r0 * W : gP, nbytes);
+      unsigned char* st = reinterpret_cast<unsigned char*>(stage);
+#pragma unroll
+      for (int u = 0; u < NV; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
+            (lane + u * kWave) * 16, 0, 0, 0);
+    }
+  };
+
+  // Workgroup barrier.  HYBRID orders LDS only: a release fence would also
+  // wait for the wave's direct loads in flight, which only the wave itself
+  // reads (after its own vmcnt wait), and global memory is not shared
+  // between the waves before the final stores.
+  auto block_sync = [&]() {
+    if constexpr (HYB) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    } else {
+      __syncthreads();
+    }
+  };
 
   // PREFETCH: a two-deep ring of chunk buffers.  The wave walks the fixed
   // sequence of positions pos = m*RPT + k (m = 0 for S, 1 for Pinv; matvecs
@@ -276,10 +319,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
     // the middle third of the window (the terms and order of a D-only row).
     // Prefetching placements know it at compile time.
     const bool mpacked = MI == 1 && (PFM ? PFP : packed);
+    constexpr bool REG = MI == 0 ? SRES : RES;  // this matrix's rows in registers
 #pragma unroll
     for (int k = 0; k < RPT; ++k) {
       T acc = T(0);
-      if constexpr (RES) {
+      if constexpr (REG) {
         if (valid[k]) {
           const T* __restrict__ w = vpad + wstart[k];
           if constexpr (PD && MI == 1) {
@@ -290,6 +334,25 @@ pcg_batched_kernel(PcgArgs<T> a) {
             for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], w[c], acc);
           }
         }
+      } else if constexpr (HYB) {
+        // Pinv chunk k is in, or on its way to, the stage.  Wait for this
+        // wave's direct loads, multiply, and once every stage read has
+        // returned, load the next chunk of the sequence (chunk 0 of the next
+        // matvec after the last) into the stage.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (chunk_r0(k) < n) {  // wave-uniform
+          if (valid[k]) {
+            const T* __restrict__ m = stage + lane * W;
+            const T* __restrict__ w = vpad + wstart[k];
+#pragma unroll 3
+            for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
+#pragma unroll
+              for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], w[c], acc);
+            }
+          }
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        }
+        dma_chunk((k + 1) % RPT);
       } else {
         const int r0 = chunk_r0(k);
         if constexpr (PFM) {
@@ -364,7 +427,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
         if (lane == 0) slots[wave + k * NW] = c;
       }
     }
-    __syncthreads();
+    block_sync();
     T s = slots[0];
     for (int c = 1; c < nchunks; ++c) s = s + slots[c];
     return s;
@@ -387,6 +450,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     ring_load(0);
     if (kRingDepth == 2) ring_load(1 % (2 * RPT));
   }
+  dma_chunk(0);
 #pragma unroll
   for (int k = 0; k < RPT; ++k)
     if (valid[k]) p_pad[ss + row[k]] = xr[k];
@@ -396,7 +460,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     r_pad[e] = T(0);
     r_pad[(kp + 1) * ss + e] = T(0);
   }
-  __syncthreads();
+  block_sync();
 
   T sv[RPT];
   matvec(MatS{}, sv, mS, p_pad);  // S x0
@@ -405,7 +469,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     rr[k] = valid[k] ? tmp[k] - sv[k] : T(0);
     if (valid[k]) r_pad[ss + row[k]] = rr[k];
   }
-  __syncthreads();
+  block_sync();
   matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
@@ -437,7 +501,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
         if (valid[k]) r_pad[ss + row[k]] = rr[k];
       }
       iters = it + 1;
-      __syncthreads();
+      block_sync();
       matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
       const T rz = chunk_dot(rr, sv, slotA);
       rho_last = rz;
@@ -452,13 +516,16 @@ pcg_batched_kernel(PcgArgs<T> a) {
         if (valid[k]) p_pad[ss + row[k]] = pr[k];
       }
       rho = rz;
-      __syncthreads();
+      block_sync();
     }
   }
 
 #pragma unroll
   for (int k = 0; k < RPT; ++k)
     if (valid[k]) a.x[prob * n + row[k]] = xr[k];
+  // The last matvec started a load of the next chunk into the stage: let it
+  // land before the workgroup's LDS can pass to another workgroup.
+  if constexpr (HYB) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tid == 0) {
     if (a.iters) a.iters[prob] = iters;
     if (a.status) a.status[prob] = status;
@@ -481,6 +548,7 @@ struct Plan {
   bool packed = false;  // Pinv given as packed D blocks
   bool res_auto = false;  // resident rows per lane left to the occupancy choice
   bool prefetch = false;
+  bool hyb = false;  // S resident, Pinv streamed by direct loads into LDS
   int stage_elems = 0;
   size_t lds = 0;
 };
@@ -512,6 +580,18 @@ constexpr bool kResidentRowsFit(int ss, int rpt, bool pd) {
   return rpt * (pd ? 4 : 6) * ss * (int)sizeof(T) / 4 <= (rpt == 1 ? 96 : 176);
 }
 
+// HYBRID placement: built for the specialised sizes whose S and Pinv rows do
+// not fit the one-row resident budget together; rpt rows of S alone within
+// 192 registers (workgroups of at most 8 waves).
+template <typename T>
+constexpr bool kHybridSize(int ss) {
+  return !kResidentFits<T>(ss);
+}
+template <typename T>
+constexpr bool kHybridRowsFit(int ss, int rpt) {
+  return kHybridSize<T>(ss) && rpt >= 1 && rpt <= 3 && rpt * 3 * ss * (int)sizeof(T) / 4 <= 192;
+}
+
 // Streamed with prefetch: specialised sizes whose 64-row chunk is at most 16
 // 16-byte vectors per lane.
 template <typename T>
@@ -531,7 +611,7 @@ int prefetch_stage_elems(int ss) {
 // prefetching streamed placement is allowed (specialised, 16-byte aligned).
 template <typename T>
 bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag,
-               size_t lds_max, Plan* plan) {
+               bool hybrid, size_t lds_max, Plan* plan) {
   const int n = kp * ss;
   const int W = 3 * ss;
   const int nchunks = (n + 63) / 64;
@@ -554,6 +634,26 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
     p.stage_elems = 0;
     p.lds = lds_bytes<T>(ss, kp, p.NW, 0);
     if (p.lds <= lds_max) {
+      *plan = p;
+      return true;
+    }
+  }
+  // HYBRID (general Pinv, 16-byte aligned, specialised size): the fewest
+  // rows per lane whose workgroup and LDS stages fit.
+  if (hybrid && !pinv_diag) {
+    for (int rpt = 1; rpt <= 3; ++rpt) {
+      if (rpt * 3 * ss * (int)sizeof(T) / 4 > 192) break;
+      const int NW = (nchunks + rpt - 1) / rpt;
+      if (NW * 64 > max_threads_for(rpt, kHybrid)) continue;
+      const int stage = prefetch_stage_elems<T>(ss);
+      const size_t lds = lds_bytes<T>(ss, kp, NW, stage);
+      if (lds > lds_max) continue;
+      Plan p;
+      p.NW = NW;
+      p.RPT = rpt;
+      p.hyb = true;
+      p.stage_elems = stage;
+      p.lds = lds;
       *plan = p;
       return true;
     }
@@ -679,9 +779,28 @@ int launch_res(const PcgArgs<T>& a, int n_problems, const Plan& pl_in, hipStream
 }
 
 template <typename T, int SS>
+int launch_hyb(const PcgArgs<T>& a, int n_problems, const Plan& pl, hipStream_t st) {
+  switch (pl.RPT) {
+    case 1:
+      if constexpr (kHybridRowsFit<T>(SS, 1)) return launch_one<T, SS, 1, kHybrid>(a, n_problems, pl, st);
+      break;
+    case 2:
+      if constexpr (kHybridRowsFit<T>(SS, 2)) return launch_one<T, SS, 2, kHybrid>(a, n_problems, pl, st);
+      break;
+    case 3:
+      if constexpr (kHybridRowsFit<T>(SS, 3)) return launch_one<T, SS, 3, kHybrid>(a, n_problems, pl, st);
+      break;
+    default:
+      break;
+  }
+  return fail(GLASS_EUNSUPPORTED, "pcg: internal plan error (hybrid rows per lane)");
+}
+
+template <typename T, int SS>
 int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
               hipStream_t st) {
   if constexpr (SS > 0) {
+    if (pl.hyb) return launch_hyb<T, SS>(a, n_problems, pl, st);
     if (pl.res) {
       if (!pl.pd) return launch_res<T, SS, false, false>(a, n_problems, pl, st);
       return pl.packed ? launch_res<T, SS, true, true>(a, n_problems, pl, st)
@@ -716,11 +835,13 @@ bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, siz
   const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
   const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
                         std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
+  const bool hybrid = specialised && vec && kHybridSize<T>(ss) &&
+                      std::getenv("GLASS_AMD_PCG_NO_HYBRID") == nullptr;
   pinv_diag = pinv_diag || pinv_packed;
-  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, lds_max, pl)) return false;
-  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && pl->res) {
+  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, hybrid, lds_max, pl)) return false;
+  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && (pl->res || pl->hyb)) {
     Plan alt;
-    if (make_plan<T>(ss, kp, false, prefetch, pinv_packed, lds_max, &alt)) *pl = alt;
+    if (make_plan<T>(ss, kp, false, prefetch, pinv_packed, false, lds_max, &alt)) *pl = alt;
   }
   if (pinv_packed && !pl->pd && (pl->res || pl->prefetch)) return false;  // not reached
   pl->packed = pinv_packed;
@@ -774,6 +895,7 @@ int placement_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_pa
   Plan pl;
   if (!choose_plan<T>(ss, kp, vec, pinv_diag, pinv_packed, dev.max_lds_per_block, &pl))
     return fail(GLASS_EUNSUPPORTED, "pcg: problem too large for one workgroup (rows or LDS)");
+  if (pl.hyb) return GLASS_PLACEMENT_S_RESIDENT;
   return pl.res ? GLASS_PLACEMENT_RESIDENT
                 : (pl.prefetch ? GLASS_PLACEMENT_STREAMED_PREFETCH : GLASS_PLACEMENT_STREAMED);
 }

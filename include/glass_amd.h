@@ -158,15 +158,18 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
 
 /* Where glass_pcg_batched_ex keeps S and Pinv for a problem shape and flags
  * on the current device: GLASS_PLACEMENT_RESIDENT (each lane's rows in
- * registers, read from HBM once per solve) or
+ * registers, read from HBM once per solve),
  * GLASS_PLACEMENT_STREAMED[_PREFETCH] (re-read from memory for every
- * matvec).  aligned16: whether S and Pinv will be 16-byte aligned.  flags:
+ * matvec) or GLASS_PLACEMENT_S_RESIDENT (S's rows in registers, read once;
+ * Pinv re-read for every matvec through the LDS, 16-byte aligned matrices
+ * only).  Every placement gives the same bits.  aligned16: whether S and Pinv will be 16-byte aligned.  flags:
  * as glass_pcg_batched_ex (0 for glass_pcg_batched).  Returns a negative
  * GLASS_E* code for shapes the solve rejects.  Enqueues nothing. */
 enum {
   GLASS_PLACEMENT_RESIDENT = 0,
   GLASS_PLACEMENT_STREAMED_PREFETCH = 1,
-  GLASS_PLACEMENT_STREAMED = 2
+  GLASS_PLACEMENT_STREAMED = 2,
+  GLASS_PLACEMENT_S_RESIDENT = 3
 };
 int glass_pcg_batched_placement(int state_size, int knot_points,
                                 glass_dtype dtype, int aligned16, unsigned flags);

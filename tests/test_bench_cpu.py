@@ -68,7 +68,7 @@ def _counter_csv(path, counter, rows):
 
 def test_summarize_pmc_calibrates_and_reads_back(tmp_path):
     neg = "void at::native::neg_kernel_cuda(...)"
-    pcg3 = "void glass::pcg_batched_kernel<float, 21, 3, 1>(glass::PcgArgs<float>)"
+    pcg3 = "void glass::pcg_batched_kernel<float, 21, 3, 7>(glass::PcgArgs<float>)"
     # Counter instances of one dispatch are summed (two rows for dispatch 2).
     _counter_csv(tmp_path / "f.csv", "FETCH_SIZE",
                  [(1, neg, 524288.0), (2, pcg3, 1000.0), (2, pcg3, 24.0), (3, pcg3, 1024.0)])

@@ -173,6 +173,7 @@ def test_pcg_prefetch_ring_matches_plain_staging(gpu, monkeypatch):
     w = workloads.WORKLOADS[3]
     inp = workloads.generate(w, n_problems=10)
     say("pcg cfg3 prefetch vs plain staging")
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
     a = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
     monkeypatch.setenv("GLASS_AMD_PCG_NO_PREFETCH", "1")
     b = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
@@ -181,14 +182,22 @@ def test_pcg_prefetch_ring_matches_plain_staging(gpu, monkeypatch):
 
 
 def test_pcg_placement_query_matches_the_workloads(gpu, monkeypatch):
-    """S and Pinv stay in registers for the ss=6 and ss=14 fp32 workloads and
-    stream (with prefetch) for ss=21 kp=64; forcing streaming is reported."""
+    """S and Pinv stay in registers for the ss=6 and ss=14 fp32 workloads; for
+    ss=21 kp=64 S stays in registers and Pinv streams (with prefetch when the
+    S-resident placement is switched off); forcing streaming is reported."""
     assert gpu.pcg_batched_placement(6, 32, torch.float32) == gpu.PLACEMENT_RESIDENT
     assert gpu.pcg_batched_placement(14, 32, torch.float32) == gpu.PLACEMENT_RESIDENT
-    assert gpu.pcg_batched_placement(21, 64, torch.float32) == gpu.PLACEMENT_STREAMED_PREFETCH
+    assert gpu.pcg_batched_placement(21, 64, torch.float32) == gpu.PLACEMENT_S_RESIDENT
+    assert gpu.pcg_batched_placement(14, 32, torch.float64) == gpu.PLACEMENT_S_RESIDENT
     assert gpu.pcg_batched_placement(21, 64, torch.float32, aligned16=False) == \
         gpu.PLACEMENT_STREAMED
+    assert gpu.pcg_batched_placement(21, 64, torch.float32, pinv_block_diagonal=True) == \
+        gpu.PLACEMENT_STREAMED_PREFETCH
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
+    assert gpu.pcg_batched_placement(21, 64, torch.float32) == gpu.PLACEMENT_STREAMED_PREFETCH
+    monkeypatch.delenv("GLASS_AMD_PCG_NO_HYBRID")
     monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
+    assert gpu.pcg_batched_placement(21, 64, torch.float32) == gpu.PLACEMENT_STREAMED_PREFETCH
     assert gpu.pcg_batched_placement(14, 32, torch.float32) != gpu.PLACEMENT_RESIDENT
     with pytest.raises(gpu.GlassError):
         gpu.pcg_batched_placement(64, 200, torch.float32)
@@ -451,3 +460,47 @@ def test_pcg_resident_rows_per_lane_bit_identical(gpu, monkeypatch, rpt):
         got2 = pcg_gpu(gpu, inp2, w2.ss, w2.kp, w2.max_iters, w2.rel_tol, w2.abs_tol)
         for u, v in zip(ref2, got2):
             np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("ss,kp,B,dtype", [
+    (21, 64, None, np.float32),   # the ss=21 workload, all 2048 problems
+    (21, 20, 3, np.float32),      # 7 chunks: one row per lane, 7 waves
+    (21, 40, 5, np.float32),      # 14 chunks: two rows per lane
+    (21, 60, 4, np.float32),      # 20 chunks, the last one ragged (1260 rows)
+    (21, 4, 2, np.float32),       # two chunks, the second ragged (84 rows)
+    (14, 32, 40, np.float64),     # the ss=14 workload in float64
+    (12, 70, 3, np.float64),      # 14 chunks, ragged, two rows per lane
+])
+def test_pcg_s_resident_matches_streamed(gpu, monkeypatch, ss, kp, B, dtype):
+    """S-resident placement (S rows in registers, Pinv chunks loaded straight
+    into the LDS stage): the same terms in the same order as the streamed
+    placements, so bit-identical outputs, and the oracle bars on every
+    problem.  (The placement needs every problem's matrices on a 16-byte
+    boundary: kp*ss a multiple of 4 in float32.)"""
+    if ss == 21 and kp == 64:
+        w = workloads.WORKLOADS[3]
+        inp = workloads.generate(w)
+        max_iters, rel, abs_tol = w.max_iters, w.rel_tol, w.abs_tol
+    elif ss == 14 and kp == 32:
+        w = workloads.WORKLOADS[2]
+        inp = {k: v.astype(dtype) for k, v in workloads.generate(w, n_problems=B).items()}
+        max_iters, rel, abs_tol = w.max_iters, w.rel_tol, w.abs_tol
+    else:
+        rng = np.random.default_rng(ss * 1000 + kp)
+        S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.1, dtype)
+        inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
+               "b": rng.standard_normal((B, kp * ss)).astype(dtype),
+               "x0": rng.standard_normal((B, kp * ss)).astype(dtype)}
+        max_iters, rel, abs_tol = 300, (1e-8 if dtype == np.float32 else 1e-14), 0.0
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    assert gpu.pcg_batched_placement(ss, kp, tdt) == gpu.PLACEMENT_S_RESIDENT
+    say("pcg ss=%d kp=%d B=%d %s S-resident" % (ss, kp, inp["b"].shape[0], np.dtype(dtype).name))
+    got = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
+    assert np.all(got[2] == gpu.CONVERGED)
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
+    assert gpu.pcg_batched_placement(ss, kp, tdt) != gpu.PLACEMENT_S_RESIDENT
+    say("  streamed reference placement")
+    ref = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
+    for u, v in zip(ref, got):
+        np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, ss, kp, max_iters, rel, abs_tol, got, dtype)
