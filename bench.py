@@ -65,9 +65,9 @@ KERNEL_OF = {
     "pcg2_f64": "pcg_batched_kernel<double, 14, 1, 7>",
     "grid4_f32": "pcg_grid_kernel<float, 12,",
     "pcg2_pd": "pcg_batched_kernel<float, 14, 2, 3>",
-    "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 4>",
+    "pcg3_pd": "pcg_batched_kernel<float, 21, 3, 9>",
     "pcg2_pdp": "pcg_batched_kernel<float, 14, 2, 6>",
-    "pcg3_pdp": "pcg_batched_kernel<float, 21, 3, 5>",
+    "pcg3_pdp": "pcg_batched_kernel<float, 21, 3, 8>",
     "grid4_sr": "pcg_grid_cg1_kernel<double, 12,",
     "grid4_f32_sr": "pcg_grid_cg1_kernel<float, 12,",
 }

@@ -99,6 +99,8 @@ enum Mode {
   kStreamPrefetchPDP = 5,  // streamed with prefetch, Pinv as packed D blocks
   kResidentPDP = 6,        // resident, Pinv as packed D blocks
   kHybrid = 7,             // S resident, Pinv streamed by direct loads into LDS
+  kHybridPDP = 8,          // S resident, Pinv's packed D blocks held whole in LDS
+  kHybridPD = 9,           // S resident, D parts of the [L|D|R] Pinv gathered into LDS
 };
 
 // Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for the
@@ -108,7 +110,7 @@ enum Mode {
 constexpr int max_threads_for(int rpt, int mode) {
   const bool resident = mode == kResident || mode == kResidentPD || mode == kResidentPDP;
   return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || mode == kStreamPrefetchPDP ||
-          mode == kHybrid || rpt == 3 || rpt == 4 ||
+          mode == kHybrid || mode == kHybridPDP || mode == kHybridPD || rpt == 3 || rpt == 4 ||
           (resident && rpt > 1))
              ? 512
              : 1024;
@@ -121,9 +123,14 @@ pcg_batched_kernel(PcgArgs<T> a) {
   constexpr bool PD = MODE == kResidentPD || MODE == kResidentPDP;  // Pinv rows: D part only
   constexpr bool PFM =
       MODE == kStreamPrefetch || MODE == kStreamPrefetchPD || MODE == kStreamPrefetchPDP;
-  // HYBRID: S rows resident in registers, Pinv chunks streamed into the
-  // wave's LDS stage by direct buffer -> LDS loads.
-  constexpr bool HYB = MODE == kHybrid;
+  // HYBRID: S rows resident in registers; Pinv chunks streamed into the
+  // wave's LDS stage by direct buffer -> LDS loads (HYBS), or Pinv's D blocks
+  // loaded whole into LDS once the same way (HYBP): copied when Pinv comes as
+  // packed D blocks, gathered from the [L|D|R] rows under the block-diagonal
+  // hint.
+  constexpr bool HYBS = MODE == kHybrid;
+  constexpr bool HYBP = MODE == kHybridPDP || MODE == kHybridPD;
+  constexpr bool HYB = HYBS || HYBP;
   constexpr bool SRES = RES || HYB;  // S rows held in registers
   // Pinv chunks of packed D blocks in the prefetch ring (compile time, so the
   // ring keeps one load pattern per position).
@@ -143,7 +150,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   const long long prob = blockIdx.x;
   const long long mstride = (long long)n * W;
   // Pinv as packed D blocks: fixed by the mode, except for plain staging.
-  const bool packed = MODE == kResidentPDP || MODE == kStreamPrefetchPDP ||
+  const bool packed = MODE == kResidentPDP || MODE == kStreamPrefetchPDP || MODE == kHybridPDP ||
                       (MODE == kStream && a.ppacked != 0);
   const T* __restrict__ gS = a.S + prob * mstride;
   const T* __restrict__ gP = a.P + prob * (packed ? (long long)n * ss : mstride);
@@ -157,6 +164,8 @@ pcg_batched_kernel(PcgArgs<T> a) {
   T* slotB = slotA + nchunks;
   const size_t head = ((size_t)(2 * pad_len + 2 * nchunks) * sizeof(T) + 15) & ~(size_t)15;
   T* stage = reinterpret_cast<T*>(smem_raw + head) + (size_t)wave * a.stage_elems;
+  // HYBP: the problem's packed Pinv D blocks, [n][ss], after the head.
+  T* pinv_lds = reinterpret_cast<T*>(smem_raw + head);
 
   // Row bookkeeping.
   int row[RPT], wstart[RPT];
@@ -257,7 +266,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // fetch.  The loads use no registers once issued, so the next chunk is in
   // flight while the wave multiplies, reduces and waits at barriers.
   auto dma_chunk = [&](int k) {
-    if constexpr (HYB) {
+    if constexpr (HYBS) {
       const int r0 = chunk_r0(k);
       const bool has = r0 < n;
       const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
@@ -268,6 +277,41 @@ pcg_batched_kernel(PcgArgs<T> a) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
             (lane + u * kWave) * 16, 0, 0, 0);
+    }
+  };
+
+  // HYBP: every wave loads pieces q = wave, wave + NW, ... of the problem's
+  // D blocks into pinv_lds, laid out [n][ss].  Packed D blocks are one
+  // contiguous range, copied in 1 KB pieces (the range check zero-fills the
+  // last piece past the data).  Under the block-diagonal hint each lane
+  // gathers one 4-byte word of a D block from its [L|D|R] row (256-byte
+  // pieces; words past the D blocks read zeros).  Each wave waits for its
+  // own pieces before the barrier that precedes the first Pinv matvec.
+  auto dma_pinv_whole = [&]() {
+    if constexpr (MODE == kHybridPD) {
+      constexpr int DPE = (int)sizeof(T) / 4;  // 4-byte words per element
+      const int nwords = n * SS * DPE;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(gP, n * W * (int)sizeof(T));
+      const int npieces = (nwords + kWave - 1) / kWave;
+      unsigned char* base = reinterpret_cast<unsigned char*>(pinv_lds);
+      for (int q = wave; q < npieces; q += NW) {
+        const int d = q * kWave + lane;  // word of the [n][ss] D layout
+        const int e = d / DPE, r = e / SS, c = e - r * SS;
+        const int off = d < nwords ? (r * 3 * SS + SS + c) * (int)sizeof(T) + (d - e * DPE) * 4
+                                   : 0x7ffffff0;  // past the end: zero
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(base + q * kWave * 4), 4, off, 0, 0,
+            0);
+      }
+    } else if constexpr (HYBP) {
+      const int nbytes = n * ss * (int)sizeof(T);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(gP, nbytes);
+      const int npieces = (nbytes + kWave * 16 - 1) / (kWave * 16);
+      unsigned char* base = reinterpret_cast<unsigned char*>(pinv_lds);
+      for (int q = wave; q < npieces; q += NW)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(base + q * kWave * 16), 16,
+            q * kWave * 16 + lane * 16, 0, 0, 0);
     }
   };
 
@@ -334,7 +378,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
             for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], w[c], acc);
           }
         }
-      } else if constexpr (HYB) {
+      } else if constexpr (HYBS) {
         // Pinv chunk k is in, or on its way to, the stage.  Wait for this
         // wave's direct loads, multiply, and once every stage read has
         // returned, load the next chunk of the sequence (chunk 0 of the next
@@ -353,6 +397,15 @@ pcg_batched_kernel(PcgArgs<T> a) {
           asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         dma_chunk((k + 1) % RPT);
+      } else if constexpr (HYBP) {
+        // The row's ss values of its D block, times the middle third of the
+        // window (the terms and order of a D-only row).
+        if (valid[k]) {
+          const T* __restrict__ m = pinv_lds + row[k] * SS;
+          const T* __restrict__ w = vpad + wstart[k] + SS;
+#pragma unroll
+          for (int c = 0; c < SS; ++c) acc = fma(m[c], w[c], acc);
+        }
       } else {
         const int r0 = chunk_r0(k);
         if constexpr (PFM) {
@@ -451,6 +504,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     if (kRingDepth == 2) ring_load(1 % (2 * RPT));
   }
   dma_chunk(0);
+  dma_pinv_whole();
 #pragma unroll
   for (int k = 0; k < RPT; ++k)
     if (valid[k]) p_pad[ss + row[k]] = xr[k];
@@ -469,6 +523,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     rr[k] = valid[k] ? tmp[k] - sv[k] : T(0);
     if (valid[k]) r_pad[ss + row[k]] = rr[k];
   }
+  if constexpr (HYBP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // D blocks landed
   block_sync();
   matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
 #pragma unroll
@@ -611,7 +666,7 @@ int prefetch_stage_elems(int ss) {
 // prefetching streamed placement is allowed (specialised, 16-byte aligned).
 template <typename T>
 bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag,
-               bool hybrid, size_t lds_max, Plan* plan) {
+               bool hybrid, bool pinv_packed, size_t lds_max, Plan* plan) {
   const int n = kp * ss;
   const int W = 3 * ss;
   const int nchunks = (n + 63) / 64;
@@ -638,20 +693,25 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       return true;
     }
   }
-  // HYBRID (general Pinv, 16-byte aligned, specialised size): the fewest
-  // rows per lane whose workgroup and LDS stages fit.
-  if (hybrid && !pinv_diag) {
+  // HYBRID (16-byte aligned, specialised size; a general Pinv streamed, or
+  // its D blocks held whole in LDS, packed or under the block-diagonal
+  // hint): the fewest rows per lane whose workgroup and LDS fit.
+  if (hybrid) {
     for (int rpt = 1; rpt <= 3; ++rpt) {
       if (rpt * 3 * ss * (int)sizeof(T) / 4 > 192) break;
       const int NW = (nchunks + rpt - 1) / rpt;
       if (NW * 64 > max_threads_for(rpt, kHybrid)) continue;
-      const int stage = prefetch_stage_elems<T>(ss);
-      const size_t lds = lds_bytes<T>(ss, kp, NW, stage);
+      // D blocks in LDS: n*ss elements in whole 1 KB pieces.
+      const size_t dbytes = ((size_t)n * ss * sizeof(T) + 1023) & ~(size_t)1023;
+      const int stage = pinv_diag ? 0 : prefetch_stage_elems<T>(ss);
+      const size_t lds = pinv_diag ? lds_bytes<T>(ss, kp, NW, 0) + dbytes
+                                   : lds_bytes<T>(ss, kp, NW, stage);
       if (lds > lds_max) continue;
       Plan p;
       p.NW = NW;
       p.RPT = rpt;
       p.hyb = true;
+      p.pd = pinv_diag;
       p.stage_elems = stage;
       p.lds = lds;
       *plan = p;
@@ -778,17 +838,17 @@ int launch_res(const PcgArgs<T>& a, int n_problems, const Plan& pl_in, hipStream
   return fail(GLASS_EUNSUPPORTED, "pcg: internal plan error (resident rows per lane)");
 }
 
-template <typename T, int SS>
+template <typename T, int SS, int M>
 int launch_hyb(const PcgArgs<T>& a, int n_problems, const Plan& pl, hipStream_t st) {
   switch (pl.RPT) {
     case 1:
-      if constexpr (kHybridRowsFit<T>(SS, 1)) return launch_one<T, SS, 1, kHybrid>(a, n_problems, pl, st);
+      if constexpr (kHybridRowsFit<T>(SS, 1)) return launch_one<T, SS, 1, M>(a, n_problems, pl, st);
       break;
     case 2:
-      if constexpr (kHybridRowsFit<T>(SS, 2)) return launch_one<T, SS, 2, kHybrid>(a, n_problems, pl, st);
+      if constexpr (kHybridRowsFit<T>(SS, 2)) return launch_one<T, SS, 2, M>(a, n_problems, pl, st);
       break;
     case 3:
-      if constexpr (kHybridRowsFit<T>(SS, 3)) return launch_one<T, SS, 3, kHybrid>(a, n_problems, pl, st);
+      if constexpr (kHybridRowsFit<T>(SS, 3)) return launch_one<T, SS, 3, M>(a, n_problems, pl, st);
       break;
     default:
       break;
@@ -800,7 +860,10 @@ template <typename T, int SS>
 int launch_ss(const PcgArgs<T>& a, int n_problems, const Plan& pl,
               hipStream_t st) {
   if constexpr (SS > 0) {
-    if (pl.hyb) return launch_hyb<T, SS>(a, n_problems, pl, st);
+    if (pl.hyb)
+      return !pl.pd ? launch_hyb<T, SS, kHybrid>(a, n_problems, pl, st)
+                    : (pl.packed ? launch_hyb<T, SS, kHybridPDP>(a, n_problems, pl, st)
+                                 : launch_hyb<T, SS, kHybridPD>(a, n_problems, pl, st));
     if (pl.res) {
       if (!pl.pd) return launch_res<T, SS, false, false>(a, n_problems, pl, st);
       return pl.packed ? launch_res<T, SS, true, true>(a, n_problems, pl, st)
@@ -838,10 +901,12 @@ bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, siz
   const bool hybrid = specialised && vec && kHybridSize<T>(ss) &&
                       std::getenv("GLASS_AMD_PCG_NO_HYBRID") == nullptr;
   pinv_diag = pinv_diag || pinv_packed;
-  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, hybrid, lds_max, pl)) return false;
+  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, hybrid, pinv_packed, lds_max, pl))
+    return false;
   if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && (pl->res || pl->hyb)) {
     Plan alt;
-    if (make_plan<T>(ss, kp, false, prefetch, pinv_packed, false, lds_max, &alt)) *pl = alt;
+    if (make_plan<T>(ss, kp, false, prefetch, pinv_packed, false, pinv_packed, lds_max, &alt))
+      *pl = alt;
   }
   if (pinv_packed && !pl->pd && (pl->res || pl->prefetch)) return false;  // not reached
   pl->packed = pinv_packed;
@@ -895,7 +960,8 @@ int placement_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_pa
   Plan pl;
   if (!choose_plan<T>(ss, kp, vec, pinv_diag, pinv_packed, dev.max_lds_per_block, &pl))
     return fail(GLASS_EUNSUPPORTED, "pcg: problem too large for one workgroup (rows or LDS)");
-  if (pl.hyb) return GLASS_PLACEMENT_S_RESIDENT;
+  // S in registers with the D blocks in LDS reads both once.
+  if (pl.hyb) return pl.pd ? GLASS_PLACEMENT_RESIDENT : GLASS_PLACEMENT_S_RESIDENT;
   return pl.res ? GLASS_PLACEMENT_RESIDENT
                 : (pl.prefetch ? GLASS_PLACEMENT_STREAMED_PREFETCH : GLASS_PLACEMENT_STREAMED);
 }

@@ -157,8 +157,9 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
                          void* hip_stream);
 
 /* Where glass_pcg_batched_ex keeps S and Pinv for a problem shape and flags
- * on the current device: GLASS_PLACEMENT_RESIDENT (each lane's rows in
- * registers, read from HBM once per solve),
+ * on the current device: GLASS_PLACEMENT_RESIDENT (both read from HBM once
+ * per solve: each lane's rows in registers, or for packed D blocks that do
+ * not fit there, S's rows in registers and the D blocks in LDS),
  * GLASS_PLACEMENT_STREAMED[_PREFETCH] (re-read from memory for every
  * matvec) or GLASS_PLACEMENT_S_RESIDENT (S's rows in registers, read once;
  * Pinv re-read for every matvec through the LDS, 16-byte aligned matrices

@@ -192,8 +192,10 @@ def test_pcg_placement_query_matches_the_workloads(gpu, monkeypatch):
     assert gpu.pcg_batched_placement(21, 64, torch.float32, aligned16=False) == \
         gpu.PLACEMENT_STREAMED
     assert gpu.pcg_batched_placement(21, 64, torch.float32, pinv_block_diagonal=True) == \
-        gpu.PLACEMENT_STREAMED_PREFETCH
+        gpu.PLACEMENT_RESIDENT
     monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
+    assert gpu.pcg_batched_placement(21, 64, torch.float32, pinv_block_diagonal=True) == \
+        gpu.PLACEMENT_STREAMED_PREFETCH
     assert gpu.pcg_batched_placement(21, 64, torch.float32) == gpu.PLACEMENT_STREAMED_PREFETCH
     monkeypatch.delenv("GLASS_AMD_PCG_NO_HYBRID")
     monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
@@ -251,7 +253,7 @@ def test_empty_batches_are_no_ops(gpu):
     (12, 60, 9, np.float32, False),
     (21, 40, 7, np.float32, True),     # 840 rows: resident only with the flag
     (6, 20, 9, np.float64, False),
-    (21, 64, 5, np.float32, False),    # streamed either way: the flag is ignored
+    (21, 64, 5, np.float32, True),     # S resident; with the flag the D parts in LDS too
 ])
 def test_pcg_pinv_block_diagonal_hint(gpu, ss, kp, B, dtype, resident_only_with_flag):
     """GLASS_PCG_PINV_BLOCK_DIAGONAL on block-Jacobi preconditioners: the
@@ -325,9 +327,10 @@ def test_pcg_pinv_block_diagonal_streamed_prefetch(gpu, monkeypatch):
     (6, 32, 40, np.float32),
     (12, 60, 9, np.float32),
     (21, 40, 7, np.float32),    # 840 rows: resident with D blocks
-    (21, 64, 5, np.float32),    # streamed with prefetch
+    (21, 64, 5, np.float32),    # S in registers, D blocks in LDS
     (6, 20, 9, np.float64),
-    (14, 32, 6, np.float64),    # plain streamed staging, specialised size
+    (14, 32, 6, np.float64),    # S in registers, D blocks in LDS
+    (14, 100, 3, np.float64),   # plain streamed staging, specialised size
     (9, 32, 5, np.float32),     # plain streamed staging, generic size, 16-byte paths
     (9, 23, 5, np.float32),     # generic size, ragged last chunk, element paths
     (14, 1, 3, np.float32),     # one block-row (Pinv is exactly inv(S))
@@ -337,7 +340,8 @@ def test_pcg_pinv_packed_diagonal_blocks(gpu, ss, kp, B, dtype):
     """GLASS_PCG_PINV_DIAGONAL_BLOCKS: Pinv passed as packed D blocks
     [B, kp, ss, ss] gives the same bits as the [L|D|R] layout with zero L
     and R blocks (the same terms in the same order) in every placement, and
-    meets the oracle; the placement query reports the hinted placement."""
+    meets the oracle; the placement query reports the hinted placement, or
+    the resident one where S fits in registers and the D blocks in LDS."""
     rng = np.random.default_rng(ss * 1000 + kp)
     S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.2, dtype)
     inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
@@ -347,7 +351,8 @@ def test_pcg_pinv_packed_diagonal_blocks(gpu, ss, kp, B, dtype):
     tdt = torch.float32 if dtype == np.float32 else torch.float64
     hinted = gpu.pcg_batched_placement(ss, kp, tdt, pinv_block_diagonal=True)
     packed = gpu.pcg_batched_placement(ss, kp, tdt, pinv_diagonal_blocks=True)
-    assert packed == hinted
+    assert packed == hinted or (packed == gpu.PLACEMENT_RESIDENT
+                                and hinted != gpu.PLACEMENT_RESIDENT)
     say("pcg Pinv packed D blocks ss=%d kp=%d B=%d %s placement %d"
         % (ss, kp, B, np.dtype(dtype).name, packed))
     ref = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0)
@@ -387,8 +392,8 @@ def test_pcg_pinv_packed_element_aligned_pointer(gpu, cfg):
 
 
 def test_pcg_pinv_packed_diagonal_blocks_workloads(gpu, monkeypatch):
-    """Packed D blocks on both full workloads (ss=14 resident, ss=21
-    streamed with prefetch) against the [L|D|R] runs, then the other
+    """Packed D blocks on both full workloads (ss=14 resident, ss=21 with S
+    in registers and the D blocks in LDS) against the [L|D|R] runs, then the other
     streamed forms: prefetch at 1, 2 and 4 rows per lane, and plain
     staging."""
     for cfg in (2, 3):
@@ -416,6 +421,7 @@ def test_pcg_pinv_packed_diagonal_blocks_workloads(gpu, monkeypatch):
             np.testing.assert_array_equal(u, v)
     monkeypatch.delenv("GLASS_AMD_PCG_RPT")
     monkeypatch.setenv("GLASS_AMD_PCG_NO_PREFETCH", "1")
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")  # ss=21: plain staging too
     assert gpu.pcg_batched_placement(w2.ss, w2.kp, torch.float32, pinv_diagonal_blocks=True) \
         == gpu.PLACEMENT_STREAMED
     w3 = workloads.WORKLOADS[3]
@@ -503,4 +509,55 @@ def test_pcg_s_resident_matches_streamed(gpu, monkeypatch, ss, kp, B, dtype):
     ref = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
     for u, v in zip(ref, got):
         np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, ss, kp, max_iters, rel, abs_tol, got, dtype)
+
+
+@pytest.mark.parametrize("ss,kp,B,dtype", [
+    (21, 64, None, np.float32),   # the ss=21 workload, all 2048 problems
+    (21, 60, 4, np.float32),      # 20 chunks, ragged last chunk
+    (21, 52, 3, np.float32),      # 18 chunks on 6 waves, ragged
+    (14, 32, 40, np.float64),     # the ss=14 workload in float64
+    (21, 10, 3, np.float64),      # 4 chunks, one row per lane
+])
+def test_pcg_packed_pinv_in_lds_matches_streamed(gpu, monkeypatch, ss, kp, B, dtype):
+    """Pinv's D blocks in LDS with S in registers (both matrices read once per
+    solve): loaded whole when Pinv comes as packed D blocks, gathered from the
+    [L|D|R] rows under the block-diagonal hint.  The same terms in the same
+    order as the streamed placements of both forms and as the general
+    contraction: bit-identical outputs, and the oracle bars.  (Shapes whose S
+    and D rows do not fit the register-resident placement.)"""
+    if (ss, kp) in ((21, 64), (14, 32)):
+        w = workloads.WORKLOADS[3 if ss == 21 else 2]
+        inp = {k: v.astype(dtype) for k, v in workloads.generate(w, n_problems=B).items()}
+        max_iters, rel, abs_tol = w.max_iters, w.rel_tol, w.abs_tol
+    else:
+        rng = np.random.default_rng(ss * 1000 + kp + 7)
+        S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.1, dtype)
+        inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
+               "b": rng.standard_normal((B, kp * ss)).astype(dtype),
+               "x0": rng.standard_normal((B, kp * ss)).astype(dtype)}
+        max_iters, rel, abs_tol = 300, (1e-8 if dtype == np.float32 else 1e-14), 0.0
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    assert gpu.pcg_batched_placement(ss, kp, tdt, pinv_diagonal_blocks=True) == \
+        gpu.PLACEMENT_RESIDENT
+    say("pcg ss=%d kp=%d B=%d %s packed D blocks in LDS" % (ss, kp, inp["b"].shape[0],
+                                                           np.dtype(dtype).name))
+    assert gpu.pcg_batched_placement(ss, kp, tdt, pinv_block_diagonal=True) == \
+        gpu.PLACEMENT_RESIDENT
+    got = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol, pinv_diagonal_blocks=True)
+    assert np.all(got[2] == gpu.CONVERGED)
+    say("  D parts gathered from [L|D|R] rows (block-diagonal hint)")
+    hinted = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol, pinv_block_diagonal=True)
+    general = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
+    assert gpu.pcg_batched_placement(ss, kp, tdt, pinv_diagonal_blocks=True) != \
+        gpu.PLACEMENT_RESIDENT
+    say("  streamed placements, packed and hinted")
+    ref = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol, pinv_diagonal_blocks=True)
+    ref_h = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol, pinv_block_diagonal=True)
+    for u, v, g, h, rh in zip(ref, got, general, hinted, ref_h):
+        np.testing.assert_array_equal(u, v)
+        np.testing.assert_array_equal(g, v)
+        np.testing.assert_array_equal(h, v)
+        np.testing.assert_array_equal(rh, v)
     assert_pcg_parity(inp, ss, kp, max_iters, rel, abs_tol, got, dtype)
