@@ -13,9 +13,10 @@
 // order, so the result is independent of NT.  The operation streams S once:
 // it is HBM-bandwidth bound, and the LDS hop only exists to turn the
 // 3*ss-strided per-row reads into coalesced 16-byte loads.  For the
-// specialised state sizes every load of the tile is issued before the first
-// LDS store (ceil(3*ss*sizeof(T)/16) vectors per thread in flight), through a
-// buffer resource over exactly the tile's bytes: the hardware range-checks
+// specialised state sizes the tile goes from memory straight into LDS with
+// direct buffer -> LDS loads (ceil(3*ss*sizeof(T)/16) 16-byte vectors per
+// thread, all in flight, none through registers), marked non-temporal, through
+// a buffer resource over exactly the tile's bytes: the hardware range-checks
 // raw buffer loads per dword, so a tile ending inside a vector still arrives
 // whole and lanes past the end read zeros, without branching.  The tile height is chosen so that the rows of a
 // problem split into tiles with as little of a ragged last tile as possible.
@@ -24,10 +25,24 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+// Tile staging for the specialised state sizes: 1 = direct buffer -> LDS
+// loads (no registers in flight, no LDS stores), 0 = buffer loads into
+// registers, then LDS stores.  GLASS_AMD_BDMV_AUX: cache-policy bits of the
+// S loads; 2 = non-temporal (S is read once, so its lines need not stay in
+// the L2 or the Infinity Cache).
+#ifndef GLASS_AMD_BDMV_DIRECT
+#define GLASS_AMD_BDMV_DIRECT 1
+#endif
+#ifndef GLASS_AMD_BDMV_AUX
+#define GLASS_AMD_BDMV_AUX 2
+#endif
+
 namespace glass {
 namespace {
 
 constexpr int kBdmvMaxThreads = 256;
+constexpr bool kBdmvDirect = GLASS_AMD_BDMV_DIRECT != 0;
+constexpr int kBdmvAux = GLASS_AMD_BDMV_AUX;
 
 template <typename T, int SS>
 __global__ void __launch_bounds__(kBdmvMaxThreads)
@@ -60,13 +75,31 @@ bdmv_kernel(T* __restrict__ y, const T* __restrict__ S,
   if constexpr (SS > 0) {
     const int count = rows * W;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(gS, count * (int)sizeof(T));
-    vec16_t t[U];
+    if constexpr (kBdmvDirect) {
+      // Vector tid + u*NT lands at the same byte offset of s_mat: a wave's
+      // 64 lanes write one contiguous 1 KB per load.
+      const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+      unsigned char* sb = reinterpret_cast<unsigned char*>(s_mat);
 #pragma unroll
-    for (int u = 0; u < U; ++u) t[u] = buffer_load16(rs, (tid + u * NT) * 16);
-    for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];
-    vec16_t* s4 = reinterpret_cast<vec16_t*>(s_mat);
+      for (int u = 0; u < U; ++u)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(sb + (u * NT + wave * kWave) * 16), 16,
+            (tid + u * NT) * 16, 0, 0, kBdmvAux);
+      for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];
+      // The tile's direct loads have landed before the barrier publishes
+      // them to the other waves.
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      vec16_t t[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) s4[tid + u * NT] = t[u];
+      for (int u = 0; u < U; ++u)
+        t[u] = __builtin_bit_cast(
+            vec16_t, __builtin_amdgcn_raw_buffer_load_b128(rs, (tid + u * NT) * 16, 0, kBdmvAux));
+      for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];
+      vec16_t* s4 = reinterpret_cast<vec16_t*>(s_mat);
+#pragma unroll
+      for (int u = 0; u < U; ++u) s4[tid + u * NT] = t[u];
+    }
   } else {
     copy_to_lds<true>(s_mat, gS, rows * W, tid, NT, vec != 0);
     for (int e = tid; e < vcount; e += NT) s_win[e] = gv[e];
