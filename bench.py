@@ -124,20 +124,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def algorithmic_bytes_pcg(w, iters: np.ndarray, resident, pinv_diag=False) -> float:
+def algorithmic_bytes_pcg(w, iters: np.ndarray, resident, pinv_diag=False,
+                          pinned_rows=0) -> float:
     """Bytes one solve must move between HBM and the chip, by the algorithm:
     S and Pinv (n*3ss each; Pinv n*ss when only its D blocks are read) once
     if they stay on chip, else once per pass (the initial S x0 / Pinv r pass
     plus one per iteration); x read, b read, x written (n each); iters
     (4 bytes).  resident: True (both on chip), False (both streamed) or "S"
-    (S on chip, Pinv streamed)."""
+    (S on chip, Pinv streamed except pinned_rows of its rows, which stay on
+    chip)."""
     es = np.dtype(w.dtype).itemsize
     s_bytes = w.n * 3 * w.ss * es
     p_bytes = w.n * (w.ss if pinv_diag else 3 * w.ss) * es
     vec = 3 * w.n * es + 4
     passes = iters.astype(np.float64) + 1
     if resident == "S":
-        return float(np.sum(s_bytes + passes * p_bytes + vec))
+        p_pin = pinned_rows * (w.ss if pinv_diag else 3 * w.ss) * es
+        return float(np.sum(s_bytes + p_pin + passes * (p_bytes - p_pin) + vec))
     if resident:
         passes = np.ones_like(passes)
     return float(np.sum(passes * (s_bytes + p_bytes) + vec))
@@ -392,7 +395,10 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         w.ss, w.kp, S.dtype, pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
     resident = grid or placement == glass.PLACEMENT_RESIDENT or (
         "S" if placement == glass.PLACEMENT_S_RESIDENT else False)
-    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed)
+    pinned = glass.pcg_batched_pinned_rows(
+        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd,
+        pinv_diagonal_blocks=packed) if resident == "S" else 0
+    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed, pinned_rows=pinned)
     for k in range(min(10, len(xs))):
         xs[k].zero_()
     iso = isolated_ms(torch, lambda k: run(xs[k]), reps=min(10, len(xs)))

@@ -22,7 +22,8 @@ __all__ = [
     "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
     "PCG_PINV_BLOCK_DIAGONAL", "PCG_PINV_DIAGONAL_BLOCKS", "GRID_SINGLE_REDUCTION",
-    "pcg_batched_placement", "PLACEMENT_RESIDENT", "PLACEMENT_STREAMED_PREFETCH",
+    "pcg_batched_placement", "pcg_batched_pinned_rows", "PLACEMENT_RESIDENT",
+    "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT",
 ]
 
@@ -71,6 +72,7 @@ def load():
             "glass_bdsv_batched": ([P, P, P, I, I, I, P, P, Z, I, P], I),
             "glass_bdsv_workspace_bytes": ([I, I, I, I], Z),
             "glass_pcg_batched_placement": ([I, I, I, I, U], I),
+            "glass_pcg_batched_pinned_rows": ([I, I, I, I, U], I),
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
@@ -221,6 +223,23 @@ def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=Tr
                                                if pinv_diagonal_blocks else 0))
     if rc < 0:
         _check(rc, "glass_pcg_batched_placement")
+    return rc
+
+
+def pcg_batched_pinned_rows(state_size: int, knot_points: int, dtype, aligned16=True,
+                            pinv_block_diagonal=False, pinv_diagonal_blocks=False) -> int:
+    """Pinv rows per problem that the S-resident placement keeps in LDS for the
+    whole solve (read once; the others are read once per matvec pass); 0 for
+    the other placements.  Raises for shapes the solve rejects."""
+    import torch
+    code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
+    rc = load().glass_pcg_batched_pinned_rows(int(state_size), int(knot_points), code,
+                                              1 if aligned16 else 0,
+                                              (PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0)
+                                              | (PCG_PINV_DIAGONAL_BLOCKS
+                                                 if pinv_diagonal_blocks else 0))
+    if rc < 0:
+        _check(rc, "glass_pcg_batched_pinned_rows")
     return rc
 
 

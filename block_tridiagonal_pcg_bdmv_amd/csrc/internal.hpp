@@ -42,6 +42,9 @@ int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
 // pinv_packed: Pinv given as packed D blocks (implies pinv_diag).
 int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
                           bool pinv_packed);
+// Pinv rows the S-resident placement keeps pinned in LDS (0 otherwise).
+int pcg_batched_pinned_rows(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
+                            bool pinv_packed);
 
 size_t bdsv_workspace_bytes(int ss, int kp, long long n_problems, glass_dtype dt);
 int launch_bdsv(glass_dtype dt, void* x, const void* S, const void* b, int ss,

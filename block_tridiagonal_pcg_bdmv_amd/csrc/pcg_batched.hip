@@ -51,6 +51,7 @@
 // multiplied with the middle third of the window.  The terms and their order
 // are those of the D-only rows above, so the results are the same; every
 // byte fetched is a D byte.
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <type_traits>
@@ -85,6 +86,8 @@ struct PcgArgs {
   T abs_tol;
   int vec;          // 16-byte staging allowed (alignment checked on the host)
   int stage_elems;  // per-wave LDS stage, elements
+  int npin;         // HYBRID streaming: waves below npin keep their last Pinv
+                    // chunk pinned in LDS (loaded once)
   int ppacked;      // Pinv is packed D blocks, [kp*ss][ss] per problem (read
                     // by kStream; the other modes fix it at compile time)
 };
@@ -164,6 +167,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
   T* slotB = slotA + nchunks;
   const size_t head = ((size_t)(2 * pad_len + 2 * nchunks) * sizeof(T) + 15) & ~(size_t)15;
   T* stage = reinterpret_cast<T*>(smem_raw + head) + (size_t)wave * a.stage_elems;
+  // HYBS: a wave below a.npin holds its last chunk (k = RPT-1) of Pinv in a
+  // pinned slot after the NW stages, loaded once; only its other chunks
+  // stream.  Host: RPT >= 2 and the slots fit in LDS.
+  const bool pin_last = HYBS && wave < a.npin;  // wave-uniform
+  T* pinned = reinterpret_cast<T*>(smem_raw + head) + (size_t)(NW + wave) * a.stage_elems;
   // HYBP: the problem's packed Pinv D blocks, [n][ss], after the head.
   T* pinv_lds = reinterpret_cast<T*>(smem_raw + head);
 
@@ -265,13 +273,13 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // every vector of a chunk the wave does not have, write zeros without a
   // fetch.  The loads use no registers once issued, so the next chunk is in
   // flight while the wave multiplies, reduces and waits at barriers.
-  auto dma_chunk = [&](int k) {
+  auto dma_chunk_to = [&](int k, T* dst) {
     if constexpr (HYBS) {
       const int r0 = chunk_r0(k);
       const bool has = r0 < n;
       const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gP + (long long)r0 * W : gP, nbytes);
-      unsigned char* st = reinterpret_cast<unsigned char*>(stage);
+      unsigned char* st = reinterpret_cast<unsigned char*>(dst);
 #pragma unroll
       for (int u = 0; u < NV; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -279,6 +287,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
             (lane + u * kWave) * 16, 0, 0, 0);
     }
   };
+  auto dma_chunk = [&](int k) { dma_chunk_to(k, stage); };
 
   // HYBP: every wave loads pieces q = wave, wave + NW, ... of the problem's
   // D blocks into pinv_lds, laid out [n][ss].  Packed D blocks are one
@@ -379,14 +388,15 @@ pcg_batched_kernel(PcgArgs<T> a) {
           }
         }
       } else if constexpr (HYBS) {
-        // Pinv chunk k is in, or on its way to, the stage.  Wait for this
-        // wave's direct loads, multiply, and once every stage read has
-        // returned, load the next chunk of the sequence (chunk 0 of the next
-        // matvec after the last) into the stage.
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Pinv chunk k is pinned, or in (or on its way to) the stage.  For
+        // the stage: wait for this wave's direct loads, multiply, and once
+        // every stage read has returned, load the next streamed chunk of the
+        // sequence (chunk 0 of the next matvec after the last) into it.
+        const bool from_pin = pin_last && k == RPT - 1;  // wave-uniform
+        if (!from_pin) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (chunk_r0(k) < n) {  // wave-uniform
           if (valid[k]) {
-            const T* __restrict__ m = stage + lane * W;
+            const T* __restrict__ m = (from_pin ? pinned : stage) + lane * W;
             const T* __restrict__ w = vpad + wstart[k];
 #pragma unroll 3
             for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
@@ -394,9 +404,13 @@ pcg_batched_kernel(PcgArgs<T> a) {
               for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], w[c], acc);
             }
           }
-          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (!from_pin) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-        dma_chunk((k + 1) % RPT);
+        if (!from_pin) {
+          int next = (k + 1) % RPT;
+          if (pin_last && next == RPT - 1) next = 0;
+          dma_chunk(next);
+        }
       } else if constexpr (HYBP) {
         // The row's ss values of its D block, times the middle third of the
         // window (the terms and order of a D-only row).
@@ -504,6 +518,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     if (kRingDepth == 2) ring_load(1 % (2 * RPT));
   }
   dma_chunk(0);
+  if (pin_last) dma_chunk_to(RPT - 1, pinned);
   dma_pinv_whole();
 #pragma unroll
   for (int k = 0; k < RPT; ++k)
@@ -523,7 +538,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
     rr[k] = valid[k] ? tmp[k] - sv[k] : T(0);
     if (valid[k]) r_pad[ss + row[k]] = rr[k];
   }
-  if constexpr (HYBP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // D blocks landed
+  // D blocks, or pinned chunks, landed
+  if constexpr (HYBP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (HYBS) {
+    if (pin_last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
   block_sync();
   matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
 #pragma unroll
@@ -604,6 +623,7 @@ struct Plan {
   bool res_auto = false;  // resident rows per lane left to the occupancy choice
   bool prefetch = false;
   bool hyb = false;  // S resident, Pinv streamed by direct loads into LDS
+  int npin = 0;      // waves whose last Pinv chunk stays pinned in LDS
   int stage_elems = 0;
   size_t lds = 0;
 };
@@ -714,6 +734,16 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       p.pd = pinv_diag;
       p.stage_elems = stage;
       p.lds = lds;
+      // Streaming Pinv with several chunks per wave: the LDS left over pins
+      // the last chunk of as many waves as fit (of those that have one).
+      if (!pinv_diag && rpt >= 2 && std::getenv("GLASS_AMD_PCG_NO_PIN") == nullptr) {
+        const size_t slot = (size_t)stage * sizeof(T);
+        int have_last = 0;
+        for (int w = 0; w < NW; ++w) have_last += (w + (rpt - 1) * NW) * 64 < n ? 1 : 0;
+        const int npin = std::min<int>(have_last, (int)((lds_max - lds) / slot));
+        p.npin = npin;
+        p.lds = lds + (size_t)npin * slot;
+      }
       *plan = p;
       return true;
     }
@@ -771,8 +801,8 @@ int launch_one(const PcgArgs<T>& a, int n_problems, const Plan& pl,
     (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, pl.NW * 64, pl.lds);
     std::fprintf(stderr,
                  "glass pcg plan: ss=%d kp=%d mode=%d waves=%d rows/lane=%d "
-                 "lds=%zu stage=%d workgroups/CU=%d\n",
-                 a.ss, a.kp, MODE, pl.NW, RPT, pl.lds, a.stage_elems, per_cu);
+                 "lds=%zu stage=%d pinned=%d workgroups/CU=%d\n",
+                 a.ss, a.kp, MODE, pl.NW, RPT, pl.lds, a.stage_elems, a.npin, per_cu);
   }
   hipLaunchKernelGGL(kern, dim3((unsigned)n_problems), dim3(pl.NW * 64), pl.lds,
                      stream, a);
@@ -940,6 +970,7 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.abs_tol = (T)abs_tol;
   a.vec = vec;
   a.stage_elems = pl.stage_elems;
+  a.npin = pl.npin;
   a.ppacked = pinv_packed ? 1 : 0;
   switch (ss) {
     case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
@@ -966,7 +997,31 @@ int placement_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_pa
                 : (pl.prefetch ? GLASS_PLACEMENT_STREAMED_PREFETCH : GLASS_PLACEMENT_STREAMED);
 }
 
+template <typename T>
+int pinned_rows_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_packed) {
+  DeviceInfo dev;
+  if (int rc = current_device_info(&dev)) return rc;
+  const long long n = (long long)kp * ss, es = (long long)sizeof(T);
+  const bool vec = aligned16 && (n * 3 * ss * es) % 16 == 0 &&
+                   (!pinv_packed || (n * ss * es) % 16 == 0);
+  Plan pl;
+  if (!choose_plan<T>(ss, kp, vec, pinv_diag, pinv_packed, dev.max_lds_per_block, &pl))
+    return fail(GLASS_EUNSUPPORTED, "pcg: problem too large for one workgroup (rows or LDS)");
+  int rows = 0;
+  for (int w = 0; w < pl.npin; ++w) {
+    const long long r0 = (long long)(w + (pl.RPT - 1) * pl.NW) * 64;
+    rows += (int)std::min<long long>(64, n - r0);
+  }
+  return rows;
+}
+
 }  // namespace
+
+int pcg_batched_pinned_rows(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
+                            bool pinv_packed) {
+  return dt == GLASS_F32 ? pinned_rows_typed<float>(ss, kp, aligned16, pinv_diag, pinv_packed)
+                         : pinned_rows_typed<double>(ss, kp, aligned16, pinv_diag, pinv_packed);
+}
 
 int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
                           bool pinv_packed) {

@@ -175,6 +175,15 @@ enum {
 int glass_pcg_batched_placement(int state_size, int knot_points,
                                 glass_dtype dtype, int aligned16, unsigned flags);
 
+/* In GLASS_PLACEMENT_S_RESIDENT, the number of Pinv strip rows (per problem)
+ * that stay in LDS for the whole solve: the LDS left over after the
+ * per-wave stages holds the last chunk of 64 rows of some waves, read from
+ * memory once; the other rows are read once per matvec.  0 for the other
+ * placements.  Arguments, errors and side effects as
+ * glass_pcg_batched_placement (it enqueues nothing). */
+int glass_pcg_batched_pinned_rows(int state_size, int knot_points,
+                                  glass_dtype dtype, int aligned16, unsigned flags);
+
 /*
  * One PCG solve (same steps and outputs as glass_pcg_batched with
  * n_problems = 1) spread over a cooperative grid of workgroups that stay

@@ -28,6 +28,12 @@ def test_pcg_bytes_resident_and_streamed():
     assert bench.algorithmic_bytes_pcg(w, it, resident=False) == (5 * 288 + 76) + (1 * 288 + 76)
     # only Pinv's D blocks: S 6*6*4 = 144 B plus Pinv 6*2*4 = 48 B
     assert bench.algorithmic_bytes_pcg(w, it, resident=True, pinv_diag=True) == 2 * (192 + 76)
+    # S on chip (144 B once), Pinv (144 B) once per pass
+    assert bench.algorithmic_bytes_pcg(w, it, resident="S") == \
+        (144 + 5 * 144 + 76) + (144 + 1 * 144 + 76)
+    # two of Pinv's 6 rows (2 * 6 * 4 = 48 B) pinned on chip: read once
+    assert bench.algorithmic_bytes_pcg(w, it, resident="S", pinned_rows=2) == \
+        (144 + 48 + 5 * 96 + 76) + (144 + 48 + 1 * 96 + 76)
 
 
 def test_bdmv_bytes():

@@ -193,6 +193,14 @@ def test_pcg_placement_query_matches_the_workloads(gpu, monkeypatch):
         gpu.PLACEMENT_STREAMED
     assert gpu.pcg_batched_placement(21, 64, torch.float32, pinv_block_diagonal=True) == \
         gpu.PLACEMENT_RESIDENT
+    # the LDS left over pins the last chunk (64 rows) of two waves at ss=21
+    assert gpu.pcg_batched_pinned_rows(21, 64, torch.float32) == 128
+    assert gpu.pcg_batched_pinned_rows(21, 40, torch.float32) == 128
+    assert gpu.pcg_batched_pinned_rows(14, 32, torch.float64) == 0  # one row per lane
+    assert gpu.pcg_batched_pinned_rows(14, 32, torch.float32) == 0  # resident
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_PIN", "1")
+    assert gpu.pcg_batched_pinned_rows(21, 64, torch.float32) == 0
+    monkeypatch.delenv("GLASS_AMD_PCG_NO_PIN")
     monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
     assert gpu.pcg_batched_placement(21, 64, torch.float32, pinv_block_diagonal=True) == \
         gpu.PLACEMENT_STREAMED_PREFETCH
@@ -479,9 +487,10 @@ def test_pcg_resident_rows_per_lane_bit_identical(gpu, monkeypatch, rpt):
 ])
 def test_pcg_s_resident_matches_streamed(gpu, monkeypatch, ss, kp, B, dtype):
     """S-resident placement (S rows in registers, Pinv chunks loaded straight
-    into the LDS stage): the same terms in the same order as the streamed
-    placements, so bit-identical outputs, and the oracle bars on every
-    problem.  (The placement needs every problem's matrices on a 16-byte
+    into the LDS stage, the last chunk of some waves pinned in the LDS left
+    over): the same terms in the same order as the streamed placements and as
+    the same placement without pinned chunks, so bit-identical outputs, and
+    the oracle bars on every problem.  (The placement needs every problem's matrices on a 16-byte
     boundary: kp*ss a multiple of 4 in float32.)"""
     if ss == 21 and kp == 64:
         w = workloads.WORKLOADS[3]
@@ -503,12 +512,17 @@ def test_pcg_s_resident_matches_streamed(gpu, monkeypatch, ss, kp, B, dtype):
     say("pcg ss=%d kp=%d B=%d %s S-resident" % (ss, kp, inp["b"].shape[0], np.dtype(dtype).name))
     got = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
     assert np.all(got[2] == gpu.CONVERGED)
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_PIN", "1")
+    say("  no chunks pinned in LDS")
+    unpinned = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
+    monkeypatch.delenv("GLASS_AMD_PCG_NO_PIN")
     monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
     assert gpu.pcg_batched_placement(ss, kp, tdt) != gpu.PLACEMENT_S_RESIDENT
     say("  streamed reference placement")
     ref = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
-    for u, v in zip(ref, got):
+    for u, v, w in zip(ref, got, unpinned):
         np.testing.assert_array_equal(u, v)
+        np.testing.assert_array_equal(w, v)
     assert_pcg_parity(inp, ss, kp, max_iters, rel, abs_tol, got, dtype)
 
 
