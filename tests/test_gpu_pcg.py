@@ -575,3 +575,62 @@ def test_pcg_packed_pinv_in_lds_matches_streamed(gpu, monkeypatch, ss, kp, B, dt
         np.testing.assert_array_equal(h, v)
         np.testing.assert_array_equal(rh, v)
     assert_pcg_parity(inp, ss, kp, max_iters, rel, abs_tol, got, dtype)
+
+
+@pytest.mark.parametrize("ss,kp,dtype,flag", [
+    (21, 40, np.float32, None),           # S in registers, Pinv streamed, chunks pinned
+    (21, 64, np.float32, None),
+    (21, 64, np.float32, "block_diagonal"),   # D parts gathered into LDS
+    (21, 64, np.float32, "diagonal_blocks"),  # packed D blocks in LDS
+    (14, 32, np.float64, None),           # one row per lane, no pinned chunk
+])
+def test_pcg_s_resident_status_cases(gpu, monkeypatch, ss, kp, dtype, flag):
+    """The S-resident placements through the status paths: breakdown on a
+    negative definite system and on a NaN input, rho_init = 0, max_iters = 0
+    and an exhausted max_iters, each a problem of one batch.  Statuses match
+    the oracle, and every output matches the streamed placement bit for bit
+    (the solve stops after a started load into the stage, or none)."""
+    rng = np.random.default_rng(ss * 7 + kp)
+    B = 6
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.2, dtype)
+    P = workloads.block_jacobi_pinv(D, dtype)
+    b = rng.standard_normal((B, kp * ss)).astype(dtype)
+    x0 = rng.standard_normal((B, kp * ss)).astype(dtype)
+    S[1] = -S[1]            # negative definite -> breakdown at the first step
+    b[2] = 0.0              # with x0 = 0: rho_init == 0 -> converged, 0 iterations
+    x0[2] = 0.0
+    b[3, 7] = np.nan        # NaN -> breakdown, no hang
+    inp = {"S": S, "Pinv": P, "b": b, "x0": x0}
+    kw = {"pinv_block_diagonal": flag == "block_diagonal",
+          "pinv_diagonal_blocks": flag == "diagonal_blocks"}
+    tdt = torch.float32 if dtype == np.float32 else torch.float64
+    place = gpu.pcg_batched_placement(ss, kp, tdt, **kw)
+    assert place == (gpu.PLACEMENT_S_RESIDENT if flag is None else gpu.PLACEMENT_RESIDENT)
+    prec = "f32" if dtype == np.float32 else "f64"
+    runs = {}
+    for hyb in (True, False):
+        if not hyb:
+            monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
+        for max_iters, rel, abs_tol in ((60, 1e-6, 0.0), (0, 1e-6, 0.0), (2, 0.0, 0.0),
+                                        (60, 0.0, 1e30)):
+            say("pcg ss=%d kp=%d %s flag=%s hybrid=%s max_iters=%d"
+                % (ss, kp, np.dtype(dtype).name, flag, hyb, max_iters))
+            runs[(hyb, max_iters, abs_tol)] = pcg_gpu(gpu, inp, ss, kp, max_iters, rel,
+                                                      abs_tol, **kw)
+    for key in [k for k in runs if k[0]]:
+        for u, v in zip(runs[key], runs[(False,) + key[1:]]):
+            np.testing.assert_array_equal(u, v)
+    x, it, st, _ = runs[(True, 60, 0.0)]
+    _, ito, sto, _ = oracle.pcg(x0, S, P, b, ss, kp, 60, 1e-6, 0.0, prec)
+    np.testing.assert_array_equal(st, sto)
+    assert st[1] == gpu.BREAKDOWN and it[1] == 0
+    assert st[2] == gpu.CONVERGED and it[2] == 0 and np.all(x[2] == 0)
+    assert st[3] == gpu.BREAKDOWN and it[3] == 0
+    assert np.all(np.abs(it - ito) <= 2)
+    x, it, st, _ = runs[(True, 0, 0.0)]
+    assert np.all(it == 0) and st[0] == gpu.MAX_ITERS
+    np.testing.assert_array_equal(x[0], x0[0])
+    x, it, st, _ = runs[(True, 2, 0.0)]
+    assert np.all(it[[0, 4, 5]] == 2) and np.all(st[[0, 4, 5]] == gpu.MAX_ITERS)
+    x, it, st, _ = runs[(True, 60, 1e30)]
+    assert np.all(it == 0) and np.all(st[[0, 2, 4, 5]] == gpu.CONVERGED)
