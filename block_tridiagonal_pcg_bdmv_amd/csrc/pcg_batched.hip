@@ -88,6 +88,8 @@ struct PcgArgs {
   int stage_elems;  // per-wave LDS stage, elements
   int npin;         // HYBRID streaming: waves below npin keep their last Pinv
                     // chunk pinned in LDS (loaded once)
+  int regpin;       // HYBRID streaming: a wave without a last chunk keeps its
+                    // chunk 0 of Pinv in the registers that leaves free
   int ppacked;      // Pinv is packed D blocks, [kp*ss][ss] per problem (read
                     // by kStream; the other modes fix it at compile time)
 };
@@ -172,6 +174,17 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // stream.  Host: RPT >= 2 and the slots fit in LDS.
   const bool pin_last = HYBS && wave < a.npin;  // wave-uniform
   T* pinned = reinterpret_cast<T*>(smem_raw + head) + (size_t)(NW + wave) * a.stage_elems;
+  // HYBS: a wave with chunk 0 but no chunk at k = RPT-1 keeps the Pinv rows
+  // of its chunk 0 in the S registers that position leaves unused (loaded
+  // once); only its chunks in between stream.
+  const bool preg = HYBS && a.regpin != 0 && RPT >= 2 && (wave + (RPT - 1) * NW) * 64 >= n &&
+                    wave * 64 < n;  // wave-uniform
+  // Positions k of the wave's chunk sequence that do not stream through the
+  // stage: the LDS-pinned last chunk, and for preg waves chunk 0 and the
+  // positions past the wave's chunks.
+  auto no_stream = [&](int k) {
+    return (pin_last && k == RPT - 1) || (preg && (k == 0 || (wave + k * NW) * 64 >= n));
+  };
   // HYBP: the problem's packed Pinv D blocks, [n][ss], after the head.
   T* pinv_lds = reinterpret_cast<T*>(smem_raw + head);
 
@@ -263,6 +276,13 @@ pcg_batched_kernel(PcgArgs<T> a) {
           if constexpr (RES) load_row_regs<T, WCP, false>(mP[k], gP + offP);
         }
       }
+    }
+  }
+  if constexpr (HYBS) {
+    // preg: chunk 0's Pinv rows into the registers of the absent last chunk.
+    if (preg && valid[0]) {
+      if (vec) load_row_regs<T, WC, true>(mS[RPT - 1], gP + (long long)row[0] * WC);
+      else load_row_regs<T, WC, false>(mS[RPT - 1], gP + (long long)row[0] * WC);
     }
   }
 
@@ -393,22 +413,31 @@ pcg_batched_kernel(PcgArgs<T> a) {
         // every stage read has returned, load the next streamed chunk of the
         // sequence (chunk 0 of the next matvec after the last) into it.
         const bool from_pin = pin_last && k == RPT - 1;  // wave-uniform
-        if (!from_pin) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const bool from_reg = preg && k == 0;             // wave-uniform
+        const bool streamed = !no_stream(k);
+        if (streamed) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (chunk_r0(k) < n) {  // wave-uniform
           if (valid[k]) {
-            const T* __restrict__ m = (from_pin ? pinned : stage) + lane * W;
             const T* __restrict__ w = vpad + wstart[k];
-#pragma unroll 3
-            for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
+            if (from_reg) {
 #pragma unroll
-              for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], w[c], acc);
+              for (int c = 0; c < WC; ++c) acc = fma(mS[RPT - 1][c], w[c], acc);
+            } else {
+              const T* __restrict__ m = (from_pin ? pinned : stage) + lane * W;
+#pragma unroll 3
+              for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
+#pragma unroll
+                for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], w[c], acc);
+              }
             }
           }
-          if (!from_pin) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          if (streamed) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
-        if (!from_pin) {
-          int next = (k + 1) % RPT;
-          if (pin_last && next == RPT - 1) next = 0;
+        if (streamed) {
+          int next = k;  // the next streamed position (at worst k itself)
+          do {
+            next = next + 1 == RPT ? 0 : next + 1;
+          } while (no_stream(next));
           dma_chunk(next);
         }
       } else if constexpr (HYBP) {
@@ -517,7 +546,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
     ring_load(0);
     if (kRingDepth == 2) ring_load(1 % (2 * RPT));
   }
-  dma_chunk(0);
+  if constexpr (HYBS) {
+    int first = 0;
+    while (first < RPT && no_stream(first)) ++first;
+    if (first < RPT) dma_chunk(first);
+  }
   if (pin_last) dma_chunk_to(RPT - 1, pinned);
   dma_pinv_whole();
 #pragma unroll
@@ -624,6 +657,7 @@ struct Plan {
   bool prefetch = false;
   bool hyb = false;  // S resident, Pinv streamed by direct loads into LDS
   int npin = 0;      // waves whose last Pinv chunk stays pinned in LDS
+  bool regpin = false;  // waves without a last chunk hold chunk 0 of Pinv in registers
   int stage_elems = 0;
   size_t lds = 0;
 };
@@ -717,10 +751,30 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
   // its D blocks held whole in LDS, packed or under the block-diagonal
   // hint): the fewest rows per lane whose workgroup and LDS fit.
   if (hybrid) {
+    const bool pin_ok = std::getenv("GLASS_AMD_PCG_NO_PIN") == nullptr;
     for (int rpt = 1; rpt <= 3; ++rpt) {
       if (rpt * 3 * ss * (int)sizeof(T) / 4 > 192) break;
-      const int NW = (nchunks + rpt - 1) / rpt;
+      int NW = (nchunks + rpt - 1) / rpt;
       if (NW * 64 > max_threads_for(rpt, kHybrid)) continue;
+      // Streaming a general Pinv with several chunks per wave: one wave
+      // more leaves some waves without a last chunk, whose registers then
+      // hold a Pinv chunk; take it when that pins more chunks in all (LDS
+      // slots below plus those registers).
+      auto pins = [&](int nw) {
+        const size_t used = lds_bytes<T>(ss, kp, nw, prefetch_stage_elems<T>(ss));
+        if (used > lds_max) return -1;
+        const size_t slot = (size_t)prefetch_stage_elems<T>(ss) * sizeof(T);
+        int have_last = 0, reg = 0;
+        for (int w = 0; w < nw; ++w) {
+          const bool last = (w + (rpt - 1) * nw) * 64 < n;
+          have_last += last ? 1 : 0;
+          reg += !last && w * 64 < n ? 1 : 0;
+        }
+        return std::min<int>(have_last, (int)((lds_max - used) / slot)) + reg;
+      };
+      if (!pinv_diag && pin_ok && rpt >= 2 && (NW + 1) * 64 <= max_threads_for(rpt, kHybrid) &&
+          NW * 64 < n && pins(NW + 1) > pins(NW))
+        NW = NW + 1;
       // D blocks in LDS: n*ss elements in whole 1 KB pieces.
       const size_t dbytes = ((size_t)n * ss * sizeof(T) + 1023) & ~(size_t)1023;
       const int stage = pinv_diag ? 0 : prefetch_stage_elems<T>(ss);
@@ -736,7 +790,8 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       p.lds = lds;
       // Streaming Pinv with several chunks per wave: the LDS left over pins
       // the last chunk of as many waves as fit (of those that have one).
-      if (!pinv_diag && rpt >= 2 && std::getenv("GLASS_AMD_PCG_NO_PIN") == nullptr) {
+      if (!pinv_diag && rpt >= 2 && pin_ok) {
+        p.regpin = true;
         const size_t slot = (size_t)stage * sizeof(T);
         int have_last = 0;
         for (int w = 0; w < NW; ++w) have_last += (w + (rpt - 1) * NW) * 64 < n ? 1 : 0;
@@ -971,6 +1026,7 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.vec = vec;
   a.stage_elems = pl.stage_elems;
   a.npin = pl.npin;
+  a.regpin = pl.regpin ? 1 : 0;
   a.ppacked = pinv_packed ? 1 : 0;
   switch (ss) {
     case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
@@ -1011,6 +1067,11 @@ int pinned_rows_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_
   for (int w = 0; w < pl.npin; ++w) {
     const long long r0 = (long long)(w + (pl.RPT - 1) * pl.NW) * 64;
     rows += (int)std::min<long long>(64, n - r0);
+  }
+  if (pl.regpin && pl.RPT >= 2) {  // chunk 0 of waves without a last chunk
+    for (int w = 0; w < pl.NW; ++w)
+      if ((long long)(w + (pl.RPT - 1) * pl.NW) * 64 >= n && (long long)w * 64 < n)
+        rows += (int)std::min<long long>(64, n - (long long)w * 64);
   }
   return rows;
 }

@@ -193,9 +193,12 @@ def test_pcg_placement_query_matches_the_workloads(gpu, monkeypatch):
         gpu.PLACEMENT_STREAMED
     assert gpu.pcg_batched_placement(21, 64, torch.float32, pinv_block_diagonal=True) == \
         gpu.PLACEMENT_RESIDENT
-    # the LDS left over pins the last chunk (64 rows) of two waves at ss=21
-    assert gpu.pcg_batched_pinned_rows(21, 64, torch.float32) == 128
-    assert gpu.pcg_batched_pinned_rows(21, 40, torch.float32) == 128
+    # ss=21 kp=64 (21 chunks of 64 rows, 3 per wave): with 8 waves, the LDS
+    # left over pins the last chunk of wave 0, and waves 5-7, which have no
+    # third chunk, hold their chunk 0 of Pinv in those registers: 4 chunks.
+    assert gpu.pcg_batched_pinned_rows(21, 64, torch.float32) == 256
+    # kp=40 (14 chunks, 2 per wave, 8 waves): one LDS slot, waves 6 and 7
+    assert gpu.pcg_batched_pinned_rows(21, 40, torch.float32) == 192
     assert gpu.pcg_batched_pinned_rows(14, 32, torch.float64) == 0  # one row per lane
     assert gpu.pcg_batched_pinned_rows(14, 32, torch.float32) == 0  # resident
     monkeypatch.setenv("GLASS_AMD_PCG_NO_PIN", "1")
