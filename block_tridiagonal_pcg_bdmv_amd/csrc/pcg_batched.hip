@@ -32,7 +32,14 @@
 //   sequence (chunks of S, then of Pinv, then of S, ...) are loaded into
 //   registers ahead of use, so they stay in flight across the multiply, the
 //   dots and the workgroup barriers (matrix loads never depend on the
-//   vectors).
+//   vectors);
+//   S RESIDENT (HYBRID) -- when S and Pinv rows do not fit the registers
+//   together: each lane holds its S rows in VGPRs for the whole solve, and
+//   Pinv goes memory -> LDS with direct buffer -> LDS loads, which hold no
+//   registers in flight.  A general Pinv streams through a per-wave stage
+//   one chunk ahead (some chunks pinned on chip: in LDS left over after the
+//   stages, or in the S registers of waves without a last chunk); a
+//   block-Jacobi Pinv's D blocks are loaded whole into LDS once.
 // Barriers per iteration: 4 (p^T Sp, r publish, r^T z, p publish).
 //
 // RESIDENT with a block-diagonal Pinv (the caller asserts its L and R blocks
