@@ -71,10 +71,18 @@
 #define GLASS_AMD_RING_DEPTH 1
 #endif
 
+// S rows of the streamed S-resident placement: 1 = each wave's chunks are
+// loaded coalesced into its LDS stage by direct loads, then copied into
+// registers; 0 = loaded per lane straight into registers.
+#ifndef GLASS_AMD_HYB_S_VIA_LDS
+#define GLASS_AMD_HYB_S_VIA_LDS 1
+#endif
+
 namespace glass {
 namespace {
 
 constexpr int kRingDepth = GLASS_AMD_RING_DEPTH;
+constexpr bool kSViaLds = GLASS_AMD_HYB_S_VIA_LDS != 0;
 static_assert(kRingDepth == 1 || kRingDepth == 2, "ring depth must be 1 or 2");
 
 template <typename T>
@@ -268,7 +276,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
         for (int c = 0; c < WCP; ++c) mP[k][c] = T(0);
       }
-      if (valid[k]) {
+      if (valid[k] && !(HYBS && kSViaLds)) {
         const long long off = (long long)row[k] * WC;
         // The D part starts ss elements into the row: at (3*row + 1) times
         // its own byte size, so the widths load_row_regs picks stay aligned.
@@ -300,12 +308,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // every vector of a chunk the wave does not have, write zeros without a
   // fetch.  The loads use no registers once issued, so the next chunk is in
   // flight while the wave multiplies, reduces and waits at barriers.
-  auto dma_chunk_to = [&](int k, T* dst) {
+  auto dma_rows_to = [&](const T* __restrict__ gM, int k, T* dst) {
     if constexpr (HYBS) {
       const int r0 = chunk_r0(k);
       const bool has = r0 < n;
       const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gP + (long long)r0 * W : gP, nbytes);
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gM + (long long)r0 * W : gM, nbytes);
       unsigned char* st = reinterpret_cast<unsigned char*>(dst);
 #pragma unroll
       for (int u = 0; u < NV; ++u)
@@ -314,6 +322,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
             (lane + u * kWave) * 16, 0, 0, 0);
     }
   };
+  auto dma_chunk_to = [&](int k, T* dst) { dma_rows_to(gP, k, dst); };
   auto dma_chunk = [&](int k) { dma_chunk_to(k, stage); };
 
   // HYBP: every wave loads pieces q = wave, wave + NW, ... of the problem's
@@ -552,6 +561,23 @@ pcg_batched_kernel(PcgArgs<T> a) {
   if constexpr (PFM) {
     ring_load(0);
     if (kRingDepth == 2) ring_load(1 % (2 * RPT));
+  }
+  if constexpr (HYBS && kSViaLds) {
+    // S chunks through the stage: coalesced direct loads, then each lane
+    // copies its row into registers.
+#pragma unroll
+    for (int k = 0; k < RPT; ++k) {
+      if (chunk_r0(k) < n) {  // wave-uniform
+        dma_rows_to(gS, k, stage);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (valid[k]) {
+          const T* __restrict__ m = stage + lane * W;
+#pragma unroll
+          for (int c = 0; c < WC; ++c) mS[k][c] = m[c];
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
+    }
   }
   if constexpr (HYBS) {
     int first = 0;
