@@ -273,6 +273,6 @@ const char* glass_status_string(int status) {
 
 const char* glass_last_error(void) { return glass::last_error_text(); }
 
-int glass_version(void) { return 100; }
+int glass_version(void) { return 200; }
 
 }  // extern "C"

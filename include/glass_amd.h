@@ -270,7 +270,8 @@ int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
 const char* glass_status_string(int status);
 /* Text describing the last failing call on this host thread ("" if none). */
 const char* glass_last_error(void);
-/* Library ABI version (major*10000 + minor*100 + patch). */
+/* Library ABI version (major*10000 + minor*100 + patch).  0.2.0 added
+ * glass_pcg_batched_pinned_rows and GLASS_PLACEMENT_S_RESIDENT. */
 int glass_version(void);
 
 #ifdef __cplusplus

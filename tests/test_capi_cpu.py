@@ -47,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings_and_version(lib):
     assert lib.glass_status_string(0) == b"ok"
     assert lib.glass_status_string(-4).startswith(b"cooperative")
-    assert lib.glass_version() >= 100
+    assert lib.glass_version() >= 200
 
 
 FAKE = ctypes.c_void_p(0x100000)  # aligned, never dereferenced: checks fail first
