@@ -301,13 +301,14 @@ pcg_batched_kernel(PcgArgs<T> a) {
     }
   }
 
-  // HYBRID: Pinv chunk k of this wave, loaded straight into the wave's LDS
-  // stage in the coalesced order (lane l's 16-byte vectors l, l+64, ...
-  // land at the same offsets as in memory, so the stage has the chunk's
-  // layout).  The resource spans exactly the chunk; vectors past its end, or
-  // every vector of a chunk the wave does not have, write zeros without a
-  // fetch.  The loads use no registers once issued, so the next chunk is in
-  // flight while the wave multiplies, reduces and waits at barriers.
+  // HYBRID: chunk k of this wave's rows of a matrix (Pinv, or S once at the
+  // start), loaded straight into LDS at dst in the coalesced order (lane l's
+  // 16-byte vectors l, l+64, ... land at the same offsets as in memory, so
+  // dst has the chunk's layout).  The resource spans exactly the chunk;
+  // vectors past its end, or every vector of a chunk the wave does not have,
+  // write zeros without a fetch.  The loads use no registers once issued, so
+  // the next Pinv chunk is in flight while the wave multiplies, reduces and
+  // waits at barriers.
   auto dma_rows_to = [&](const T* __restrict__ gM, int k, T* dst) {
     if constexpr (HYBS) {
       const int r0 = chunk_r0(k);
@@ -424,10 +425,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
           }
         }
       } else if constexpr (HYBS) {
-        // Pinv chunk k is pinned, or in (or on its way to) the stage.  For
-        // the stage: wait for this wave's direct loads, multiply, and once
-        // every stage read has returned, load the next streamed chunk of the
-        // sequence (chunk 0 of the next matvec after the last) into it.
+        // Pinv chunk k is pinned in LDS, held in registers (preg waves'
+        // chunk 0), or in (or on its way to) the stage.  For the stage: wait
+        // for this wave's direct loads, multiply, and once every stage read
+        // has returned, load the next streamed chunk of the sequence (the
+        // first one of the next matvec after the last) into it.
         const bool from_pin = pin_last && k == RPT - 1;  // wave-uniform
         const bool from_reg = preg && k == 0;             // wave-uniform
         const bool streamed = !no_stream(k);
