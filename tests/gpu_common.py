@@ -9,6 +9,16 @@ Tolerances (stated here once, used by every GPU test):
   x within relative L2 1e-4 (float32) / 1e-10 (float64) of the float64 oracle
   run for exactly the GPU's iteration count; the returned last r^T z meets
   the stopping criterion whenever the status says converged.
+* PCG stopping point, independent of the kernel's own scalars: from the
+  returned x, r = b - S x and z = Pinv r are recomputed in float64 by the
+  oracle's matvec, and for every converged problem that took k >= 1
+  iterations |r^T z| < CRIT_SLACK * thresh, with thresh = abs_tol + rel_tol *
+  |rho_init| from the float64 oracle; and the float64 oracle stopped after
+  k - 1 iterations has |r^T z| >= thresh / CRIT_SLACK (the kernel did not
+  run on past the point where the criterion was first met by a wide margin).
+  CRIT_SLACK covers the difference between the kernel's recurrence residual
+  (rounded in its precision) and the true one, and the +-2 iteration slack:
+  4 for float32, 2 for float64.
 """
 
 import sys
@@ -20,6 +30,7 @@ import oracle
 
 BDMV_REL = 1e-5
 X_REL = {np.float32: 1e-4, np.float64: 1e-10}
+CRIT_SLACK = {np.float32: 4.0, np.float64: 2.0}
 
 
 def say(msg):
@@ -75,6 +86,21 @@ def pcg_gpu(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, x0=None, pinv_block
     return x.cpu().numpy(), iters.cpu().numpy(), status.cpu().numpy(), rho.cpu().numpy()
 
 
+def true_rz(S, P, b, x, ss, kp, nthreads=8):
+    """r^T z per problem with r = b - S x and z = Pinv r, all in float64 by
+    the oracle's matvec (padded vectors with zero pads)."""
+    B = b.shape[0]
+    n = kp * ss
+    xp = np.zeros((B, (kp + 2) * ss))
+    xp[:, ss:ss + n] = np.asarray(x, np.float64).reshape(B, n)
+    sx = oracle.bdmv(S, xp, ss, kp, "f64", nthreads=nthreads)[:, ss:ss + n]
+    r = np.asarray(b, np.float64).reshape(B, n) - sx
+    rp = np.zeros_like(xp)
+    rp[:, ss:ss + n] = r
+    z = oracle.bdmv(P, rp, ss, kp, "f64", nthreads=nthreads)[:, ss:ss + n]
+    return np.einsum("ij,ij->i", r, z)
+
+
 def assert_pcg_parity(inp, ss, kp, max_iters, rel_tol, abs_tol, result, dtype,
                       nthreads=8, x0=None):
     """x / iters / status / rho from the GPU against the oracle."""
@@ -101,4 +127,29 @@ def assert_pcg_parity(inp, ss, kp, max_iters, rel_tol, abs_tol, result, dtype,
         den = np.maximum(np.linalg.norm(xr, axis=1), 1e-300)
         worst = float((num / den).max())
         assert worst <= tol, "x relative L2 error %g > %g at %d iterations" % (worst, tol, k)
+    # the stopping point, from the returned x (see the module docstring)
+    slack = CRIT_SLACK[dtype]
+    rho_init64 = np.abs(true_rz(inp["S"], inp["Pinv"], inp["b"], x0, ss, kp, nthreads))
+    thresh64 = abs_tol + rel_tol * rho_init64
+    chk = np.nonzero(conv & (itg >= 1))[0]
+    if chk.size:
+        rz = np.abs(true_rz(inp["S"][chk], inp["Pinv"][chk], inp["b"][chk], xg[chk], ss, kp,
+                            nthreads))
+        ratio = rz / thresh64[chk]
+        assert np.all(ratio < slack), \
+            "true |r^T z| over %g x the criterion: worst ratio %g" % (slack, float(ratio.max()))
+        worst_before = np.inf
+        for k in np.unique(itg[chk]):
+            sel = chk[itg[chk] == k]
+            xm, _, _, _ = oracle.pcg(x0[sel], inp["S"][sel], inp["Pinv"][sel], inp["b"][sel],
+                                     ss, kp, int(k) - 1, 0.0, 0.0, "f64", nthreads)
+            rzm = np.abs(true_rz(inp["S"][sel], inp["Pinv"][sel], inp["b"][sel], xm, ss, kp,
+                                 nthreads))
+            before = rzm / thresh64[sel]
+            worst_before = min(worst_before, float(before.min()))
+            assert np.all(before >= 1.0 / slack), \
+                "criterion already met %g x over at one iteration fewer than the GPU's %d" % (
+                    float(before.min()), k)
+        say("  stopping point: true |r^T z| / thresh <= %.3g at the GPU's x, >= %.3g one "
+            "iteration earlier" % (float(ratio.max()), worst_before))
     return itg

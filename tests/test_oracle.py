@@ -526,3 +526,48 @@ def test_bdsv_f32_close_to_f64():
     x64, _ = oracle.bdsv(inp["S"].astype(np.float64), inp["b"].astype(np.float64), w.ss, w.kp)
     rel = np.linalg.norm(x32 - x64, axis=1) / np.linalg.norm(x64, axis=1)
     assert rel.max() < 1e-5
+
+
+def test_pcg_exact_inverse_in_strip_form_one_iteration():
+    """kp = 2: S^-1 is a full 2x2 block matrix, which the [L|D|R] layout holds
+    exactly (row 0: [0 | X00 | X01], row 1: [X10 | X11 | 0]).  With Pinv =
+    S^-1, z0 = S^-1 r0 = x* - x0, so alpha = 1 and PCG lands on x* after one
+    iteration.  A Pinv whose L or R part were read at the wrong place,
+    transposed, or dropped would not."""
+    rng = np.random.default_rng(123)
+    ss, kp, B = 3, 2, 4
+    S, _ = workloads.random_spd_strips(rng, B, ss, kp, 0.3)
+    P = np.zeros_like(S)
+    for q in range(B):
+        X = np.linalg.inv(oracle.dense_expand(S[q], ss, kp))
+        P[q, 0, :, ss:2 * ss] = X[:ss, :ss]
+        P[q, 0, :, 2 * ss:] = X[:ss, ss:]
+        P[q, 1, :, :ss] = X[ss:, :ss]
+        P[q, 1, :, ss:2 * ss] = X[ss:, ss:]
+    b = rng.standard_normal((B, kp * ss))
+    x0 = rng.standard_normal((B, kp * ss))
+    x, it, st, _ = oracle.pcg(x0, S, P, b, ss, kp, 10, 1e-20, 0.0)
+    assert np.all(it == 1) and np.all(st == oracle.CONVERGED), (it, st)
+    for q in range(B):
+        A = oracle.dense_expand(S[q], ss, kp)
+        np.testing.assert_allclose(x[q], np.linalg.solve(A, b[q]), rtol=1e-10, atol=1e-12)
+
+
+@pytest.mark.parametrize("ss,kp", [(2, 4), (5, 6)])
+def test_pcg_block_tridiagonal_pinv_matches_dense_solve(ss, kp):
+    """With the SPD block-tridiagonal preconditioner of the generator (non-zero
+    L/R blocks), PCG converges to the dense solution, in no more iterations
+    than with block Jacobi (a better preconditioner: Pinv S ~ I - F^2)."""
+    rng = np.random.default_rng(ss * 5 + kp)
+    B = 4
+    S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.2)
+    P = workloads.block_tridiagonal_pinv(S, D)
+    Pj = workloads.block_jacobi_pinv(D)
+    b = rng.standard_normal((B, kp * ss))
+    x, it, st, _ = oracle.pcg(np.zeros_like(b), S, P, b, ss, kp, 100, 1e-26, 0.0)
+    _, itj, _, _ = oracle.pcg(np.zeros_like(b), S, Pj, b, ss, kp, 100, 1e-26, 0.0)
+    assert np.all(st == oracle.CONVERGED)
+    assert np.all(it <= itj), (it, itj)
+    for q in range(B):
+        A = oracle.dense_expand(S[q], ss, kp)
+        np.testing.assert_allclose(x[q], np.linalg.solve(A, b[q]), rtol=1e-10, atol=1e-12)

@@ -61,3 +61,57 @@ def test_config_table_matches_stated_workloads():
     assert (c[2].ss, c[2].kp, c[2].n_problems, c[2].margin) == (14, 32, 4096, 0.2)
     assert (c[3].ss, c[3].kp, c[3].n_problems, c[3].max_iters) == (21, 64, 2048, 500)
     assert (c[4].ss, c[4].kp, c[4].dtype, c[4].rel_tol) == (12, 8192, np.float64, 1e-10)
+
+
+@pytest.mark.parametrize("ss,kp,margin", [(2, 5, 0.3), (6, 8, 0.1), (14, 4, 0.2), (3, 1, 0.5)])
+def test_tridiagonal_pinv_is_the_dense_first_order_inverse_and_spd(ss, kp, margin):
+    """pinv="tridiagonal": built from its definition with dense matrices
+    (Pinv = D^-1 - D^-1 E D^-1, D the block diagonal of the expanded S, E the
+    rest), symmetric, positive definite, non-zero L/R blocks for kp > 1, zero
+    off-matrix blocks, and a better preconditioner than block Jacobi
+    (condition number of Pinv S no larger)."""
+    rng = np.random.default_rng(ss * 31 + kp)
+    S, D = workloads.random_spd_strips(rng, 2, ss, kp, margin)
+    P = workloads.block_tridiagonal_pinv(S, D)
+    Pj = workloads.block_jacobi_pinv(D)
+    assert np.all(P[:, 0, :, :ss] == 0) and np.all(P[:, -1, :, 2 * ss:] == 0)
+    if kp > 1:
+        assert np.abs(P[:, 1:, :, :ss]).min(axis=(2, 3)).max() > 0
+        assert np.all(np.abs(P[:, :-1, :, 2 * ss:]).sum(axis=(2, 3)) > 0)
+    n = kp * ss
+    for q in range(2):
+        A = oracle.dense_expand(S[q], ss, kp)
+        Dd = np.zeros_like(A)
+        for br in range(kp):
+            sl = slice(br * ss, (br + 1) * ss)
+            Dd[sl, sl] = A[sl, sl]
+        E = A - Dd
+        Di = np.linalg.inv(Dd)
+        M = oracle.dense_expand(P[q], ss, kp)
+        np.testing.assert_allclose(M, Di - Di @ E @ Di, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(M, M.T, rtol=0, atol=1e-15)
+        lam = np.linalg.eigvalsh(M)
+        assert lam[0] > 0, lam[0]
+        # Pinv S is similar to I - F^2 with F = D^-1/2 E D^-1/2: eigenvalues in (0, 1]
+        ev = np.sort(np.linalg.eigvals(M @ A).real)
+        assert ev[0] > 0 and ev[-1] <= 1 + 1e-12
+        evj = np.sort(np.linalg.eigvals(oracle.dense_expand(Pj[q], ss, kp) @ A).real)
+        assert ev[-1] / ev[0] <= evj[-1] / evj[0] * (1 + 1e-9)
+        assert M.shape == (n, n)
+
+
+def test_generate_tridiagonal_pinv_option():
+    """The option changes only Pinv: S, b and x0 are the same draws, Pinv's D
+    blocks are the block-Jacobi inverse and its L/R blocks are not zero."""
+    from dataclasses import replace
+    w = workloads.WORKLOADS[2]
+    a = workloads.generate(w, n_problems=3)
+    b = workloads.generate(replace(w, pinv="tridiagonal"), n_problems=3)
+    for k in ("S", "b", "x0"):
+        np.testing.assert_array_equal(a[k], b[k])
+    ss = w.ss
+    np.testing.assert_array_equal(a["Pinv"][..., ss:2 * ss], b["Pinv"][..., ss:2 * ss])
+    assert np.count_nonzero(b["Pinv"][:, :, :, 2 * ss:]) > 0
+    assert np.count_nonzero(b["Pinv"][:, 1:, :, :ss]) > 0
+    with pytest.raises(ValueError):
+        workloads.generate(replace(w, pinv="nonsense"), n_problems=1)

@@ -26,6 +26,17 @@ blocks) plus ``margin``.  By Gershgorin every eigenvalue is at least
 Pinv is block-Jacobi: its D part is inv(D_br) computed in float64 and
 symmetrised, its L/R parts are zero.  x0 = 0.  Everything is formed in float64
 and rounded once to the workload dtype.
+
+Preconditioner option ``pinv="tridiagonal"`` (the same page lets Pinv be any
+block-tridiagonal matrix in [L|D|R] form; this choice is ours): the
+first-order Neumann approximation of S^-1 about its block diagonal,
+    Pinv = D^-1 - D^-1 E D^-1,   E = the L and R blocks of S,
+so Pinv's D blocks are inv(D_br), its R blocks -inv(D_br) R_br inv(D_br+1) and
+its L blocks the transposes of the R blocks of the row above.  With
+F = D^-1/2 E D^-1/2, Pinv = D^-1/2 (I - F) D^-1/2.  F is block-tridiagonal
+with zero diagonal blocks (2-cyclic), so its spectrum is symmetric about 0;
+S = D^1/2 (I + F) D^1/2 SPD means every eigenvalue of F exceeds -1, hence
+all lie in (-1, 1) and Pinv is SPD too.  Pinv S is similar to I - F^2.
 """
 
 from __future__ import annotations
@@ -48,6 +59,7 @@ class Workload:
     abs_tol: float = 0.0
     max_iters: int = 0
     seed: int = 0
+    pinv: str = "block_jacobi"   # or "tridiagonal" (see the module docstring)
 
     @property
     def n(self) -> int:
@@ -126,11 +138,16 @@ def generate(w: Workload, n_problems: int | None = None, with_pinv: bool | None 
         S, D = _assemble(R, U, ss, kp, w.margin)
         S_out[lo:hi] = S
         if with_pinv:
-            inv = np.linalg.inv(D)
-            inv = 0.5 * (inv + np.swapaxes(inv, -1, -2))
-            P = np.zeros_like(S)
-            P[:, :, :, ss:2 * ss] = inv
-            P_out[lo:hi] = P
+            if w.pinv == "tridiagonal":
+                P_out[lo:hi] = _tridiagonal_pinv64(S, D)
+            elif w.pinv == "block_jacobi":
+                inv = np.linalg.inv(D)
+                inv = 0.5 * (inv + np.swapaxes(inv, -1, -2))
+                P = np.zeros_like(S)
+                P[:, :, :, ss:2 * ss] = inv
+                P_out[lo:hi] = P
+            else:
+                raise ValueError("unknown preconditioner %r" % (w.pinv,))
         if w.kind == "bdmv":
             vec_out[lo:hi, ss:(kp + 1) * ss] = g
         else:
@@ -174,3 +191,42 @@ def block_jacobi_pinv(D: np.ndarray, dtype=np.float64) -> np.ndarray:
     P = np.zeros((B, kp, ss, 3 * ss), dtype=np.float64)
     P[:, :, :, ss:2 * ss] = inv
     return P.astype(dtype)
+
+
+def _tridiagonal_pinv64(S: np.ndarray, D: np.ndarray) -> np.ndarray:
+    """Float64 strips of Pinv = D^-1 - D^-1 E D^-1 (module docstring) for
+    float64 strips S [B, kp, ss, 3ss] with D blocks D [B, kp, ss, ss]."""
+    B, kp, ss, _ = D.shape
+    inv = np.linalg.inv(D)
+    inv = 0.5 * (inv + np.swapaxes(inv, -1, -2))
+    P = np.zeros((B, kp, ss, 3 * ss), dtype=np.float64)
+    P[:, :, :, ss:2 * ss] = inv
+    if kp > 1:
+        R = S[:, :-1, :, 2 * ss:]
+        PR = -np.matmul(np.matmul(inv[:, :-1], R), inv[:, 1:])
+        P[:, :-1, :, 2 * ss:] = PR
+        P[:, 1:, :, :ss] = np.swapaxes(PR, -1, -2)
+    return P
+
+
+def block_tridiagonal_pinv(S: np.ndarray, D: np.ndarray, dtype=np.float64) -> np.ndarray:
+    """The SPD block-tridiagonal preconditioner of ``pinv="tridiagonal"``
+    (non-zero L and R blocks) for strips S built by ``random_spd_strips`` /
+    ``generate`` (symmetric, L_{br+1} = R_br^T) and their float64 D blocks."""
+    return _tridiagonal_pinv64(np.asarray(S, np.float64), np.asarray(D, np.float64)).astype(dtype)
+
+
+def laplacian_coupled_strips(S: np.ndarray, scale: float) -> np.ndarray:
+    """A stiffer SPD system for long solves: scale * S plus the block 1-D
+    Laplacian tridiag(-I, 2I, -I) (positive semidefinite, eigenvalues
+    2 - 2 cos(k pi / (kp+1)) > 0), so the sum stays symmetric positive
+    definite while its condition number grows as scale shrinks.  S: strips
+    [B, kp, ss, 3ss] of a symmetric S; returns float64 strips."""
+    S = scale * np.asarray(S, np.float64)
+    ss = S.shape[2]
+    eye = np.eye(ss)
+    S[:, :, :, ss:2 * ss] += 2.0 * eye
+    if S.shape[1] > 1:
+        S[:, :-1, :, 2 * ss:] -= eye
+        S[:, 1:, :, :ss] -= eye
+    return S
