@@ -18,7 +18,7 @@ import threading
 
 __all__ = [
     "GlassError", "load", "library_path", "bdmv_batched", "pcg_batched",
-    "pcg_grid", "pcg_grid_workspace_bytes", "bdsv_batched", "bdsv_workspace_bytes",
+    "pcg_grid", "pcg_grid_workspace_bytes", "pcg_grid_noalloc", "bdsv_batched", "bdsv_workspace_bytes",
     "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
     "PCG_PINV_BLOCK_DIAGONAL", "PCG_PINV_DIAGONAL_BLOCKS", "GRID_SINGLE_REDUCTION",
@@ -76,6 +76,7 @@ def load():
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
+            "glass_pcg_grid_noalloc": ([P, P, P, P, I, I, I, D, D, P, P, P, I, U, P], I),
             "glass_status_string": ([I], ctypes.c_char_p),
             "glass_last_error": ([], ctypes.c_char_p),
             "glass_version": ([], I),
@@ -283,3 +284,28 @@ def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
                                   | (GRID_SINGLE_REDUCTION if single_reduction else 0),
                                   _stream(stream))
     _check(rc, "glass_pcg_grid_ex")
+
+
+def pcg_grid_noalloc(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
+                     rel_tol: float, abs_tol: float, iters_out, status_out=None,
+                     rho_out=None, stream=None, exclusive=False, single_reduction=False):
+    """``pcg_grid`` without a workspace (glass_pcg_grid_noalloc): the
+    exchange area is the library's static per-device scratch, so the call
+    allocates nothing.  Calls that overlap in time on one device race."""
+    import torch
+    ss, kp = int(state_size), int(knot_points)
+    if _problems(S, ss, kp) != 1:
+        raise ValueError("pcg_grid_noalloc solves exactly one problem")
+    dt = S.dtype
+    n = kp * ss
+    a = (_dev(x, "x", n, dt), _dev(S, "S", S.numel(), dt),
+         _dev(Pinv, "Pinv", S.numel(), dt), _dev(b, "b", n, dt))
+    it = _dev(iters_out, "iters_out", 1, torch.int32)
+    st = _dev(status_out, "status_out", 1, torch.int32) if status_out is not None else None
+    rh = _dev(rho_out, "rho_out", 2, dt) if rho_out is not None else None
+    rc = load().glass_pcg_grid_noalloc(*a, ss, kp, int(max_iters), float(rel_tol),
+                                       float(abs_tol), it, st, rh, _dtype_code(S),
+                                       (GRID_EXCLUSIVE if exclusive else 0)
+                                       | (GRID_SINGLE_REDUCTION if single_reduction else 0),
+                                       _stream(stream))
+    _check(rc, "glass_pcg_grid_noalloc")

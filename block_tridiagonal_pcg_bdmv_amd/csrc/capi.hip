@@ -219,12 +219,15 @@ size_t glass_pcg_grid_workspace_bytes(int state_size, int knot_points,
   return glass::grid_workspace_bytes(state_size, knot_points, dtype);
 }
 
-int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
-                      int state_size, int knot_points, int max_iters,
-                      double rel_tol, double abs_tol, int* iters_out,
-                      int* status_out, void* rho_out, void* workspace,
-                      size_t workspace_bytes, glass_dtype dtype,
-                      unsigned flags, void* hip_stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the grid entry points (all but the workspace).
+int check_grid(void* x, const void* S, const void* Pinv, const void* b, int state_size,
+               int knot_points, int max_iters, double rel_tol, double abs_tol,
+               int* iters_out, int* status_out, void* rho_out, glass_dtype dtype,
+               unsigned flags) {
   if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
   if (flags & ~(unsigned)(GLASS_GRID_EXCLUSIVE | GLASS_GRID_SINGLE_REDUCTION))
     return fail(GLASS_EINVAL, "unknown grid flags");
@@ -237,14 +240,45 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
   if (!glass::aligned(iters_out, 4)) return fail(GLASS_EINVAL, "iters_out misaligned");
   if (status_out && !glass::aligned(status_out, 4)) return fail(GLASS_EINVAL, "status_out misaligned");
   if (rho_out && !glass::aligned(rho_out, elem_size(dtype))) return fail(GLASS_EINVAL, "rho_out misaligned");
+  return check_tols(max_iters, rel_tol, abs_tol);
+}
+
+}  // namespace
+
+extern "C" {
+
+int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
+                      int state_size, int knot_points, int max_iters,
+                      double rel_tol, double abs_tol, int* iters_out,
+                      int* status_out, void* rho_out, void* workspace,
+                      size_t workspace_bytes, glass_dtype dtype,
+                      unsigned flags, void* hip_stream) {
+  if (int rc = check_grid(x, S, Pinv, b, state_size, knot_points, max_iters, rel_tol, abs_tol,
+                          iters_out, status_out, rho_out, dtype, flags))
+    return rc;
   if (!workspace) return fail(GLASS_EINVAL, "workspace is NULL");
   if (!glass::aligned(workspace, 256)) return fail(GLASS_EINVAL, "workspace must be 256-byte aligned");
   if (workspace_bytes < glass::grid_workspace_bytes(state_size, knot_points, dtype))
     return fail(GLASS_EINVAL, "workspace smaller than glass_pcg_grid_workspace_bytes()");
-  if (int rc = check_tols(max_iters, rel_tol, abs_tol)) return rc;
   return glass::launch_pcg_grid(dtype, x, S, Pinv, b, state_size, knot_points,
                                 max_iters, rel_tol, abs_tol, iters_out,
                                 status_out, rho_out, workspace, workspace_bytes,
+                                (flags & GLASS_GRID_EXCLUSIVE) != 0,
+                                (flags & GLASS_GRID_SINGLE_REDUCTION) != 0,
+                                (hipStream_t)hip_stream);
+}
+
+int glass_pcg_grid_noalloc(void* x, const void* S, const void* Pinv, const void* b,
+                           int state_size, int knot_points, int max_iters,
+                           double rel_tol, double abs_tol, int* iters_out,
+                           int* status_out, void* rho_out, glass_dtype dtype,
+                           unsigned flags, void* hip_stream) {
+  if (int rc = check_grid(x, S, Pinv, b, state_size, knot_points, max_iters, rel_tol, abs_tol,
+                          iters_out, status_out, rho_out, dtype, flags))
+    return rc;
+  return glass::launch_pcg_grid(dtype, x, S, Pinv, b, state_size, knot_points,
+                                max_iters, rel_tol, abs_tol, iters_out,
+                                status_out, rho_out, nullptr, 0,
                                 (flags & GLASS_GRID_EXCLUSIVE) != 0,
                                 (flags & GLASS_GRID_SINGLE_REDUCTION) != 0,
                                 (hipStream_t)hip_stream);
@@ -273,6 +307,6 @@ const char* glass_status_string(int status) {
 
 const char* glass_last_error(void) { return glass::last_error_text(); }
 
-int glass_version(void) { return 200; }
+int glass_version(void) { return 300; }
 
 }  // extern "C"

@@ -52,6 +52,7 @@ int launch_bdsv(glass_dtype dt, void* x, const void* S, const void* b, int ss,
                 hipStream_t stream);
 
 size_t grid_workspace_bytes(int ss, int kp, glass_dtype dt);
+// workspace == nullptr: use the device's static scratch (no allocation).
 int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     const void* b, int ss, int kp, int max_iters,
                     double rel_tol, double abs_tol, int* iters, int* status,

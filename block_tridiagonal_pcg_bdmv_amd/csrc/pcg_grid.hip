@@ -48,6 +48,8 @@
 //   other poll stops as soon as it sees the flag, the kernel runs to its end,
 //   and the status output reports the timeout instead of the device hanging.
 #include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -100,15 +102,46 @@ struct WorkspaceLayout {
 
 inline size_t round256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-WorkspaceLayout layout(int ss, int kp, size_t elem) {
-  const size_t gmax = (size_t)std::min(kp / 2, kGridMaxWorkgroups);
+// Exchange area for a grid of G workgroups.
+WorkspaceLayout layout_for(size_t G, int ss, size_t elem) {
   const size_t words = elem / 4;
   WorkspaceLayout w;
   w.flags = 0;
   w.part = 256;
-  w.edges = w.part + round256(2 * gmax * kDotValues * words * sizeof(u64));
-  w.total = w.edges + round256(2 * gmax * 4 * (size_t)ss * words * sizeof(u64));
+  w.edges = w.part + round256(2 * G * kDotValues * words * sizeof(u64));
+  w.total = w.edges + round256(2 * G * 4 * (size_t)ss * words * sizeof(u64));
   return w;
+}
+
+// A caller's workspace is sized for the largest grid a chain of kp
+// block-rows can take, so it serves every device.
+WorkspaceLayout layout(int ss, int kp, size_t elem) {
+  return layout_for((size_t)std::min(kp / 2, kGridMaxWorkgroups), ss, elem);
+}
+
+// The exchange area of glass_pcg_grid_noalloc: one array per device that
+// holds the library's code, kept until the process ends.  Host code never
+// passes the array's name to a kernel (in host code it is only a stand-in
+// for the symbol); it passes the device address that hipGetSymbolAddress
+// returns for the current device, taken once per device.
+constexpr size_t kNoAllocScratchBytes = GLASS_PCG_GRID_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mutex;
+std::vector<void*> g_scratch_ptr;  // by device ordinal; null until first used
+
+int scratch_address(int device, void** out) {
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if ((int)g_scratch_ptr.size() <= device) g_scratch_ptr.resize(device + 1, nullptr);
+  if (!g_scratch_ptr[device]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return fail_hip(e, "hipGetSymbolAddress(grid scratch)");
+    if (!p) return fail(GLASS_EHIP, "hipGetSymbolAddress(grid scratch) returned NULL");
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return GLASS_OK;
 }
 
 // Zeroes the timeout flag and the tag words the solve will read: n1 words
@@ -755,6 +788,8 @@ int launch_grid_res(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
   return fail(GLASS_EUNSUPPORTED, "grid pcg: internal plan error");
 }
 
+// workspace == nullptr: the exchange area is this device's static scratch
+// (glass_pcg_grid_noalloc), laid out for the grid actually launched.
 template <typename T>
 int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
                 int max_iters, double rel_tol, double abs_tol, int* iters,
@@ -764,8 +799,8 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   if (int rc = current_device_info(&dev)) return rc;
   if (!dev.cooperative)
     return fail(GLASS_ECOOP, "device does not support cooperative launches");
-  const WorkspaceLayout wl = layout(ss, kp, sizeof(T));
-  if (ws_bytes < wl.total)
+  const bool own_scratch = workspace == nullptr;
+  if (!own_scratch && ws_bytes < layout(ss, kp, sizeof(T)).total)
     return fail(GLASS_EINVAL, "grid pcg: workspace too small");
   const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
   const bool res = specialised && kGridResidentFits<T>(ss);
@@ -792,6 +827,16 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   const size_t lds = (2 * loc_len + 8 * (size_t)ss + (size_t)kDotValues * (NW + 1)) * sizeof(T);
   if (lds > dev.max_lds_per_block)
     return fail(GLASS_EUNSUPPORTED, "grid pcg: partition does not fit in LDS");
+  WorkspaceLayout wl = layout(ss, kp, sizeof(T));
+  if (own_scratch) {
+    wl = layout_for((size_t)G, ss, sizeof(T));
+    if (wl.total > kNoAllocScratchBytes)
+      return fail(GLASS_EUNSUPPORTED,
+                  "grid pcg (no-alloc): " + std::to_string(G) + " workgroups need " +
+                      std::to_string(wl.total) + " bytes of exchange area, more than the " +
+                      std::to_string(kNoAllocScratchBytes) + " bytes of static scratch");
+    if (int rc = scratch_address(dev.device, &workspace)) return rc;
+  }
 
   GridArgs<T> a;
   a.x = x;

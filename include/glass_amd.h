@@ -234,6 +234,29 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
                       unsigned flags, void* hip_stream);
 
 /*
+ * glass_pcg_grid_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments (minus workspace and
+ * workspace_bytes), flags, steps, outputs and results (bit for bit) as
+ * glass_pcg_grid_ex.  The exchange area lives in a static device array of
+ * GLASS_PCG_GRID_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
+ * device it runs on until the process ends; the call itself allocates and
+ * frees nothing.  It needs 256 + 2*G*2*w*8 + 2*G*4*state_size*w*8 bytes
+ * (G = workgroups of the grid, usually one per compute unit; w = 1 for
+ * GLASS_F32, 2 for GLASS_F64), about 0.4 MB for a 256-workgroup fp64 grid
+ * at state_size 12; a shape that needs more returns GLASS_EUNSUPPORTED with
+ * nothing launched.  Every call on one device shares that device's array:
+ * calls ordered on one stream are safe, calls that overlap in time (other
+ * streams, other host threads) race and give unspecified results.
+ */
+#define GLASS_PCG_GRID_NOALLOC_SCRATCH_BYTES 4194304
+int glass_pcg_grid_noalloc(void* x, const void* S, const void* Pinv,
+                           const void* b, int state_size, int knot_points,
+                           int max_iters, double rel_tol, double abs_tol,
+                           int* iters_out, int* status_out, void* rho_out,
+                           glass_dtype dtype, unsigned flags, void* hip_stream);
+
+/*
  * Direct solve S x = b for n_problems independent block-tridiagonal
  * symmetric positive definite systems (glass::bdsv, named in the opening
  * paragraph of page "Block-tridiagonal Solves"; layout as above).  Steps:
@@ -271,7 +294,8 @@ const char* glass_status_string(int status);
 /* Text describing the last failing call on this host thread ("" if none). */
 const char* glass_last_error(void);
 /* Library ABI version (major*10000 + minor*100 + patch).  0.2.0 added
- * glass_pcg_batched_pinned_rows and GLASS_PLACEMENT_S_RESIDENT. */
+ * glass_pcg_batched_pinned_rows and GLASS_PLACEMENT_S_RESIDENT; 0.3.0 added
+ * glass_pcg_grid_noalloc. */
 int glass_version(void);
 
 #ifdef __cplusplus

@@ -149,3 +149,20 @@ def test_pcg_ex_flag_errors(lib):
     assert ex(0x80000000) == EINVAL
     assert ex(1 | 4) == EINVAL
     assert ex(2 | 8) == EINVAL
+
+
+def test_grid_noalloc_argument_errors(lib):
+    """glass_pcg_grid_noalloc runs the grid solve's checks (no workspace
+    arguments) before anything touches a device."""
+    def na(x=FAKE, kp=8192, it=10, rel=1e-10, flags=0, iters=FAKE, dt=1, st=None):
+        return lib.glass_pcg_grid_noalloc(x, FAKE, FAKE, FAKE, 12, kp, it, rel, 0.0, iters,
+                                          st, None, dt, flags, None)
+    assert na(x=None) == EINVAL
+    assert na(kp=3) == EINVAL
+    assert na(it=-1) == EINVAL
+    assert na(rel=float("nan")) == EINVAL
+    assert na(iters=None) == EINVAL
+    assert na(st=ctypes.c_void_p(0x100002)) == EINVAL
+    assert na(dt=2) == EINVAL
+    assert na(flags=4) == EINVAL
+    assert b"flag" in lib.glass_last_error()
