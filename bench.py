@@ -146,6 +146,15 @@ def algorithmic_bytes_pcg(w, iters: np.ndarray, resident, pinv_diag=False,
     return float(np.sum(passes * (s_bytes + p_bytes) + vec))
 
 
+def compulsory_bytes_pcg(w, B: int, pinv_diag=False) -> float:
+    """Bytes every placement must move per launch: S and Pinv once (Pinv's D
+    blocks only when only they are read), x read, b read, x written, iters."""
+    es = np.dtype(w.dtype).itemsize
+    s_bytes = w.n * 3 * w.ss * es
+    p_bytes = w.n * (w.ss if pinv_diag else 3 * w.ss) * es
+    return float(B) * (s_bytes + p_bytes + 3 * w.n * es + 4)
+
+
 def algorithmic_bytes_bdmv(w, B: int) -> float:
     es = np.dtype(w.dtype).itemsize
     return float(B) * (w.n * 3 * w.ss * es + (w.kp + 2) * w.ss * es + w.n * es)
@@ -303,11 +312,24 @@ def isolated_ms(torch, fn, reps=10):
     return float(np.median([a.elapsed_time(b) for a, b in ev]))
 
 
-def roofline(nbytes, avg_ms, traffic):
+def roofline(nbytes, avg_ms, traffic, compulsory=None, served_by="hbm"):
+    """HBM roofline of a launch.  ``nbytes``: the placement's algorithmic bytes
+    (matrices that stay on chip once, re-read ones once per pass).
+    ``compulsory``: the bytes any placement must move (matrices once); its
+    fraction is reported beside the placement's.  ``served_by``: "hbm" when
+    every byte is read once, "hbm+infinity-cache" when the placement re-reads
+    a working set that the 256 MB Infinity Cache partly serves (the rate of
+    those bytes is then not an HBM rate)."""
     achieved = nbytes / (avg_ms * 1e-3) / 1e9
-    return {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-            "algorithmic_bytes_per_launch": nbytes}
+    out = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+           "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+           "algorithmic_bytes_per_launch": nbytes, "served_by": served_by}
+    if compulsory is not None:
+        ca = compulsory / (avg_ms * 1e-3) / 1e9
+        out["compulsory_bytes_per_launch"] = compulsory
+        out["compulsory_achieved"] = ca
+        out["frac_compulsory"] = ca / HBM_PEAK_GBS
+    return out
 
 
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X dense fp32 vector
@@ -326,17 +348,28 @@ def algorithmic_flops_bdsv(w) -> float:
     return kp * per_row + (kp - 1) * (2.0 * ss * ss * (ss + 1) + 2.0 * ss * ss)
 
 
+# The library is built with packed FP32 instructions disabled, so one fp32
+# vector FMA per lane per clock is its ceiling: 256 CUs x 64 FMA/clk x 2 FLOP
+# x 2.4 GHz = 78.6 TFLOP/s, half the packed 157.3.
+FP32_UNPACKED_PEAK_TFLOPS = 78.6
+
+
 def roofline_alu(flops, nbytes, avg_ms, traffic, dtype):
-    """Arithmetic-bound kernel: useful FLOP/s against the vector peak of its
-    dtype; the HBM rate of its algorithmic bytes is given beside it."""
-    peak = FP32_VECTOR_PEAK_TFLOPS if np.dtype(dtype) == np.float32 else FP64_VECTOR_PEAK_TFLOPS
+    """Arithmetic-bound kernel: useful FLOP/s against the vector peak its
+    build can reach (unpacked fp32, or fp64), with the packed fp32 figure and
+    the HBM rate of its algorithmic bytes beside it."""
+    f32 = np.dtype(dtype) == np.float32
+    peak = FP32_UNPACKED_PEAK_TFLOPS if f32 else FP64_VECTOR_PEAK_TFLOPS
     achieved = flops / (avg_ms * 1e-3) / 1e12
     gbs = nbytes / (avg_ms * 1e-3) / 1e9
-    return {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-            "frac": achieved / peak, "traffic": traffic,
-            "algorithmic_flops_per_launch": flops,
-            "algorithmic_bytes_per_launch": nbytes,
-            "hbm_achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    out = {"bound": "alu", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+           "frac": achieved / peak, "traffic": traffic,
+           "algorithmic_flops_per_launch": flops,
+           "algorithmic_bytes_per_launch": nbytes,
+           "hbm_achieved_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
+    if f32:
+        out["frac_of_packed_peak"] = achieved / FP32_VECTOR_PEAK_TFLOPS
+    return out
 
 
 def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
@@ -353,6 +386,7 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     b = torch.from_numpy(inp["b"]).to(dev)
     xs = [torch.zeros((B, w.n), dtype=S.dtype, device=dev) for _ in range(steps + warmup)]
     iters = torch.zeros(B, dtype=torch.int32, device=dev)
+    status = torch.full((B,), -1, dtype=torch.int32, device=dev)
     grid = w.kind == "grid"
     if grid:
         ws = torch.empty(glass.pcg_grid_workspace_bytes(w.ss, w.kp, S.dtype),
@@ -370,10 +404,10 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     def run(x, exclusive=True):
         if grid:
             glass.pcg_grid(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters, ws,
-                           exclusive=exclusive, single_reduction=single)
+                           status, exclusive=exclusive, single_reduction=single)
         else:
             glass.pcg_batched(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters,
-                              pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
+                              status, pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
 
     for k in range(warmup):
         run(xs[steps + k])
@@ -388,6 +422,7 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     wall = time.perf_counter() - t0
     launch_ms = tm.launch_ms()
     it = iters.cpu().numpy()
+    st = status.cpu().numpy()
     avg_ms = float(np.mean(launch_ms))
     # S and Pinv count once if they stay on chip (the grid solve and the
     # batched resident placement), else once per pass.
@@ -399,6 +434,8 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         w.ss, w.kp, S.dtype, pinv_block_diagonal=pd,
         pinv_diagonal_blocks=packed) if resident == "S" else 0
     nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed, pinned_rows=pinned)
+    compulsory = compulsory_bytes_pcg(w, B, pinv_diag=pd or packed)
+    served_by = "hbm" if resident is True else "hbm+infinity-cache"
     for k in range(min(10, len(xs))):
         xs[k].zero_()
     iso = isolated_ms(torch, lambda k: run(xs[k]), reps=min(10, len(xs)))
@@ -410,7 +447,11 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         "kernel_ms_min": float(np.min(launch_ms)),
         "kernel_ms_isolated": iso,
         "iterations": {str(k): int(v) for k, v in zip(*np.unique(it, return_counts=True))},
-        "roofline": roofline(nbytes, avg_ms, traffic.get(key)),
+        # every timed solve must have converged (a breakdown or a grid
+        # timeout would otherwise be timed as a fast valid solve)
+        "not_converged": int((st != glass.CONVERGED).sum()),
+        "valid": bool(np.all(st == glass.CONVERGED)),
+        "roofline": roofline(nbytes, avg_ms, traffic.get(key), compulsory, served_by),
     }
     if not grid:
         out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it.max()))
@@ -528,10 +569,34 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     return out
 
 
-def measured_copy_gbs(torch, nbytes=1 << 30, reps=10):
-    """Device-to-device copy rate on this GPU (torch copy of 1 GiB; read +
-    write bytes per second), the measured reference the HBM fractions are
-    also given against."""
+def measured_read_gbs(torch, glass, nbytes=1 << 30, reps=10):
+    """The device's streaming-read rate: glass_stream_read over 1 GiB (read
+    once with coalesced 16-byte non-temporal loads; median of 10).  The HBM
+    fractions are also given against it: it is the practical ceiling of a
+    read-bound kernel, which the vendor peak is not.  The checksum of the
+    read is verified."""
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        glass.stream_read(src, sink)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        glass.stream_read(src, sink)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    # 2^28 words of 1: each read buffer XORs to 0 (an even number of 1s).
+    assert int(np.bitwise_xor.reduce(sink.cpu().numpy())) == 0
+    del src, sink
+    return nbytes / (ms * 1e-3) / 1e9
+
+
+def torch_copy_gbs(torch, nbytes=1 << 30, reps=10):
+    """Device-to-device torch copy of 1 GiB (read + write bytes per second),
+    reported for context."""
     dev = torch.device("cuda:0")
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
@@ -613,12 +678,15 @@ def main():
               flush=True)
     if args.calibration_copy:
         calibration_copy(torch)
-    copy_gbs = measured_copy_gbs(torch)
+    read_gbs = measured_read_gbs(torch, glass)
+    copy_gbs = torch_copy_gbs(torch)
     for r in res.values():
         rl = r["roofline"]
         gbs = rl["achieved"] if rl["bound"] == "hbm" else rl.get("hbm_achieved_gbs")
         if gbs is not None:
-            rl["frac_of_measured_copy"] = gbs / copy_gbs
+            rl["frac_of_measured_read"] = gbs / read_gbs
+        if rl.get("compulsory_achieved") is not None:
+            rl["frac_compulsory_of_measured_read"] = rl["compulsory_achieved"] / read_gbs
 
     head = res.get("pcg3") or next(iter(res.values()))
     w = workloads.WORKLOADS[3]
@@ -635,7 +703,8 @@ def main():
                    "parallelism": "one problem per workgroup"},
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
-        "measured_copy_gbs": copy_gbs,
+        "measured_read_gbs": read_gbs,
+        "torch_copy_gbs": copy_gbs,
         "workloads": res,
     }
     print(json.dumps(line), flush=True)

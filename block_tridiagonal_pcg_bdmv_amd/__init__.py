@@ -24,7 +24,7 @@ __all__ = [
     "PCG_PINV_BLOCK_DIAGONAL", "PCG_PINV_DIAGONAL_BLOCKS", "GRID_SINGLE_REDUCTION",
     "pcg_batched_placement", "pcg_batched_pinned_rows", "PLACEMENT_RESIDENT",
     "PLACEMENT_STREAMED_PREFETCH",
-    "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT",
+    "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT", "stream_read",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +77,7 @@ def load():
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
             "glass_pcg_grid_noalloc": ([P, P, P, P, I, I, I, D, D, P, P, P, I, U, P], I),
+            "glass_stream_read": ([P, Z, P, Z, P], I),
             "glass_status_string": ([I], ctypes.c_char_p),
             "glass_last_error": ([], ctypes.c_char_p),
             "glass_version": ([], I),
@@ -309,3 +310,17 @@ def pcg_grid_noalloc(x, S, Pinv, b, state_size: int, knot_points: int, max_iters
                                        | (GRID_SINGLE_REDUCTION if single_reduction else 0),
                                        _stream(stream))
     _check(rc, "glass_pcg_grid_noalloc")
+
+
+def stream_read(src, sink, stream=None):
+    """Measurement aid (glass_stream_read): read every byte of the contiguous
+    device tensor ``src`` once; ``sink`` (int32 device tensor, zeroed by the
+    caller) receives one XOR of 32-bit words per workgroup launched."""
+    import torch
+    if not (src.is_cuda and src.is_contiguous()):
+        raise ValueError("src must be a contiguous device tensor")
+    nbytes = src.numel() * src.element_size()
+    sk = _dev(sink, "sink", sink.numel(), torch.int32)
+    rc = load().glass_stream_read(ctypes.c_void_p(src.data_ptr()), nbytes, sk, sink.numel(),
+                                  _stream(stream))
+    _check(rc, "glass_stream_read")

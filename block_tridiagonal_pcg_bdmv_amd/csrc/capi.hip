@@ -294,6 +294,16 @@ int glass_pcg_grid(void* x, const void* S, const void* Pinv, const void* b,
                            workspace, workspace_bytes, dtype, 0u, hip_stream);
 }
 
+int glass_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sink_words,
+                      void* hip_stream) {
+  if (!src || !sink) return fail(GLASS_EINVAL, "stream read: NULL pointer");
+  if (!glass::aligned(src, 16) || nbytes % 16 != 0 || nbytes == 0)
+    return fail(GLASS_EINVAL, "stream read: src must be 16-byte aligned, nbytes a positive multiple of 16");
+  if (!glass::aligned(sink, 4) || sink_words == 0)
+    return fail(GLASS_EINVAL, "stream read: sink must be 4-byte aligned with at least one word");
+  return glass::launch_stream_read(src, nbytes, sink, sink_words, (hipStream_t)hip_stream);
+}
+
 const char* glass_status_string(int status) {
   switch (status) {
     case GLASS_OK: return "ok";

@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstddef>
 #include <string>
 
@@ -58,6 +59,10 @@ int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     double rel_tol, double abs_tol, int* iters, int* status,
                     void* rho, void* workspace, size_t workspace_bytes,
                     bool exclusive, bool single, hipStream_t stream);
+
+// Streaming-read probe (measurement aid); arguments validated by the C ABI.
+int launch_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sink_words,
+                       hipStream_t stream);
 
 inline bool aligned(const void* p, size_t a) {
   return (reinterpret_cast<uintptr_t>(p) % a) == 0;

@@ -1,0 +1,65 @@
+// Streaming-read rate probe (a measurement aid, not a step of the solve):
+// reads a buffer once with coalesced 16-byte non-temporal loads, the access
+// pattern of the bandwidth-bound kernels here, and folds every 32-bit word
+// into one XOR per workgroup so the loads cannot be dropped and the result
+// can be checked.  Its rate is the device's practical read ceiling, which the
+// benchmark reports the HBM-bound kernels against next to the vendor peak.
+#include "common.hpp"
+#include "internal.hpp"
+
+namespace glass {
+namespace {
+
+constexpr int kProbeThreads = 256;
+constexpr int kProbeUnroll = 8;  // 16-byte loads in flight per thread
+constexpr long long kProbeChunkVecs = (long long)kProbeThreads * kProbeUnroll;
+
+__global__ void __launch_bounds__(kProbeThreads)
+stream_read_kernel(const vec16_t* __restrict__ src, long long nvec, unsigned* __restrict__ sink) {
+  const int tid = threadIdx.x;
+  unsigned acc = 0u;
+  const long long nchunks = (nvec + kProbeChunkVecs - 1) / kProbeChunkVecs;
+  for (long long c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const long long base = c * kProbeChunkVecs + tid;
+    vec16_t t[kProbeUnroll];
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      const long long i = base + (long long)u * kProbeThreads;
+      t[u] = i < nvec ? __builtin_nontemporal_load(src + i) : vec16_t{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kProbeUnroll; ++u) {
+      acc ^= __float_as_uint(t[u][0]) ^ __float_as_uint(t[u][1]) ^ __float_as_uint(t[u][2]) ^
+             __float_as_uint(t[u][3]);
+    }
+  }
+  __shared__ unsigned red[kProbeThreads];
+  red[tid] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned x = 0u;
+    for (int k = 0; k < kProbeThreads; ++k) x ^= red[k];
+    sink[blockIdx.x] = x;
+  }
+}
+
+}  // namespace
+
+int launch_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sink_words,
+                       hipStream_t stream) {
+  DeviceInfo dev;
+  if (int rc = current_device_info(&dev)) return rc;
+  const long long nvec = (long long)(nbytes / 16);
+  const long long nchunks = (nvec + kProbeChunkVecs - 1) / kProbeChunkVecs;
+  // Eight workgroups per compute unit at most, never more than the sink holds.
+  long long grid = std::min<long long>(nchunks, 8LL * dev.cu_count);
+  grid = std::min<long long>(grid, (long long)sink_words);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, stream,
+                     reinterpret_cast<const vec16_t*>(src), nvec, sink);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "stream read probe launch");
+  return GLASS_OK;
+}
+
+}  // namespace glass

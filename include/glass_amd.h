@@ -289,6 +289,20 @@ int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
                        void* workspace, size_t workspace_bytes,
                        glass_dtype dtype, void* hip_stream);
 
+/*
+ * Measurement aid, not a step of the solve: reads nbytes at src (device
+ * memory, 16-byte aligned, nbytes a positive multiple of 16) once with
+ * coalesced 16-byte non-temporal loads and writes, for each workgroup w
+ * launched, sink[w] = the XOR of the 32-bit words that workgroup read.  The
+ * XOR of sink[0 .. sink_words) (words past the workgroups launched are left
+ * untouched, so zero them first) is the XOR of every 32-bit word of the
+ * buffer.  At most sink_words workgroups are launched (8 per compute unit at
+ * most); the time of the call gives the device's streaming-read rate, the
+ * practical ceiling of the read-bound kernels above.
+ */
+int glass_stream_read(const void* src, size_t nbytes, unsigned* sink,
+                      size_t sink_words, void* hip_stream);
+
 /* Static text for a GLASS_* return code. */
 const char* glass_status_string(int status);
 /* Text describing the last failing call on this host thread ("" if none). */

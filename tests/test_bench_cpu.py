@@ -58,8 +58,8 @@ def test_roofline_fields():
     r = bench.roofline(8e9, 1.0, None)
     assert r["bound"] == "hbm" and r["unit"] == "GB/s"
     assert r["achieved"] == pytest.approx(8000.0) and r["frac"] == pytest.approx(1.0)
-    a = bench.roofline_alu(1.573e11, 1e9, 1.0, 123.0, np.float32)
-    assert a["bound"] == "alu" and a["unit"] == "TFLOP/s" and a["peak"] == 157.3
+    a = bench.roofline_alu(7.86e10, 1e9, 1.0, 123.0, np.float32)
+    assert a["bound"] == "alu" and a["unit"] == "TFLOP/s" and a["peak"] == 78.6
     assert a["frac"] == pytest.approx(1.0) and a["traffic"] == 123.0
     assert a["hbm_achieved_gbs"] == pytest.approx(1000.0)
     assert bench.roofline_alu(1e9, 0, 1.0, None, np.float64)["peak"] == 78.6
@@ -98,3 +98,19 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_compulsory_bytes_and_fraction():
+    # ss=2, kp=3, float32, 2 problems: S and Pinv once (288 B), vectors 76 B
+    w = replace(workloads.WORKLOADS[0], ss=2, kp=3, dtype=np.float32)
+    assert bench.compulsory_bytes_pcg(w, 2) == 2 * (288 + 76)
+    assert bench.compulsory_bytes_pcg(w, 2, pinv_diag=True) == 2 * (192 + 76)
+    r = bench.roofline(16e9, 1.0, None, compulsory=4e9, served_by="hbm+infinity-cache")
+    assert r["frac"] == pytest.approx(2.0) and r["frac_compulsory"] == pytest.approx(0.5)
+    assert r["served_by"] == "hbm+infinity-cache"
+
+
+def test_alu_roofline_uses_the_unpacked_fp32_peak():
+    r = bench.roofline_alu(78.6e9, 1e9, 1.0, None, np.float32)
+    assert r["peak"] == pytest.approx(78.6) and r["frac"] == pytest.approx(1.0)
+    assert r["frac_of_packed_peak"] == pytest.approx(78.6 / 157.3)
