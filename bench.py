@@ -70,13 +70,17 @@ KERNEL_OF = {
     "pcg3_pdp": "pcg_batched_kernel<float, 21, 3, 8>",
     "grid4_sr": "pcg_grid_cg1_kernel<double, 12,",
     "grid4_f32_sr": "pcg_grid_cg1_kernel<float, 12,",
+    "pcg0_multi": "pcg_multi_kernel<float, 6, 32, 6>",
+    "pcg0_b4096": "pcg_batched_kernel<float, 6, 1, 0>",
+    "pcg0_b4096_multi": "pcg_multi_kernel<float, 6, 32, 6>",
 }
 # Workload inputs: the five configurations; bdsv2 is the direct solve of the
 # same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
 # are the precision variants of pcg2 and grid4 (same recipe and seeds).
 CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "pcg3_stream": 3, "grid4": 4, "bdsv2": 2,
              "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3, "pcg2_pdp": 2,
-             "pcg3_pdp": 3, "grid4_sr": 4, "grid4_f32_sr": 4}
+             "pcg3_pdp": 3, "grid4_sr": 4, "grid4_f32_sr": 4, "pcg0_multi": 0, "pcg0_b4096": 0,
+             "pcg0_b4096_multi": 0}
 # Workloads run with GLASS_PCG_PINV_BLOCK_DIAGONAL (their Pinv is block-Jacobi,
 # so the assertion holds): pcg2_pd and pcg3_pd are the ss=14 and ss=21
 # workloads with the hint.
@@ -88,6 +92,10 @@ PINV_PACKED = {"pcg2_pdp", "pcg3_pdp"}
 # (GLASS_AMD_PCG_NO_HYBRID=1): pcg3_stream is the ss=21 workload with S and
 # Pinv both streamed, the placement the S-resident one replaced.
 NO_HYBRID = {"pcg3_stream"}
+# Workloads run with several problems per wave (GLASS_AMD_PCG_MULTI=1): the
+# ss=6 systems at their 64 problems and at 4096 (pcg0_b4096 is the same 4096
+# problems in the default workgroup placement).
+MULTI = {"pcg0_multi", "pcg0_b4096_multi"}
 # Grid workloads run in the single-reduction form (GLASS_GRID_SINGLE_REDUCTION).
 SINGLE_RED = {"grid4_sr", "grid4_f32_sr"}
 VARIANT_OF = {
@@ -100,6 +108,9 @@ VARIANT_OF = {
     "pcg2_pdp": dict(name="pcg_ss14_kp32_b4096_f32_pinv_diagonal_blocks"),
     "pcg3_pdp": dict(name="pcg_ss21_kp64_b2048_f32_pinv_diagonal_blocks"),
     "pcg2_f64": dict(name="pcg_ss14_kp32_b4096_f64", dtype=np.float64),
+    "pcg0_multi": dict(name="pcg_ss6_kp32_b64_f32_several_per_wave"),
+    "pcg0_b4096": dict(name="pcg_ss6_kp32_b4096_f32", n_problems=4096),
+    "pcg0_b4096_multi": dict(name="pcg_ss6_kp32_b4096_f32_several_per_wave", n_problems=4096),
     "grid4_f32": dict(name="grid_pcg_ss12_kp8192_f32", dtype=np.float32, rel_tol=1e-7),
 }
 
@@ -400,6 +411,10 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         os.environ["GLASS_AMD_PCG_NO_HYBRID"] = "1"
     else:
         os.environ.pop("GLASS_AMD_PCG_NO_HYBRID", None)
+    if key in MULTI:
+        os.environ["GLASS_AMD_PCG_MULTI"] = "1"
+    else:
+        os.environ.pop("GLASS_AMD_PCG_MULTI", None)
 
     def run(x, exclusive=True):
         if grid:
@@ -428,8 +443,8 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     # batched resident placement), else once per pass.
     placement = None if grid else glass.pcg_batched_placement(
         w.ss, w.kp, S.dtype, pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
-    resident = grid or placement == glass.PLACEMENT_RESIDENT or (
-        "S" if placement == glass.PLACEMENT_S_RESIDENT else False)
+    resident = grid or placement in (glass.PLACEMENT_RESIDENT, glass.PLACEMENT_SEVERAL_PER_WAVE) \
+        or ("S" if placement == glass.PLACEMENT_S_RESIDENT else False)
     pinned = glass.pcg_batched_pinned_rows(
         w.ss, w.kp, S.dtype, pinv_block_diagonal=pd,
         pinv_diagonal_blocks=packed) if resident == "S" else 0
@@ -673,7 +688,7 @@ def main():
             # pcg3_stream runs pcg3's inputs in another placement: no second
             # CPU baseline
             res[name] = bench_pcg(torch, glass, name, args.steps, args.warmup, budget,
-                                  with_cpu and name not in NO_HYBRID, traffic)
+                                  with_cpu and name not in NO_HYBRID | MULTI, traffic)
         print("[bench] %s done: %s" % (name, json.dumps(res[name])[:300]), file=sys.stderr,
               flush=True)
     if args.calibration_copy:

@@ -24,7 +24,7 @@ __all__ = [
     "PCG_PINV_BLOCK_DIAGONAL", "PCG_PINV_DIAGONAL_BLOCKS", "GRID_SINGLE_REDUCTION",
     "pcg_batched_placement", "pcg_batched_pinned_rows", "PLACEMENT_RESIDENT",
     "PLACEMENT_STREAMED_PREFETCH",
-    "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT", "stream_read",
+    "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT", "PLACEMENT_SEVERAL_PER_WAVE", "stream_read",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -208,6 +208,7 @@ def bdsv_batched(x, S, b, state_size: int, knot_points: int, status_out=None,
 
 
 PLACEMENT_RESIDENT, PLACEMENT_STREAMED_PREFETCH, PLACEMENT_STREAMED, PLACEMENT_S_RESIDENT = 0, 1, 2, 3
+PLACEMENT_SEVERAL_PER_WAVE = 4
 
 
 def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=True,

@@ -39,6 +39,13 @@ int launch_pcg_batched(glass_dtype dt, void* x, const void* S,
                        double abs_tol, int* iters, int* status, void* rho,
                        bool pinv_diag, bool pinv_packed, hipStream_t stream);
 
+// Several problems per wave (pcg_multi.hip): whether the shape has that
+// placement, and its launcher (arguments validated by the C ABI).
+bool pcg_multi_fits(glass_dtype dt, int ss, int kp);
+int launch_pcg_multi(glass_dtype dt, void* x, const void* S, const void* Pinv, const void* b,
+                     int ss, int kp, int n_problems, int max_iters, double rel_tol,
+                     double abs_tol, int* iters, int* status, void* rho, hipStream_t stream);
+
 // Placement glass_pcg_batched_ex would choose (GLASS_PLACEMENT_*), or an error.
 // pinv_packed: Pinv given as packed D blocks (implies pinv_diag).
 int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,

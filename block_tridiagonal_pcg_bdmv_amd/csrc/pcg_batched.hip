@@ -1033,11 +1033,29 @@ bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, siz
   return true;
 }
 
+// Several problems per wave (pcg_multi.hip) for the small shapes it covers
+// with Pinv in [L|D|R] form.  Chosen by itself where it was measured faster
+// than the workgroup placement: chains of at most 16 rows (one row per lane,
+// four problems per wave; 1.2-2.4x at kp = 1-2).  With more rows per lane
+// each lane's serial chain outweighs the barriers it saves (measured slower
+// at kp = 4-32).  GLASS_AMD_PCG_MULTI=1 selects it wherever it fits, 0 never.
+bool use_multi(glass_dtype dt, int ss, int kp, bool pinv_packed) {
+  if (pinv_packed || !pcg_multi_fits(dt, ss, kp)) return false;
+  const char* f = std::getenv("GLASS_AMD_PCG_MULTI");
+  if (f && f[0] == '1' && f[1] == '\0') return true;
+  if (f && f[0] == '0' && f[1] == '\0') return false;
+  return (long long)kp * ss <= 16;
+}
+
 template <typename T>
 int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
                  int n_problems, int max_iters, double rel_tol, double abs_tol,
                  int* iters, int* status, T* rho, bool pinv_diag, bool pinv_packed,
                  hipStream_t st) {
+  constexpr glass_dtype dt = sizeof(T) == 4 ? GLASS_F32 : GLASS_F64;
+  if (use_multi(dt, ss, kp, pinv_packed))
+    return launch_pcg_multi(dt, x, S, P, b, ss, kp, n_problems, max_iters, rel_tol, abs_tol,
+                            iters, status, rho, st);
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   const bool vec = vector_ok<T>(S, P, ss, kp, pinv_packed);
@@ -1074,6 +1092,8 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
 
 template <typename T>
 int placement_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_packed) {
+  constexpr glass_dtype dt = sizeof(T) == 4 ? GLASS_F32 : GLASS_F64;
+  if (use_multi(dt, ss, kp, pinv_packed)) return GLASS_PLACEMENT_SEVERAL_PER_WAVE;
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   const long long n = (long long)kp * ss, es = (long long)sizeof(T);
@@ -1090,6 +1110,8 @@ int placement_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_pa
 
 template <typename T>
 int pinned_rows_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_packed) {
+  constexpr glass_dtype dt = sizeof(T) == 4 ? GLASS_F32 : GLASS_F64;
+  if (use_multi(dt, ss, kp, pinv_packed)) return 0;
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   const long long n = (long long)kp * ss, es = (long long)sizeof(T);

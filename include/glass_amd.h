@@ -170,7 +170,13 @@ enum {
   GLASS_PLACEMENT_RESIDENT = 0,
   GLASS_PLACEMENT_STREAMED_PREFETCH = 1,
   GLASS_PLACEMENT_STREAMED = 2,
-  GLASS_PLACEMENT_S_RESIDENT = 3
+  GLASS_PLACEMENT_S_RESIDENT = 3,
+  GLASS_PLACEMENT_SEVERAL_PER_WAVE = 4  /* small problems (state_size 6, up to
+                                           192 rows; Pinv in [L|D|R] form):
+                                           16 or 32 lanes per problem, 4 or 2
+                                           problems per wave, S and Pinv rows
+                                           in registers (read once), no
+                                           workgroup barriers */
 };
 int glass_pcg_batched_placement(int state_size, int knot_points,
                                 glass_dtype dtype, int aligned16, unsigned flags);
