@@ -67,6 +67,14 @@ int env_int(const char* name, int fallback) {
   return (int)v;
 }
 
+int env_flag(const char* name, int fallback) {
+  const char* s = std::getenv(name);
+  if (!s) return fallback;
+  if (s[0] == '0' && s[1] == '\0') return 0;
+  if (s[0] == '1' && s[1] == '\0') return 1;
+  return fallback;
+}
+
 }  // namespace glass
 
 using glass::fail;

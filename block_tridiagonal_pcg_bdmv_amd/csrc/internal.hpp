@@ -28,6 +28,8 @@ int current_device_info(DeviceInfo* out);
 // Optional launch-shape override from the environment (tests and tuning
 // sweeps): returns `fallback` when `name` is unset or not a positive integer.
 int env_int(const char* name, int fallback);
+// A 0/1 switch from the environment: "0" or "1", else `fallback`.
+int env_flag(const char* name, int fallback);
 
 // Kernel launchers.  Arguments are already validated by the C ABI.
 int launch_bdmv(glass_dtype dt, void* y, const void* S, const void* v, int ss,

@@ -121,6 +121,7 @@ enum Mode {
   kHybrid = 7,             // S resident, Pinv streamed by direct loads into LDS
   kHybridPDP = 8,          // S resident, Pinv's packed D blocks held whole in LDS
   kHybridPD = 9,           // S resident, D parts of the [L|D|R] Pinv gathered into LDS
+  kResidentDma = 10,       // resident; Pinv rows arrive through the wave's LDS stage
 };
 
 // Workgroup size bound: 8 waves (so a lane may use up to 256 VGPRs) for the
@@ -128,7 +129,8 @@ enum Mode {
 // lane; 16 waves otherwise (rows beyond 4096 need them, at the cost of
 // spills).
 constexpr int max_threads_for(int rpt, int mode) {
-  const bool resident = mode == kResident || mode == kResidentPD || mode == kResidentPDP;
+  const bool resident = mode == kResident || mode == kResidentPD || mode == kResidentPDP ||
+                        mode == kResidentDma;
   return (mode == kStreamPrefetch || mode == kStreamPrefetchPD || mode == kStreamPrefetchPDP ||
           mode == kHybrid || mode == kHybridPDP || mode == kHybridPD || rpt == 3 || rpt == 4 ||
           (resident && rpt > 1))
@@ -139,7 +141,12 @@ constexpr int max_threads_for(int rpt, int mode) {
 template <typename T, int SS, int RPT, int MODE>
 __global__ void __launch_bounds__(max_threads_for(RPT, MODE))
 pcg_batched_kernel(PcgArgs<T> a) {
-  constexpr bool RES = MODE == kResident || MODE == kResidentPD || MODE == kResidentPDP;
+  constexpr bool RES = MODE == kResident || MODE == kResidentPD || MODE == kResidentPDP ||
+                       MODE == kResidentDma;
+  // RESD: resident rows, with each wave's 64 Pinv rows brought into its LDS
+  // stage by coalesced direct loads (no registers in flight) while the S
+  // rows load straight into registers; each lane then copies its Pinv row.
+  constexpr bool RESD = MODE == kResidentDma;
   constexpr bool PD = MODE == kResidentPD || MODE == kResidentPDP;  // Pinv rows: D part only
   constexpr bool PFM =
       MODE == kStreamPrefetch || MODE == kStreamPrefetchPD || MODE == kStreamPrefetchPDP;
@@ -285,10 +292,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
             MODE == kResidentPDP ? (long long)row[k] * SS : off + (PD ? SS : 0);
         if (vec) {
           load_row_regs<T, WC, true>(mS[k], gS + off);
-          if constexpr (RES) load_row_regs<T, WCP, true>(mP[k], gP + offP);
+          if constexpr (RES && !RESD) load_row_regs<T, WCP, true>(mP[k], gP + offP);
         } else {
           load_row_regs<T, WC, false>(mS[k], gS + off);
-          if constexpr (RES) load_row_regs<T, WCP, false>(mP[k], gP + offP);
+          if constexpr (RES && !RESD) load_row_regs<T, WCP, false>(mP[k], gP + offP);
         }
       }
     }
@@ -366,7 +373,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // reads (after its own vmcnt wait), and global memory is not shared
   // between the waves before the final stores.
   auto block_sync = [&]() {
-    if constexpr (HYB) {
+    if constexpr (HYB || RESD) {
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -564,6 +571,25 @@ pcg_batched_kernel(PcgArgs<T> a) {
     ring_load(0);
     if (kRingDepth == 2) ring_load(1 % (2 * RPT));
   }
+  if constexpr (RESD) {
+    // This wave's Pinv rows (one chunk: RPT == 1) into its stage, issued
+    // after x0 and b so that waiting for those does not wait for them.  The
+    // stage holds exactly the chunk; lanes past its last 16-byte vector are
+    // masked off.
+    const int r0 = chunk_r0(0);
+    const int cvec = (min(64, n - r0) * W * (int)sizeof(T) + 15) / 16;
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(gP + (long long)r0 * W, (n - r0) * W * (int)sizeof(T));
+    unsigned char* st = reinterpret_cast<unsigned char*>(stage);
+    constexpr int NVC = (64 * WC * (int)sizeof(T) + 1023) / 1024;
+#pragma unroll
+    for (int u = 0; u < NVC; ++u) {
+      if (lane + u * kWave < cvec)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
+            (lane + u * kWave) * 16, 0, 0, 0);
+    }
+  }
   if constexpr (HYBS && kSViaLds) {
     // S chunks through the stage: coalesced direct loads, then each lane
     // copies its row into registers.
@@ -608,6 +634,15 @@ pcg_batched_kernel(PcgArgs<T> a) {
   }
   // D blocks, or pinned chunks, landed
   if constexpr (HYBP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (RESD) {
+    // The wave's Pinv rows landed in its stage: each lane copies its own.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (valid[0]) {
+      const T* __restrict__ m = stage + lane * W;
+#pragma unroll
+      for (int c = 0; c < WC; ++c) mP[0][c] = m[c];
+    }
+  }
   if constexpr (HYBS) {
     if (pin_last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
@@ -689,6 +724,7 @@ struct Plan {
   bool pd = false;  // Pinv's D blocks only (resident, or streamed with prefetch)
   bool packed = false;  // Pinv given as packed D blocks
   bool res_auto = false;  // resident rows per lane left to the occupancy choice
+  bool resdma = false;    // resident, Pinv rows through the wave's LDS stage
   bool prefetch = false;
   bool hyb = false;  // S resident, Pinv streamed by direct loads into LDS
   int npin = 0;      // waves whose last Pinv chunk stays pinned in LDS
@@ -755,7 +791,8 @@ int prefetch_stage_elems(int ss) {
 // prefetching streamed placement is allowed (specialised, 16-byte aligned).
 template <typename T>
 bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag,
-               bool hybrid, bool pinv_packed, size_t lds_max, Plan* plan) {
+               bool hybrid, bool pinv_packed, size_t lds_max, Plan* plan,
+               bool prefetch_ok_for_dma = false) {
   const int n = kp * ss;
   const int W = 3 * ss;
   const int nchunks = (n + 63) / 64;
@@ -778,6 +815,17 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
     p.stage_elems = 0;
     p.lds = lds_bytes<T>(ss, kp, p.NW, 0);
     if (p.lds <= lds_max) {
+      // One row per lane, a general Pinv and 16-byte aligned rows: the Pinv
+      // rows can come through a 64-row LDS stage per wave (the launch keeps
+      // it only where it does not cost occupancy).
+      if (res_rpt == 1 && !pinv_diag && prefetch_ok_for_dma && env_flag("GLASS_AMD_PCG_RES_DMA", 1)) {
+        const size_t lds_d = lds_bytes<T>(ss, kp, p.NW, 64 * W);
+        if (lds_d <= lds_max) {
+          p.resdma = true;
+          p.stage_elems = 64 * W;
+          p.lds = lds_d;
+        }
+      }
       *plan = p;
       return true;
     }
@@ -919,9 +967,28 @@ int launch_rpt(const PcgArgs<T>& a, int n_problems, const Plan& pl,
 // workgroups per CU (more problems in flight); a smaller batch keeps one row
 // per lane (the most waves per problem, the shortest solve).
 template <typename T, int SS, bool PD, bool PACKED>
-int launch_res(const PcgArgs<T>& a, int n_problems, const Plan& pl_in, hipStream_t st) {
+int launch_res(const PcgArgs<T>& a_in, int n_problems, const Plan& pl_in, hipStream_t st) {
   constexpr int M = PACKED ? kResidentPDP : (PD ? kResidentPD : kResident);
   Plan pl = pl_in;
+  PcgArgs<T> a = a_in;
+  if constexpr (!PD && !PACKED && kResidentRowsFit<T>(SS, 1, false)) {
+    if (pl.resdma) {
+      // The Pinv stage only where it keeps the occupancy of the plain kernel.
+      int per_d = 0, per_p = 0;
+      const size_t lds_p = lds_bytes<T>(a.ss, a.kp, pl.NW, 0);
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &per_d, pcg_batched_kernel<T, SS, 1, kResidentDma>, pl.NW * 64, pl.lds) ==
+              hipSuccess &&
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(
+              &per_p, pcg_batched_kernel<T, SS, 1, kResident>, pl.NW * 64, lds_p) == hipSuccess &&
+          per_d >= per_p && per_d > 0)
+        return launch_one<T, SS, 1, kResidentDma>(a, n_problems, pl, st);
+      pl.resdma = false;
+      pl.stage_elems = 0;
+      pl.lds = lds_p;
+      a.stage_elems = 0;
+    }
+  }
   if constexpr (kResidentRowsFit<T>(SS, 1, PD) && kResidentRowsFit<T>(SS, 2, PD)) {
     DeviceInfo dev;
     const int nchunks = (a.kp * SS + 63) / 64;
@@ -1021,7 +1088,8 @@ bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, siz
   const bool hybrid = specialised && vec && kHybridSize<T>(ss) &&
                       std::getenv("GLASS_AMD_PCG_NO_HYBRID") == nullptr;
   pinv_diag = pinv_diag || pinv_packed;
-  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, hybrid, pinv_packed, lds_max, pl))
+  if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, hybrid, pinv_packed, lds_max, pl,
+                    specialised && vec))
     return false;
   if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && (pl->res || pl->hyb)) {
     Plan alt;
@@ -1041,10 +1109,7 @@ bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, siz
 // at kp = 4-32).  GLASS_AMD_PCG_MULTI=1 selects it wherever it fits, 0 never.
 bool use_multi(glass_dtype dt, int ss, int kp, bool pinv_packed) {
   if (pinv_packed || !pcg_multi_fits(dt, ss, kp)) return false;
-  const char* f = std::getenv("GLASS_AMD_PCG_MULTI");
-  if (f && f[0] == '1' && f[1] == '\0') return true;
-  if (f && f[0] == '0' && f[1] == '\0') return false;
-  return (long long)kp * ss <= 16;
+  return env_flag("GLASS_AMD_PCG_MULTI", (long long)kp * ss <= 16 ? 1 : 0) == 1;
 }
 
 template <typename T>
