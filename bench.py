@@ -419,7 +419,8 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     def run(x, exclusive=True):
         if grid:
             glass.pcg_grid(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters, ws,
-                           status, exclusive=exclusive, single_reduction=single)
+                           status, exclusive=exclusive, single_reduction=single,
+                           keep_workspace=True)
         else:
             glass.pcg_batched(x, S, P, b, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, iters,
                               status, pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
@@ -472,6 +473,7 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it.max()))
     if grid:
         out["launch"] = "exclusive"
+        out["workspace"] = "kept (GLASS_GRID_KEEP_WORKSPACE: no per-solve clearing kernel)"
         out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it[0]))
         for k in range(min(10, len(xs))):
             xs[k].zero_()

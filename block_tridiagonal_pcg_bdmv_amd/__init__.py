@@ -22,6 +22,7 @@ __all__ = [
     "CONVERGED",
     "MAX_ITERS", "BREAKDOWN", "GRID_TIMEOUT", "BDSV_OK", "BDSV_NOT_SPD", "GRID_EXCLUSIVE",
     "PCG_PINV_BLOCK_DIAGONAL", "PCG_PINV_DIAGONAL_BLOCKS", "GRID_SINGLE_REDUCTION",
+    "GRID_KEEP_WORKSPACE",
     "pcg_batched_placement", "pcg_batched_pinned_rows", "PLACEMENT_RESIDENT",
     "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT", "PLACEMENT_SEVERAL_PER_WAVE", "stream_read",
@@ -39,6 +40,7 @@ CONVERGED, MAX_ITERS, BREAKDOWN, GRID_TIMEOUT = 0, 1, 2, 3
 BDSV_OK, BDSV_NOT_SPD = 0, 1
 GRID_EXCLUSIVE = 1  # glass_pcg_grid_ex flag: ordinary dispatch on the stream's queue
 GRID_SINGLE_REDUCTION = 2  # glass_pcg_grid_ex flag: one grid reduction per iteration
+GRID_KEEP_WORKSPACE = 4  # glass_pcg_grid_ex flag: the workspace is kept for grid solves
 PCG_PINV_BLOCK_DIAGONAL = 1  # glass_pcg_batched_ex flag: Pinv's L and R blocks are zero
 PCG_PINV_DIAGONAL_BLOCKS = 2  # glass_pcg_batched_ex flag: Pinv is packed D blocks [B, kp, ss, ss]
 
@@ -255,7 +257,7 @@ def pcg_grid_workspace_bytes(state_size: int, knot_points: int, dtype) -> int:
 def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
              rel_tol: float, abs_tol: float, iters_out, workspace,
              status_out=None, rho_out=None, stream=None, exclusive=False,
-             single_reduction=False):
+             single_reduction=False, keep_workspace=False):
     """One PCG solve over a cooperative grid.  Same arguments as
     ``pcg_batched`` with one problem, plus a device ``workspace`` tensor of at
     least ``pcg_grid_workspace_bytes`` bytes (any dtype, 256-byte aligned).
@@ -263,7 +265,10 @@ def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
     the stream's queue, for callers that know no other kernel occupies the
     device during the solve.  ``single_reduction=True`` passes
     GLASS_GRID_SINGLE_REDUCTION: the single-reduction form of PCG (one grid
-    reduction per iteration; same iterates in exact arithmetic)."""
+    reduction per iteration; same iterates in exact arithmetic).
+    ``keep_workspace=True`` passes GLASS_GRID_KEEP_WORKSPACE: the workspace
+    is used by nothing but grid solves between calls, so its exchange words
+    need no clearing per solve."""
     import torch
     ss, kp = int(state_size), int(knot_points)
     if _problems(S, ss, kp) != 1:
@@ -283,7 +288,8 @@ def pcg_grid(x, S, Pinv, b, state_size: int, knot_points: int, max_iters: int,
                                   ctypes.c_void_p(workspace.data_ptr()), wbytes,
                                   _dtype_code(S),
                                   (GRID_EXCLUSIVE if exclusive else 0)
-                                  | (GRID_SINGLE_REDUCTION if single_reduction else 0),
+                                  | (GRID_SINGLE_REDUCTION if single_reduction else 0)
+                                  | (GRID_KEEP_WORKSPACE if keep_workspace else 0),
                                   _stream(stream))
     _check(rc, "glass_pcg_grid_ex")
 

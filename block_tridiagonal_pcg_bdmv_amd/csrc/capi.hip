@@ -237,7 +237,8 @@ int check_grid(void* x, const void* S, const void* Pinv, const void* b, int stat
                int* iters_out, int* status_out, void* rho_out, glass_dtype dtype,
                unsigned flags) {
   if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
-  if (flags & ~(unsigned)(GLASS_GRID_EXCLUSIVE | GLASS_GRID_SINGLE_REDUCTION))
+  if (flags & ~(unsigned)(GLASS_GRID_EXCLUSIVE | GLASS_GRID_SINGLE_REDUCTION |
+                          GLASS_GRID_KEEP_WORKSPACE))
     return fail(GLASS_EINVAL, "unknown grid flags");
   if (knot_points < 4) return fail(GLASS_EINVAL, "grid pcg needs knot_points >= 4");
   if (int rc = check_ptr(x, dtype, "x")) return rc;
@@ -273,6 +274,7 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
                                 status_out, rho_out, workspace, workspace_bytes,
                                 (flags & GLASS_GRID_EXCLUSIVE) != 0,
                                 (flags & GLASS_GRID_SINGLE_REDUCTION) != 0,
+                                (flags & GLASS_GRID_KEEP_WORKSPACE) != 0,
                                 (hipStream_t)hip_stream);
 }
 
@@ -289,6 +291,7 @@ int glass_pcg_grid_noalloc(void* x, const void* S, const void* Pinv, const void*
                                 status_out, rho_out, nullptr, 0,
                                 (flags & GLASS_GRID_EXCLUSIVE) != 0,
                                 (flags & GLASS_GRID_SINGLE_REDUCTION) != 0,
+                                (flags & GLASS_GRID_KEEP_WORKSPACE) != 0,
                                 (hipStream_t)hip_stream);
 }
 

@@ -67,7 +67,7 @@ int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     const void* b, int ss, int kp, int max_iters,
                     double rel_tol, double abs_tol, int* iters, int* status,
                     void* rho, void* workspace, size_t workspace_bytes,
-                    bool exclusive, bool single, hipStream_t stream);
+                    bool exclusive, bool single, bool keep, hipStream_t stream);
 
 // Streaming-read probe (measurement aid); arguments validated by the C ABI.
 int launch_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sink_words,

@@ -38,8 +38,15 @@
 //   included).  One buffer would do for edges published every other barrier
 //   (the standard steps), not for the single-reduction form, which publishes
 //   them at every barrier.
-//   A reset kernel zeroes every tag word before the solve, so tags start at 1
-//   and stale words from an earlier solve never match.
+//   Tags are relative to a per-solve base: barrier b is tagged base + b.  By
+//   default a reset kernel zeroes the words the solve reads and the base is 1.
+//   When the caller keeps the workspace for grid solves only
+//   (GLASS_GRID_KEEP_WORKSPACE, and always for the static no-alloc scratch),
+//   the host hands each solve a base above every tag an earlier solve could
+//   have written there (a solve has at most 2 max_iters + 2 barriers), so
+//   stale words never match and no reset is launched; the whole area is
+//   zeroed once, on first use of the address and before the 32-bit tags
+//   would wrap.
 // * Matrices: for the specialised state sizes each thread keeps its S row
 //   (extended rows) and Pinv row (own rows) in VGPRs, loaded once with every
 //   load of the row in flight; the iteration then touches only registers,
@@ -48,7 +55,9 @@
 //   other poll stops as soon as it sees the flag, the kernel runs to its end,
 //   and the status output reports the timeout instead of the device hanging.
 #include <cstdlib>
+#include <map>
 #include <mutex>
+#include <utility>
 #include <vector>
 
 #include "common.hpp"
@@ -84,6 +93,8 @@ struct GridArgs {
   int nb_max;
   int wide;               // matrix bases 16-byte aligned: vector row loads
   unsigned spin_limit;    // poll rounds before a wait gives up
+  unsigned tag_base;      // barrier b of this solve is tagged tag_base + b; a
+                          // timeout stores tag_base into flags[0]
 };
 
 typedef unsigned long long u64;
@@ -144,14 +155,68 @@ int scratch_address(int device, void** out) {
   return GLASS_OK;
 }
 
-// Zeroes the timeout flag and the tag words the solve will read: n1 words
-// of partial buffers at w1 and n2 words of edges at w2.
-__global__ void grid_reset_kernel(unsigned int* flags, u64* w1, int n1, u64* w2, int n2) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  const int stride = gridDim.x * blockDim.x;
+// Zeroes the timeout flag and tag words: n1 words at w1 and n2 words at w2
+// (the partial buffers and edges the solve reads, or the whole area).
+__global__ void grid_reset_kernel(unsigned int* flags, u64* w1, long long n1, u64* w2,
+                                  long long n2) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const long long stride = (long long)gridDim.x * blockDim.x;
   if (i == 0) flags[0] = 0u;
-  for (int j = i; j < n1; j += stride) w1[j] = 0ull;
-  for (int j = i; j < n2; j += stride) w2[j] = 0ull;
+  for (long long j = i; j < n1; j += stride) w1[j] = 0ull;
+  for (long long j = i; j < n2; j += stride) w2[j] = 0ull;
+}
+
+// Tag epochs of kept exchange areas, by (device, address): the next free tag
+// base, valid only after the whole area was zeroed (every word there is then
+// zero or a tag below it).
+struct Epoch {
+  unsigned next = 0;
+};
+std::mutex g_epoch_mutex;
+std::map<std::pair<int, uintptr_t>, Epoch> g_epochs;
+constexpr unsigned long long kTagLimit = 0xFFFFFF00ull;
+
+enum ResetKind { kResetNone = 0, kResetRegion = 1, kResetAll = 2 };
+struct EpochPlan {
+  unsigned base = 1;
+  ResetKind reset = kResetRegion;
+};
+
+// Barriers one solve can use: the standard steps 1 + 2 max_iters, the
+// single-reduction form max_iters + 2.
+inline unsigned long long barrier_bound(int max_iters) {
+  return 2ull * (unsigned long long)max_iters + 2ull;
+}
+
+EpochPlan epoch_begin(int device, const void* area, bool keep, int max_iters) {
+  EpochPlan p;
+  const auto key = std::make_pair(device, reinterpret_cast<uintptr_t>(area));
+  std::lock_guard<std::mutex> lock(g_epoch_mutex);
+  if (!keep) {
+    g_epochs.erase(key);  // the caller may change the area before a later kept solve
+    return p;             // zero what this solve reads, tags from 1
+  }
+  auto it = g_epochs.find(key);
+  if (it != g_epochs.end() &&
+      (unsigned long long)it->second.next + barrier_bound(max_iters) + 1ull < kTagLimit) {
+    p.base = it->second.next;
+    p.reset = kResetNone;
+  } else {
+    p.reset = kResetAll;
+  }
+  return p;
+}
+
+void epoch_commit(int device, const void* area, bool keep, int max_iters, const EpochPlan& p) {
+  if (!keep) return;
+  const auto key = std::make_pair(device, reinterpret_cast<uintptr_t>(area));
+  const unsigned long long next = (unsigned long long)p.base + barrier_bound(max_iters) + 1ull;
+  std::lock_guard<std::mutex> lock(g_epoch_mutex);
+  if (next >= kTagLimit) {
+    g_epochs.erase(key);
+  } else {
+    g_epochs[key].next = (unsigned)next;
+  }
 }
 
 __device__ __forceinline__ u64 load_word(const u64* p) {
@@ -186,16 +251,18 @@ __device__ __forceinline__ bool get_tagged(const u64* src, unsigned tag, double&
 }
 
 // One more round of a bounded poll by a whole wave (see the timeout rule at
-// the top of the file); false when the poll must stop.
+// the top of the file); false when the poll must stop.  The flag holds the
+// tag base of the solve that timed out, so a flag left by an earlier solve
+// never stops this one.
 __device__ __forceinline__ bool keep_polling(unsigned& spins, unsigned int* flags, int lane,
-                                             unsigned limit) {
+                                             unsigned limit, unsigned tag_base) {
   __builtin_amdgcn_s_sleep(1);
   ++spins;
   if ((spins & 63u) == 0u &&
-      __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+      __hip_atomic_load(flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == tag_base)
     return false;  // another workgroup already gave up: do not wait again
   if (spins > limit) {
-    if (lane == 0) __hip_atomic_store(flags, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) __hip_atomic_store(flags, tag_base, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return false;
   }
   return true;
@@ -214,6 +281,7 @@ struct GridXchg {
   size_t edge_parity;
   unsigned int* flags;
   unsigned spin_limit;
+  unsigned tag_base;
   int G, g;
 };
 
@@ -232,6 +300,7 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
                                            int lane) {
   static_assert(NV >= 1 && NV <= kDotValues, "values per grid dot");
   constexpr int WD = kTagWords<T>;
+  const unsigned tag = xc.tag_base + bar;
   T vs[NV];
 #pragma unroll
   for (int q = 0; q < NV; ++q) vs[q] = wave_sum(v[q]);
@@ -253,10 +322,10 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
     const u64* right = xc.right ? xc.right + epar : nullptr;
     if (edge_lds)
       for (int j = lane; j < n_edge; j += kWave)
-        put_tagged(xc.my_edges + epar + j * WD, edge_lds[j], bar);
+        put_tagged(xc.my_edges + epar + j * WD, edge_lds[j], tag);
     if (lane == 0) {
 #pragma unroll
-      for (int q = 0; q < NV; ++q) put_tagged(slots + (xc.g * NV + q) * WD, part[q], bar);
+      for (int q = 0; q < NV; ++q) put_tagged(slots + (xc.g * NV + q) * WD, part[q], tag);
     }
 
     // Neighbour edges: loaded now, checked after the partials, so both
@@ -271,7 +340,7 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
         gv[k] = T(0);
         if (q < n_edge) {
           const u64* src = q < half ? left : right;
-          if (src) gok &= get_tagged(src + (q < half ? q + half : q - half) * WD, bar, gv[k]);
+          if (src) gok &= get_tagged(src + (q < half ? q + half : q - half) * WD, tag, gv[k]);
         }
       }
     }
@@ -292,11 +361,11 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
 #pragma unroll
           for (int q = 0; q < NV; ++q) {
             val[k][q] = T(0);
-            if (j < xc.G) ok &= get_tagged(slots + (j * NV + q) * WD, bar, val[k][q]);
+            if (j < xc.G) ok &= get_tagged(slots + (j * NV + q) * WD, tag, val[k][q]);
           }
         }
         if (__all(ok)) break;
-        if (!keep_polling(spins, xc.flags, lane, xc.spin_limit)) break;
+        if (!keep_polling(spins, xc.flags, lane, xc.spin_limit, xc.tag_base)) break;
       }
 #pragma unroll
       for (int k = 0; k < kSumBatch; ++k)
@@ -311,14 +380,14 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
     if (edge_lds) {
       unsigned spins = 0;
       while (!__all(gok)) {
-        if (!keep_polling(spins, xc.flags, lane, xc.spin_limit)) break;
+        if (!keep_polling(spins, xc.flags, lane, xc.spin_limit, xc.tag_base)) break;
         gok = true;
 #pragma unroll
         for (int k = 0; k < GP; ++k) {
           const int q = lane + k * kWave;
           if (q < n_edge) {
             const u64* src = q < half ? left : right;
-            if (src) gok &= get_tagged(src + (q < half ? q + half : q - half) * WD, bar, gv[k]);
+            if (src) gok &= get_tagged(src + (q < half ? q + half : q - half) * WD, tag, gv[k]);
           }
         }
       }
@@ -395,6 +464,7 @@ pcg_grid_kernel(GridArgs<T> a) {
   xc.right = g + 1 < G ? a.edges + (size_t)(g + 1) * n_edge * WD : nullptr;
   xc.edge_parity = (size_t)G * n_edge * WD;
   xc.spin_limit = a.spin_limit;
+  xc.tag_base = a.tag_base;
   xc.flags = a.flags;
   xc.G = G;
   xc.g = g;
@@ -512,7 +582,7 @@ pcg_grid_kernel(GridArgs<T> a) {
   if (iters > 0 && own) a.x[grow] = xr;
   if (g == 0 && tid == 0) {
     const bool timed_out =
-        __hip_atomic_load(a.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        __hip_atomic_load(a.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.tag_base;
     if (a.iters) a.iters[0] = iters;
     if (a.status) a.status[0] = timed_out ? GLASS_PCG_GRID_TIMEOUT : status;
     if (a.rho) {
@@ -603,6 +673,7 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
   xc.right = g + 1 < G ? a.edges + (size_t)(g + 1) * n_edge * WD : nullptr;
   xc.edge_parity = (size_t)G * n_edge * WD;
   xc.spin_limit = a.spin_limit;
+  xc.tag_base = a.tag_base;
   xc.flags = a.flags;
   xc.G = G;
   xc.g = g;
@@ -722,7 +793,7 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
   if (iters > 0 && own) a.x[grow] = xr;
   if (g == 0 && tid == 0) {
     const bool timed_out =
-        __hip_atomic_load(a.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+        __hip_atomic_load(a.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.tag_base;
     if (a.iters) a.iters[0] = iters;
     if (a.status) a.status[0] = timed_out ? GLASS_PCG_GRID_TIMEOUT : status;
     if (a.rho) {
@@ -734,7 +805,8 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
 
 template <typename T, int SS, bool RES>
 int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
-                      bool exclusive, bool single, hipStream_t st) {
+                      bool exclusive, bool single, void* area, size_t area_bytes, bool keep,
+                      hipStream_t st) {
   auto kern = single ? pcg_grid_cg1_kernel<T, SS, RES> : pcg_grid_kernel<T, SS, RES>;
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
@@ -747,14 +819,28 @@ int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
   if (e != hipSuccess) return fail_hip(e, "occupancy query (grid)");
   if ((long long)per_cu * dev.cu_count < a.G)
     return fail(GLASS_ECOOP, "grid pcg: workgroups cannot all be co-resident");
-  // Tag words this grid reads: both partial buffers and the edges.
-  const int n_part = 2 * a.G * kDotValues * kTagWords<T>;
-  const int n_edge = 2 * a.G * 4 * a.ss * kTagWords<T>;
-  const int reset_blocks = std::min(256, (std::max(n_part, n_edge) + 255) / 256);
-  hipLaunchKernelGGL(grid_reset_kernel, dim3(reset_blocks), dim3(256), 0, st, a.flags, a.part,
-                     n_part, a.edges, n_edge);
-  e = hipGetLastError();
-  if (e != hipSuccess) return fail_hip(e, "grid reset launch");
+  // Tag base and reset (see the exchange rules at the top of the file).
+  const EpochPlan ep = epoch_begin(dev.device, area, keep, a.max_iters);
+  a.tag_base = ep.base;
+  if (ep.reset != kResetNone) {
+    long long n1, n2;
+    u64* w1;
+    if (ep.reset == kResetAll) {  // the whole area
+      w1 = reinterpret_cast<u64*>(area);
+      n1 = (long long)(area_bytes / sizeof(u64));
+      n2 = 0;
+    } else {  // the words this grid reads: both partial buffers and the edges
+      w1 = a.part;
+      n1 = 2LL * a.G * kDotValues * kTagWords<T>;
+      n2 = 2LL * a.G * 4 * a.ss * kTagWords<T>;
+    }
+    const long long most = std::max(n1, n2);
+    const int reset_blocks = (int)std::min<long long>(1024, (most + 255) / 256);
+    hipLaunchKernelGGL(grid_reset_kernel, dim3(reset_blocks), dim3(256), 0, st, a.flags, w1, n1,
+                       a.edges, n2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail_hip(e, "grid reset launch");
+  }
   void* args[] = {&a};
   if (exclusive) {
     // Ordinary dispatch on the caller's queue: all G workgroups fit at once
@@ -763,13 +849,14 @@ int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
     // queue (about 20 us per solve).
     e = hipLaunchKernel((const void*)kern, dim3(a.G), dim3(NT), args, (unsigned)lds, st);
     if (e != hipSuccess) return fail_hip(e, "grid pcg launch");
-    return GLASS_OK;
+  } else {
+    e = hipLaunchCooperativeKernel((const void*)kern, dim3(a.G), dim3(NT), args,
+                                   (unsigned)lds, st);
+    if (e == hipErrorCooperativeLaunchTooLarge)
+      return fail(GLASS_ECOOP, "grid pcg: cooperative launch too large");
+    if (e != hipSuccess) return fail_hip(e, "grid pcg cooperative launch");
   }
-  e = hipLaunchCooperativeKernel((const void*)kern, dim3(a.G), dim3(NT), args,
-                                 (unsigned)lds, st);
-  if (e == hipErrorCooperativeLaunchTooLarge)
-    return fail(GLASS_ECOOP, "grid pcg: cooperative launch too large");
-  if (e != hipSuccess) return fail_hip(e, "grid pcg cooperative launch");
+  epoch_commit(dev.device, area, keep, a.max_iters, ep);
   return GLASS_OK;
 }
 
@@ -782,9 +869,11 @@ constexpr bool kGridResidentFits(int ss) {
 
 template <typename T, int SS>
 int launch_grid_res(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
-                    bool exclusive, bool single, hipStream_t st) {
+                    bool exclusive, bool single, void* area, size_t area_bytes, bool keep,
+                    hipStream_t st) {
   if constexpr (kGridResidentFits<T>(SS))
-    return launch_grid_typed<T, SS, true>(a, NT, lds, dev, exclusive, single, st);
+    return launch_grid_typed<T, SS, true>(a, NT, lds, dev, exclusive, single, area, area_bytes,
+                                          keep, st);
   return fail(GLASS_EUNSUPPORTED, "grid pcg: internal plan error");
 }
 
@@ -794,7 +883,7 @@ template <typename T>
 int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
                 int max_iters, double rel_tol, double abs_tol, int* iters,
                 int* status, T* rho, void* workspace, size_t ws_bytes,
-                bool exclusive, bool single, hipStream_t st) {
+                bool exclusive, bool single, bool keep, hipStream_t st) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   if (!dev.cooperative)
@@ -836,6 +925,8 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
                       std::to_string(wl.total) + " bytes of exchange area, more than the " +
                       std::to_string(kNoAllocScratchBytes) + " bytes of static scratch");
     if (int rc = scratch_address(dev.device, &workspace)) return rc;
+    ws_bytes = kNoAllocScratchBytes;
+    keep = true;  // only these solves ever write the library's own scratch
   }
 
   GridArgs<T> a;
@@ -866,13 +957,18 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   }
   if (res) {
     switch (ss) {
-      case 6: return launch_grid_res<T, 6>(a, NT, lds, dev, exclusive, single, st);
-      case 12: return launch_grid_res<T, 12>(a, NT, lds, dev, exclusive, single, st);
-      case 14: return launch_grid_res<T, 14>(a, NT, lds, dev, exclusive, single, st);
-      default: return launch_grid_res<T, 21>(a, NT, lds, dev, exclusive, single, st);
+      case 6: return launch_grid_res<T, 6>(a, NT, lds, dev, exclusive, single, workspace, ws_bytes,
+                                           keep, st);
+      case 12: return launch_grid_res<T, 12>(a, NT, lds, dev, exclusive, single, workspace,
+                                             ws_bytes, keep, st);
+      case 14: return launch_grid_res<T, 14>(a, NT, lds, dev, exclusive, single, workspace,
+                                             ws_bytes, keep, st);
+      default: return launch_grid_res<T, 21>(a, NT, lds, dev, exclusive, single, workspace,
+                                             ws_bytes, keep, st);
     }
   }
-  return launch_grid_typed<T, 0, false>(a, NT, lds, dev, exclusive, single, st);
+  return launch_grid_typed<T, 0, false>(a, NT, lds, dev, exclusive, single, workspace, ws_bytes,
+                                        keep, st);
 }
 
 }  // namespace
@@ -885,16 +981,16 @@ int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     const void* b, int ss, int kp, int max_iters,
                     double rel_tol, double abs_tol, int* iters, int* status,
                     void* rho, void* workspace, size_t workspace_bytes,
-                    bool exclusive, bool single, hipStream_t stream) {
+                    bool exclusive, bool single, bool keep, hipStream_t stream) {
   if (dt == GLASS_F32)
     return launch_grid<float>((float*)x, (const float*)S, (const float*)Pinv,
                               (const float*)b, ss, kp, max_iters, rel_tol,
                               abs_tol, iters, status, (float*)rho, workspace,
-                              workspace_bytes, exclusive, single, stream);
+                              workspace_bytes, exclusive, single, keep, stream);
   return launch_grid<double>((double*)x, (const double*)S, (const double*)Pinv,
                              (const double*)b, ss, kp, max_iters, rel_tol,
                              abs_tol, iters, status, (double*)rho, workspace,
-                             workspace_bytes, exclusive, single, stream);
+                             workspace_bytes, exclusive, single, keep, stream);
 }
 
 }  // namespace glass

@@ -222,9 +222,22 @@ int glass_pcg_batched_pinned_rows(int state_size, int knot_points,
  *     breakdown test (its step denominator equals p^T S p) and outputs as the
  *     steps above; in floating point it rounds differently.  It holds S and
  *     Pinv rows for one more block-row on each side of a workgroup's range.
+ *   GLASS_GRID_KEEP_WORKSPACE  the caller keeps this workspace for grid
+ *     solves: between this call and the previous grid solve given the same
+ *     workspace address on this device, nothing else wrote it.  The library
+ *     then skips the per-solve clearing of its exchange words (one small
+ *     kernel launch, about 4 us per solve on MI355X): the host remembers, per
+ *     address, which tags earlier solves may have left and starts this
+ *     solve's tags above them.  The first kept solve at an address, and one
+ *     about every 2^32 grid barriers, still clears the whole workspace.
+ *     Without the flag the workspace contents on entry do not matter.
  * Other flag bits return GLASS_EINVAL.
  */
-enum { GLASS_GRID_EXCLUSIVE = 1u, GLASS_GRID_SINGLE_REDUCTION = 2u };
+enum {
+  GLASS_GRID_EXCLUSIVE = 1u,
+  GLASS_GRID_SINGLE_REDUCTION = 2u,
+  GLASS_GRID_KEEP_WORKSPACE = 4u
+};
 size_t glass_pcg_grid_workspace_bytes(int state_size, int knot_points,
                                       glass_dtype dtype);
 int glass_pcg_grid(void* x, const void* S, const void* Pinv, const void* b,
@@ -244,7 +257,9 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same arguments (minus workspace and
  * workspace_bytes), flags, steps, outputs and results (bit for bit) as
- * glass_pcg_grid_ex.  The exchange area lives in a static device array of
+ * glass_pcg_grid_ex; the array is always kept for grid solves (as with
+ * GLASS_GRID_KEEP_WORKSPACE), so after its first call on a device no
+ * clearing kernel is launched.  The exchange area lives in a static device array of
  * GLASS_PCG_GRID_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
  * device it runs on until the process ends; the call itself allocates and
  * frees nothing.  It needs 256 + 2*G*2*w*8 + 2*G*4*state_size*w*8 bytes

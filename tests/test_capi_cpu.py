@@ -107,8 +107,8 @@ def test_grid_argument_errors_and_workspace_size(lib):
         return lib.glass_pcg_grid_ex(FAKE, FAKE, FAKE, FAKE, 12, 8192, 10, 1e-10, 0.0,
                                      FAKE, None, None, ctypes.c_void_p(0x100000), ws, 1,
                                      flags, None)
-    assert grid_ex(4) == EINVAL  # unknown flag bit
-    assert grid_ex(1 | 2 | 8) == EINVAL
+    assert grid_ex(8) == EINVAL  # unknown flag bit
+    assert grid_ex(1 | 2 | 16) == EINVAL
     assert grid_ex(0x80000000) == EINVAL
 
 
@@ -164,5 +164,5 @@ def test_grid_noalloc_argument_errors(lib):
     assert na(iters=None) == EINVAL
     assert na(st=ctypes.c_void_p(0x100002)) == EINVAL
     assert na(dt=2) == EINVAL
-    assert na(flags=4) == EINVAL
+    assert na(flags=8) == EINVAL
     assert b"flag" in lib.glass_last_error()

@@ -190,3 +190,63 @@ def test_grid_timeout_path_reports_and_drains(gpu, monkeypatch, variant):
     res = grid_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, single=variant)
     assert res[2][0] == gpu.CONVERGED
     assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float64)
+
+
+def grid_ws(glass, inp, ss, kp, max_iters, rel_tol, abs_tol, ws, keep, single, exclusive=True):
+    t = {k: to_dev(v) for k, v in inp.items()}
+    x = t["x0"].clone()
+    iters = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    rho = torch.zeros(2, dtype=x.dtype, device="cuda")
+    glass.pcg_grid(x, t["S"], t["Pinv"], t["b"], ss, kp, max_iters, rel_tol, abs_tol,
+                   iters, ws, status, rho, exclusive=exclusive, single_reduction=single,
+                   keep_workspace=keep)
+    torch.cuda.synchronize()
+    return (x.cpu().numpy(), iters.cpu().numpy(), status.cpu().numpy(),
+            rho.cpu().numpy().reshape(1, 2))
+
+
+def test_grid_keep_workspace_sequence(gpu, monkeypatch, variant):
+    """GLASS_GRID_KEEP_WORKSPACE: one workspace serves, in turn, the fp64
+    chain, a solve that stops after its first barrier (rho_init = 0), the
+    chain again, a smaller fp32 chain on another grid size, a forced timeout
+    and a normal solve after it.  No clearing kernel runs after the first
+    solve, so every stale word left there must fail its tag check: each
+    result equals the same solve with the per-solve clearing (bit for bit),
+    and the chain meets the oracle."""
+    w = workloads.WORKLOADS[4]
+    chain = workloads.generate(w)
+    zero = dict(chain, b=np.zeros_like(chain["b"]))
+    rng = np.random.default_rng(909)
+    S, D = workloads.random_spd_strips(rng, 1, 6, 300, 0.1, np.float32)
+    small = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, np.float32),
+             "b": rng.standard_normal((1, 1800)).astype(np.float32),
+             "x0": np.zeros((1, 1800), np.float32)}
+    nbytes = max(gpu.pcg_grid_workspace_bytes(w.ss, w.kp, torch.float64),
+                 gpu.pcg_grid_workspace_bytes(6, 300, torch.float32))
+    kept = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    fresh = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    seq = [("chain", chain, w.ss, w.kp, w.max_iters, w.rel_tol, None),
+           ("rho_init = 0", zero, w.ss, w.kp, w.max_iters, w.rel_tol, None),
+           ("chain again", chain, w.ss, w.kp, w.max_iters, w.rel_tol, None),
+           ("small fp32 chain", small, 6, 300, 500, 1e-7, None),
+           ("forced timeout", chain, w.ss, w.kp, w.max_iters, w.rel_tol, "0"),
+           ("chain after the timeout", chain, w.ss, w.kp, w.max_iters, w.rel_tol, None),
+           ("small fp32 chain again", small, 6, 300, 500, 1e-7, None)]
+    for name, inp, ss, kp, mi, rel, spin in seq:
+        say("grid kept workspace: %s single=%s" % (name, variant))
+        if spin is not None:
+            monkeypatch.setenv("GLASS_AMD_GRID_SPIN_LIMIT", spin)
+        got = grid_ws(gpu, inp, ss, kp, mi, rel, 0.0, kept, True, variant)
+        if spin is not None:
+            assert got[2][0] == gpu.GRID_TIMEOUT, got[2]
+            monkeypatch.delenv("GLASS_AMD_GRID_SPIN_LIMIT")
+            continue
+        ref = grid_ws(gpu, inp, ss, kp, mi, rel, 0.0, fresh, False, variant)
+        for u, v in zip(ref, got):
+            np.testing.assert_array_equal(u, v)
+        assert got[2][0] == gpu.CONVERGED
+        if name == "rho_init = 0":
+            assert got[1][0] == 0
+    res = grid_ws(gpu, chain, w.ss, w.kp, w.max_iters, w.rel_tol, 0.0, kept, True, variant)
+    assert_pcg_parity(chain, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, res, np.float64)
