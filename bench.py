@@ -383,7 +383,8 @@ def roofline_alu(flops, nbytes, avg_ms, traffic, dtype):
     return out
 
 
-def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
+def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic,
+              cooperative=True):
     cfg = CONFIG_OF[key]
     w = workload_of(key)
     inp = workloads.generate(w)
@@ -475,10 +476,11 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         out["launch"] = "exclusive"
         out["workspace"] = "kept (GLASS_GRID_KEEP_WORKSPACE: no per-solve clearing kernel)"
         out["us_per_iteration"] = avg_ms * 1e3 / max(1, int(it[0]))
-        for k in range(min(10, len(xs))):
-            xs[k].zero_()
-        out["kernel_ms_isolated_cooperative"] = isolated_ms(
-            torch, lambda k: run(xs[k], exclusive=False), reps=min(10, len(xs)))
+        if cooperative:
+            for k in range(min(10, len(xs))):
+                xs[k].zero_()
+            out["kernel_ms_isolated_cooperative"] = isolated_ms(
+                torch, lambda k: run(xs[k], exclusive=False), reps=min(10, len(xs)))
     if with_cpu:
         import oracle
         nt = 1 if grid else cpu_threads()
@@ -653,6 +655,10 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=4.0,
                     help="seconds of oracle time per workload baseline")
     ap.add_argument("--calibration-copy", action="store_true")
+    ap.add_argument("--no-cooperative", action="store_true",
+                    help="skip timing the grid solve's cooperative launch (for profiler runs: "
+                         "rocprofv3 ends with a segmentation fault at process exit after "
+                         "cooperative launches)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--pmc-commands", nargs=2, default=("?", "?"),
                     metavar=("FETCH_CMD", "WRITE_CMD"))
@@ -690,7 +696,8 @@ def main():
             # pcg3_stream runs pcg3's inputs in another placement: no second
             # CPU baseline
             res[name] = bench_pcg(torch, glass, name, args.steps, args.warmup, budget,
-                                  with_cpu and name not in NO_HYBRID | MULTI, traffic)
+                                  with_cpu and name not in NO_HYBRID | MULTI, traffic,
+                                  cooperative=not args.no_cooperative)
         print("[bench] %s done: %s" % (name, json.dumps(res[name])[:300]), file=sys.stderr,
               flush=True)
     if args.calibration_copy:

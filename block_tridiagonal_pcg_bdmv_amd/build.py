@@ -64,5 +64,13 @@ def build(verbose: bool = True, out: str = LIB, defines=()) -> str:
     return out
 
 
+# The debug build whose kernels first fill their LDS with NaN words (run the
+# GPU parity tests against it with GLASS_AMD_LIBRARY pointing at it).
+LIB_LDS_NAN = os.path.join(PKG, "libglass_amd_ldsnan.so")
+
+
 if __name__ == "__main__":
-    build()
+    if "--lds-nan-fill" in sys.argv[1:]:
+        build(out=LIB_LDS_NAN, defines=("GLASS_AMD_LDS_NAN_FILL=1",))
+    else:
+        build()

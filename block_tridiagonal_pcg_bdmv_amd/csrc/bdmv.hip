@@ -48,7 +48,7 @@ template <typename T, int SS>
 __global__ void __launch_bounds__(kBdmvMaxThreads)
 bdmv_kernel(T* __restrict__ y, const T* __restrict__ S,
             const T* __restrict__ v, int ss_rt, int kp,
-            int tiles_per_problem, int vec) {
+            int tiles_per_problem, int vec, unsigned lds_bytes) {
   const int ss = SS > 0 ? SS : ss_rt;
   const int W = 3 * ss;
   const int n = kp * ss;
@@ -63,6 +63,7 @@ bdmv_kernel(T* __restrict__ y, const T* __restrict__ S,
   const int vcount = (br_hi - br_lo + 3) * ss;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_debug_fill(smem_raw, lds_bytes);
   // s_mat: rows * W matrix entries, row-major (padded to whole vectors);
   // s_win: v[br_lo*ss, (br_hi+3)*ss).
   constexpr int U = SS > 0 ? (3 * SS * (int)sizeof(T) + 15) / 16 : 1;
@@ -158,14 +159,9 @@ int launch_typed(T* y, const T* S, const T* v, int ss, int kp, int n_problems,
   if (blocks > INT_MAX) return fail(GLASS_EUNSUPPORTED, "bdmv grid too large");
   const int vec = aligned(S, 16) && ((n * W * (long long)sizeof(T)) % 16 == 0);
   auto kern = bdmv_kernel<T, SS>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(bdmv)");
-  }
+  if (int rc = allow_dynamic_lds((const void*)kern, lds)) return rc;
   hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(NT), lds, stream, y, S,
-                     v, ss, kp, (int)tiles, vec);
+                     v, ss, kp, (int)tiles, vec, (unsigned)lds);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "bdmv launch");
   return GLASS_OK;

@@ -74,6 +74,7 @@ struct BdsvArgs {
   int kp;
   int n_problems;
   int strip_vecs;  // 16-byte vectors per lane for one strip (LDS stage)
+  unsigned lds_bytes;  // dynamic LDS of the launch (debug fill)
 };
 
 // 16-byte vectors per lane that hold one strip.
@@ -94,6 +95,7 @@ bdsv_kernel(BdsvArgs<T> a) {
   const long long prob = blockIdx.x;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_debug_fill(smem_raw, a.lds_bytes);
   T* stage = reinterpret_cast<T*>(smem_raw);            // strip: ss x 3ss (+pad)
   T* GU = stage + (size_t)NVS * 64 * (16 / sizeof(T));  // (WS ? 1 : kp) x ss x (ss+1)
   T* bv = GU + (size_t)(WS ? 1 : kp) * SS * NGU;        // b_br (ss)
@@ -337,6 +339,8 @@ bdsv_rows_kernel(BdsvArgs<T> a) {
   const int lane = threadIdx.x;
   const int r = lane >> 4, i = lane & 15;
   const long long p0 = (long long)blockIdx.x * kRowsProblemsPerWave;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_debug_fill(smem_raw, a.lds_bytes);
   const int nlive = (int)((long long)a.n_problems - p0 < kRowsProblemsPerWave
                               ? (long long)a.n_problems - p0
                               : kRowsProblemsPerWave);
@@ -357,7 +361,6 @@ bdsv_rows_kernel(BdsvArgs<T> a) {
     rW = make_rsrc(a.ws + p0 * n * NGU, nlive * n * NGU * ES);
     oW = act ? (r * n + i) * NGU * ES : INT_MAX / 2;
   }
-  extern __shared__ __align__(16) unsigned char smem_raw[];
   T* GUl = reinterpret_cast<T*>(smem_raw);  // !WS: [kp][4*ss][ss+1]
 
   T sr[SW], sb;
@@ -486,13 +489,11 @@ bdsv_rows_kernel(BdsvArgs<T> a) {
 }
 
 template <typename T, int SS, bool WS>
-int launch_rows_kernel(const BdsvArgs<T>& a, size_t lds, hipStream_t st) {
+int launch_rows_kernel(const BdsvArgs<T>& a_in, size_t lds, hipStream_t st) {
+  BdsvArgs<T> a = a_in;
+  a.lds_bytes = (unsigned)lds;
   auto kern = bdsv_rows_kernel<T, SS, WS>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(bdsv rows)");
-  }
+  if (int rc = allow_dynamic_lds((const void*)kern, lds)) return rc;
   const unsigned grid =
       (unsigned)(((long long)a.n_problems + kRowsProblemsPerWave - 1) / kRowsProblemsPerWave);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(64), lds, st, a);
@@ -506,13 +507,11 @@ int launch_rows_kernel(const BdsvArgs<T>& a, size_t lds, hipStream_t st) {
 // ---------------------------------------------------------------------------
 
 template <typename T, int SS, bool WS>
-int launch_kernel(const BdsvArgs<T>& a, size_t lds, hipStream_t st) {
+int launch_kernel(const BdsvArgs<T>& a_in, size_t lds, hipStream_t st) {
+  BdsvArgs<T> a = a_in;
+  a.lds_bytes = (unsigned)lds;
   auto kern = bdsv_kernel<T, SS, WS>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(bdsv)");
-  }
+  if (int rc = allow_dynamic_lds((const void*)kern, lds)) return rc;
   hipLaunchKernelGGL(kern, dim3((unsigned)a.n_problems), dim3(64), lds, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "bdsv launch");

@@ -5,8 +5,11 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
+#include <utility>
 #include <vector>
 
 #include "internal.hpp"
@@ -55,6 +58,51 @@ int current_device_info(DeviceInfo* out) {
     d = q;
   }
   *out = d;
+  return GLASS_OK;
+}
+
+namespace {
+std::mutex g_launch_mutex;
+// (device, kernel, threads, lds) -> workgroups per CU
+std::map<std::tuple<int, const void*, int, size_t>, int> g_occupancy;
+// (device, kernel) -> largest dynamic LDS allowed so far
+std::map<std::pair<int, const void*>, size_t> g_lds_allowed;
+}  // namespace
+
+int kernel_occupancy(const void* kernel, int threads, size_t lds, int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  const auto key = std::make_tuple(dev, kernel, threads, lds);
+  {
+    std::lock_guard<std::mutex> lock(g_launch_mutex);
+    auto it = g_occupancy.find(key);
+    if (it != g_occupancy.end()) {
+      *out = it->second;
+      return GLASS_OK;
+    }
+  }
+  int v = 0;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, lds);
+  if (e != hipSuccess) return fail_hip(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+  std::lock_guard<std::mutex> lock(g_launch_mutex);
+  g_occupancy[key] = v;
+  *out = v;
+  return GLASS_OK;
+}
+
+int allow_dynamic_lds(const void* kernel, size_t bytes) {
+  if (bytes <= 64 * 1024) return GLASS_OK;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail_hip(e, "hipGetDevice");
+  const auto key = std::make_pair(dev, kernel);
+  std::lock_guard<std::mutex> lock(g_launch_mutex);
+  size_t& have = g_lds_allowed[key];
+  if (have >= bytes) return GLASS_OK;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(dynamic LDS)");
+  have = bytes;
   return GLASS_OK;
 }
 

@@ -182,6 +182,25 @@ __device__ __forceinline__ void load_row_regs(T (&reg)[W], const T* __restrict__
   }
 }
 
+// Debug builds (-DGLASS_AMD_LDS_NAN_FILL=1): every kernel starts by filling
+// its whole dynamic LDS (`bytes` at `base`) with all-ones words, a NaN as
+// float and as double, and synchronising the workgroup, so that a read of
+// LDS before it is written turns the results into NaN.  Every thread of the
+// workgroup must call it.  Release builds compile it to nothing.
+#ifndef GLASS_AMD_LDS_NAN_FILL
+#define GLASS_AMD_LDS_NAN_FILL 0
+#endif
+__device__ __forceinline__ void lds_debug_fill(unsigned char* base, unsigned bytes) {
+#if GLASS_AMD_LDS_NAN_FILL
+  unsigned* w = reinterpret_cast<unsigned*>(base);
+  for (unsigned i = threadIdx.x; i < bytes / 4u; i += blockDim.x) w[i] = 0xFFFFFFFFu;
+  __syncthreads();
+#else
+  (void)base;
+  (void)bytes;
+#endif
+}
+
 // Round-to-nearest a*b as its own operation (never fused into a later add).
 template <typename T>
 __device__ __forceinline__ T mul_unfused(T a, T b) {

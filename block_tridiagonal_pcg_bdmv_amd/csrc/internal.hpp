@@ -25,6 +25,14 @@ struct DeviceInfo {
 // Properties of the current HIP device (queried once per device).
 int current_device_info(DeviceInfo* out);
 
+// Per-device caches of launch facts that do not change between calls:
+// kernel_occupancy = hipOccupancyMaxActiveBlocksPerMultiprocessor for
+// (kernel, block threads, dynamic LDS) on the current device;
+// allow_dynamic_lds raises a kernel's dynamic-LDS limit to `bytes` (once per
+// device for each larger size; sizes up to 64 KB need nothing).
+int kernel_occupancy(const void* kernel, int threads, size_t lds, int* out);
+int allow_dynamic_lds(const void* kernel, size_t bytes);
+
 // Optional launch-shape override from the environment (tests and tuning
 // sweeps): returns `fallback` when `name` is unset or not a positive integer.
 int env_int(const char* name, int fallback);

@@ -107,6 +107,7 @@ struct PcgArgs {
                     // chunk 0 of Pinv in the registers that leaves free
   int ppacked;      // Pinv is packed D blocks, [kp*ss][ss] per problem (read
                     // by kStream; the other modes fix it at compile time)
+  unsigned lds_bytes;  // dynamic LDS of the launch (debug fill)
 };
 
 // Placements of the matrices (see the header).
@@ -184,6 +185,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   const bool vec = a.vec != 0;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_debug_fill(smem_raw, a.lds_bytes);
   T* p_pad = reinterpret_cast<T*>(smem_raw);
   T* r_pad = p_pad + pad_len;
   const int nchunks = (n + 63) / 64;
@@ -925,18 +927,15 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
 }
 
 template <typename T, int SS, int RPT, int MODE>
-int launch_one(const PcgArgs<T>& a, int n_problems, const Plan& pl,
+int launch_one(const PcgArgs<T>& a_in, int n_problems, const Plan& pl,
                hipStream_t stream) {
+  PcgArgs<T> a = a_in;
+  a.lds_bytes = (unsigned)pl.lds;
   auto kern = pcg_batched_kernel<T, SS, RPT, MODE>;
-  if (pl.lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)pl.lds);
-    if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(pcg)");
-  }
+  if (int rc = allow_dynamic_lds((const void*)kern, pl.lds)) return rc;
   if (env_int("GLASS_AMD_VERBOSE", 0) > 0) {
     int per_cu = 0;
-    (void)hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, pl.NW * 64, pl.lds);
+    (void)kernel_occupancy((const void*)kern, pl.NW * 64, pl.lds, &per_cu);
     std::fprintf(stderr,
                  "glass pcg plan: ss=%d kp=%d mode=%d waves=%d rows/lane=%d "
                  "lds=%zu stage=%d pinned=%d workgroups/CU=%d\n",
@@ -976,11 +975,12 @@ int launch_res(const PcgArgs<T>& a_in, int n_problems, const Plan& pl_in, hipStr
       // The Pinv stage only where it keeps the occupancy of the plain kernel.
       int per_d = 0, per_p = 0;
       const size_t lds_p = lds_bytes<T>(a.ss, a.kp, pl.NW, 0);
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &per_d, pcg_batched_kernel<T, SS, 1, kResidentDma>, pl.NW * 64, pl.lds) ==
-              hipSuccess &&
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(
-              &per_p, pcg_batched_kernel<T, SS, 1, kResident>, pl.NW * 64, lds_p) == hipSuccess &&
+      if (allow_dynamic_lds((const void*)pcg_batched_kernel<T, SS, 1, kResidentDma>, pl.lds) ==
+              GLASS_OK &&
+          kernel_occupancy((const void*)pcg_batched_kernel<T, SS, 1, kResidentDma>, pl.NW * 64,
+                           pl.lds, &per_d) == GLASS_OK &&
+          kernel_occupancy((const void*)pcg_batched_kernel<T, SS, 1, kResident>, pl.NW * 64,
+                           lds_p, &per_p) == GLASS_OK &&
           per_d >= per_p && per_d > 0)
         return launch_one<T, SS, 1, kResidentDma>(a, n_problems, pl, st);
       pl.resdma = false;
@@ -996,10 +996,10 @@ int launch_res(const PcgArgs<T>& a_in, int n_problems, const Plan& pl_in, hipStr
     if (pl.res_auto && pl.RPT == 1 && nw2 * 64 <= max_threads_for(2, M) &&
         current_device_info(&dev) == GLASS_OK && n_problems > dev.cu_count) {
       int per1 = 0, per2 = 0;
-      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per1, pcg_batched_kernel<T, SS, 1, M>,
-                                                       pl.NW * 64, pl.lds) == hipSuccess &&
-          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per2, pcg_batched_kernel<T, SS, 2, M>,
-                                                       nw2 * 64, pl.lds) == hipSuccess &&
+      if (kernel_occupancy((const void*)pcg_batched_kernel<T, SS, 1, M>, pl.NW * 64, pl.lds,
+                           &per1) == GLASS_OK &&
+          kernel_occupancy((const void*)pcg_batched_kernel<T, SS, 2, M>, nw2 * 64, pl.lds,
+                           &per2) == GLASS_OK &&
           per2 > per1) {
         pl.RPT = 2;
         pl.NW = nw2;

@@ -95,6 +95,7 @@ struct GridArgs {
   unsigned spin_limit;    // poll rounds before a wait gives up
   unsigned tag_base;      // barrier b of this solve is tagged tag_base + b; a
                           // timeout stores tag_base into flags[0]
+  unsigned lds_bytes;     // dynamic LDS of the launch (debug fill)
 };
 
 typedef unsigned long long u64;
@@ -427,6 +428,7 @@ pcg_grid_kernel(GridArgs<T> a) {
   const int n_edge = 4 * ss;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_debug_fill(smem_raw, a.lds_bytes);
   T* p_loc = reinterpret_cast<T*>(smem_raw);  // block-rows A-2 .. B+1
   T* r_loc = p_loc + loc_len;                 // same indexing
   T* edge_lds = r_loc + loc_len;              // [4*ss] z of A, A+1, B-2, B-1
@@ -634,6 +636,7 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
   const int n_edge = 4 * ss;
 
   extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_debug_fill(smem_raw, a.lds_bytes);
   T* w_loc = reinterpret_cast<T*>(smem_raw);  // block-rows A-2 .. B+1
   T* m_loc = w_loc + loc_len;                 // same indexing
   T* edge_lds = m_loc + loc_len;              // [4*ss] values of A, A+1, B-2, B-1
@@ -808,17 +811,13 @@ int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
                       bool exclusive, bool single, void* area, size_t area_bytes, bool keep,
                       hipStream_t st) {
   auto kern = single ? pcg_grid_cg1_kernel<T, SS, RES> : pcg_grid_kernel<T, SS, RES>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e != hipSuccess) return fail_hip(e, "hipFuncSetAttribute(grid)");
-  }
+  if (int rc = allow_dynamic_lds((const void*)kern, lds)) return rc;
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, NT, lds);
-  if (e != hipSuccess) return fail_hip(e, "occupancy query (grid)");
+  if (int rc = kernel_occupancy((const void*)kern, NT, lds, &per_cu)) return rc;
+  hipError_t e = hipSuccess;
   if ((long long)per_cu * dev.cu_count < a.G)
     return fail(GLASS_ECOOP, "grid pcg: workgroups cannot all be co-resident");
+  a.lds_bytes = (unsigned)lds;
   // Tag base and reset (see the exchange rules at the top of the file).
   const EpochPlan ep = epoch_begin(dev.device, area, keep, a.max_iters);
   a.tag_base = ep.base;

@@ -53,6 +53,7 @@ struct MultiArgs {
   T rel_tol;
   T abs_tol;
   int wide;  // 16-byte aligned matrices: widest row loads
+  unsigned lds_bytes;  // dynamic LDS of the launch (debug fill)
 };
 
 // Sum over the LPP lanes of one problem (all lanes of the wave take part):
@@ -83,11 +84,12 @@ pcg_multi_kernel(MultiArgs<T> a) {
   const int sub = lane / LPP;  // problem within the wave
   const int l = lane % LPP;
   const long long prob = ((long long)blockIdx.x * (kMultiThreads / 64) + wave) * PPW + sub;
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  lds_debug_fill(smem_raw, a.lds_bytes);
   // A wave with no problem leaves at once (wave-uniform).
   if (((long long)blockIdx.x * (kMultiThreads / 64) + wave) * PPW >= a.n_problems) return;
   const bool has_prob = prob < a.n_problems;
 
-  extern __shared__ __align__(16) unsigned char smem_raw[];
   T* p_pad = reinterpret_cast<T*>(smem_raw) + (size_t)(wave * PPW + sub) * 2 * pad_len;
   T* r_pad = p_pad + pad_len;
 
@@ -277,10 +279,12 @@ bool multi_shape(int ss, int kp, int* lpp, int* rpl) {
 }
 
 template <typename T, int LPP, int RPL>
-int launch_multi_one(const MultiArgs<T>& a, hipStream_t st) {
+int launch_multi_one(const MultiArgs<T>& a_in, hipStream_t st) {
   constexpr int ppb = (kMultiThreads / 64) * (64 / LPP);
-  const int blocks = (a.n_problems + ppb - 1) / ppb;
-  const size_t lds = (size_t)ppb * 2 * (a.kp + 2) * 6 * sizeof(T);
+  const int blocks = (a_in.n_problems + ppb - 1) / ppb;
+  const size_t lds = (size_t)ppb * 2 * (a_in.kp + 2) * 6 * sizeof(T);
+  MultiArgs<T> a = a_in;
+  a.lds_bytes = (unsigned)lds;
   hipLaunchKernelGGL((pcg_multi_kernel<T, 6, LPP, RPL>), dim3((unsigned)blocks),
                      dim3(kMultiThreads), lds, st, a);
   const hipError_t e = hipGetLastError();
