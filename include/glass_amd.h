@@ -50,7 +50,15 @@
 extern "C" {
 #endif
 
+/* Element type of the floating-point arrays.  In C++ the enum has a fixed
+ * int underlying type, so any int a C caller passes is a value of the type
+ * (and the library rejects the others with GLASS_EINVAL) rather than
+ * undefined behaviour; the ABI is an int either way. */
+#ifdef __cplusplus
+typedef enum : int { GLASS_F32 = 0, GLASS_F64 = 1 } glass_dtype;
+#else
 typedef enum { GLASS_F32 = 0, GLASS_F64 = 1 } glass_dtype;
+#endif
 
 enum {
   GLASS_OK = 0,
