@@ -55,9 +55,9 @@ METRIC = "PCG solves/sec (batched) and bdmv HBM GB/s as fraction of MI355X peak"
 # The kernel each workload spends its time in (a substring of the demangled
 # name rocprofv3 reports).
 KERNEL_OF = {
-    "pcg0": "pcg_batched_kernel<float, 6, 1, 0>",
+    "pcg0": "pcg_batched_kernel<float, 6, 1, 10>",
     "bdmv1": "bdmv_kernel<float, 14>",
-    "pcg2": "pcg_batched_kernel<float, 14, 1, 0>",
+    "pcg2": "pcg_batched_kernel<float, 14, 1, 10>",
     "pcg3": "pcg_batched_kernel<float, 21, 3, 7>",
     "pcg3_stream": "pcg_batched_kernel<float, 21, 3, 1>",
     "grid4": "pcg_grid_kernel<double, 12,",
@@ -71,8 +71,9 @@ KERNEL_OF = {
     "grid4_sr": "pcg_grid_cg1_kernel<double, 12,",
     "grid4_f32_sr": "pcg_grid_cg1_kernel<float, 12,",
     "pcg0_multi": "pcg_multi_kernel<float, 6, 32, 6>",
-    "pcg0_b4096": "pcg_batched_kernel<float, 6, 1, 0>",
+    "pcg0_b4096": "pcg_batched_kernel<float, 6, 1, 10>",
     "pcg0_b4096_multi": "pcg_multi_kernel<float, 6, 32, 6>",
+    "pcg3_unaligned": "pcg_batched_kernel<float, 21, 3, 7>",
 }
 # Workload inputs: the five configurations; bdsv2 is the direct solve of the
 # same systems as pcg2 (ss=14, kp=32, 4096 problems); pcg2_f64 and grid4_f32
@@ -80,7 +81,7 @@ KERNEL_OF = {
 CONFIG_OF = {"pcg0": 0, "bdmv1": 1, "pcg2": 2, "pcg3": 3, "pcg3_stream": 3, "grid4": 4, "bdsv2": 2,
              "pcg2_f64": 2, "grid4_f32": 4, "pcg2_pd": 2, "pcg3_pd": 3, "pcg2_pdp": 2,
              "pcg3_pdp": 3, "grid4_sr": 4, "grid4_f32_sr": 4, "pcg0_multi": 0, "pcg0_b4096": 0,
-             "pcg0_b4096_multi": 0}
+             "pcg0_b4096_multi": 0, "pcg3_unaligned": 3}
 # Workloads run with GLASS_PCG_PINV_BLOCK_DIAGONAL (their Pinv is block-Jacobi,
 # so the assertion holds): pcg2_pd and pcg3_pd are the ss=14 and ss=21
 # workloads with the hint.
@@ -96,6 +97,11 @@ NO_HYBRID = {"pcg3_stream"}
 # ss=6 systems at their 64 problems and at 4096 (pcg0_b4096 is the same 4096
 # problems in the default workgroup placement).
 MULTI = {"pcg0_multi", "pcg0_b4096_multi"}
+# Workloads whose matrices sit at addresses aligned to the element size only
+# (4 bytes past a 16-byte boundary): the S-resident placement loads such rows
+# from the 16-byte boundary below them, so this row checks that it costs
+# nothing against the aligned pcg3.
+UNALIGNED = {"pcg3_unaligned"}
 # Grid workloads run in the single-reduction form (GLASS_GRID_SINGLE_REDUCTION).
 SINGLE_RED = {"grid4_sr", "grid4_f32_sr"}
 VARIANT_OF = {
@@ -111,6 +117,7 @@ VARIANT_OF = {
     "pcg0_multi": dict(name="pcg_ss6_kp32_b64_f32_several_per_wave"),
     "pcg0_b4096": dict(name="pcg_ss6_kp32_b4096_f32", n_problems=4096),
     "pcg0_b4096_multi": dict(name="pcg_ss6_kp32_b4096_f32_several_per_wave", n_problems=4096),
+    "pcg3_unaligned": dict(name="pcg_ss21_kp64_b2048_f32_element_aligned"),
     "grid4_f32": dict(name="grid_pcg_ss12_kp8192_f32", dtype=np.float32, rel_tol=1e-7),
 }
 
@@ -243,7 +250,11 @@ def _per_dispatch(path, counter):
     return out
 
 
-def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd, out=TRAFFIC_FILE):
+def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd, out=TRAFFIC_FILE, workloads=None):
+    """Calibrated bytes per dispatch for each profiled workload.  workloads
+    lists the workloads the profiled command ran (default: all); a kernel
+    name that two of them share gets no row, since its counters mix them."""
+    keys = list(KERNEL_OF) if workloads is None else list(workloads)
     fetch = _per_dispatch(fetch_csv, "FETCH_SIZE")
     write = _per_dispatch(write_csv, "WRITE_SIZE")
 
@@ -266,6 +277,8 @@ def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd, out=TRAFFIC_FILE):
         "",
         "WRITE_SIZE run: `%s`" % write_cmd,
         "",
+        "Workloads profiled: %s" % ",".join(keys),
+        "",
         "Calibration: a negation kernel reading and writing %d bytes reads "
         "FETCH_SIZE = %.1f KiB and WRITE_SIZE = %.1f KiB per dispatch, so "
         "bytes = FETCH_SIZE KiB x 1024 x %.4f + WRITE_SIZE KiB x 1024 x %.4f."
@@ -275,7 +288,10 @@ def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd, out=TRAFFIC_FILE):
         "WRITE_SIZE KiB/dispatch | calibrated bytes/dispatch |",
         "|---|---|---|---|---|---|",
     ]
-    for key, sub in KERNEL_OF.items():
+    for key in keys:
+        sub = KERNEL_OF[key]
+        if sum(1 for k2 in keys if KERNEL_OF[k2] == sub) > 1:
+            continue
         try:
             f, nd = find(fetch, sub)
             wv, _ = find(write, sub)
@@ -392,6 +408,13 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic,
     packed = key in PINV_PACKED
     S = torch.from_numpy(inp["S"]).to(dev)
     P = torch.from_numpy(inp["Pinv"]).to(dev)
+    if key in UNALIGNED:  # the same values 4 bytes past a 16-byte boundary
+        def shifted(t):
+            store = torch.empty(t.numel() + 1, dtype=t.dtype, device=dev)
+            view = store[1:].view(t.shape)
+            view.copy_(t)
+            return view
+        S, P = shifted(S), shifted(P)
     B = w.n_problems
     if packed:  # the D blocks alone, [B, kp, ss, ss]
         P = P.reshape(B, w.kp, w.ss, 3 * w.ss)[:, :, :, w.ss:2 * w.ss].contiguous()
@@ -444,11 +467,12 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic,
     # S and Pinv count once if they stay on chip (the grid solve and the
     # batched resident placement), else once per pass.
     placement = None if grid else glass.pcg_batched_placement(
-        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd, pinv_diagonal_blocks=packed)
+        w.ss, w.kp, S.dtype, aligned16=key not in UNALIGNED, pinv_block_diagonal=pd,
+        pinv_diagonal_blocks=packed)
     resident = grid or placement in (glass.PLACEMENT_RESIDENT, glass.PLACEMENT_SEVERAL_PER_WAVE) \
         or ("S" if placement == glass.PLACEMENT_S_RESIDENT else False)
     pinned = glass.pcg_batched_pinned_rows(
-        w.ss, w.kp, S.dtype, pinv_block_diagonal=pd,
+        w.ss, w.kp, S.dtype, aligned16=key not in UNALIGNED, pinv_block_diagonal=pd,
         pinv_diagonal_blocks=packed) if resident == "S" else 0
     nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed, pinned_rows=pinned)
     compulsory = compulsory_bytes_pcg(w, B, pinv_diag=pd or packed)
@@ -664,7 +688,9 @@ def main():
                     metavar=("FETCH_CMD", "WRITE_CMD"))
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], *args.pmc_commands)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], *args.pmc_commands,
+                      workloads=None if args.workloads == "all" else
+                      [s.strip() for s in args.workloads.split(",") if s.strip()])
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: there is no multi-GPU path (the batched "
@@ -696,7 +722,7 @@ def main():
             # pcg3_stream runs pcg3's inputs in another placement: no second
             # CPU baseline
             res[name] = bench_pcg(torch, glass, name, args.steps, args.warmup, budget,
-                                  with_cpu and name not in NO_HYBRID | MULTI, traffic,
+                                  with_cpu and name not in NO_HYBRID | MULTI | UNALIGNED, traffic,
                                   cooperative=not args.no_cooperative)
         print("[bench] %s done: %s" % (name, json.dumps(res[name])[:300]), file=sys.stderr,
               flush=True)

@@ -147,7 +147,17 @@ __device__ __forceinline__ void copy_to_lds(T* __restrict__ dst,
     for (; q < nv; q += nthreads) d4[q] = load16<STREAM>(s4 + q);
     for (int e = nv * E + tid; e < count; e += nthreads) dst[e] = src[e];
   } else {
-    for (int e = tid; e < count; e += nthreads) dst[e] = src[e];
+    // Element loads (unaligned source): U loads in flight before the stores.
+    constexpr int U = 8;
+    int e = tid;
+    for (; e + (U - 1) * nthreads < count; e += U * nthreads) {
+      T t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) t[u] = src[e + u * nthreads];
+#pragma unroll
+      for (int u = 0; u < U; ++u) dst[e + u * nthreads] = t[u];
+    }
+    for (; e < count; e += nthreads) dst[e] = src[e];
   }
 }
 

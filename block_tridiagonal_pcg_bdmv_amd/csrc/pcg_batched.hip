@@ -318,12 +318,21 @@ pcg_batched_kernel(PcgArgs<T> a) {
   // write zeros without a fetch.  The loads use no registers once issued, so
   // the next Pinv chunk is in flight while the wave multiplies, reduces and
   // waits at barriers.
+  //
+  // Matrices aligned to the element size only: the chunk is loaded from the
+  // 16-byte boundary at or below its first byte (the same 16-byte granule of
+  // the caller's allocation), so it lands `shift` bytes into dst, and readers
+  // add the shift (stage_shift).  64 rows of 3ss elements are a multiple of
+  // 16 bytes, so the shift is the same for every chunk of one matrix of one
+  // problem; the host uses this only where the stage has the spare bytes.
   auto dma_rows_to = [&](const T* __restrict__ gM, int k, T* dst) {
     if constexpr (HYBS) {
       const int r0 = chunk_r0(k);
       const bool has = r0 < n;
-      const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) : 0;
-      const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? gM + (long long)r0 * W : gM, nbytes);
+      const unsigned char* src = reinterpret_cast<const unsigned char*>(gM + (long long)r0 * W);
+      const int shift = (int)(reinterpret_cast<uintptr_t>(src) & 15u);
+      const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) + shift : 0;
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? src - shift : src, nbytes);
       unsigned char* st = reinterpret_cast<unsigned char*>(dst);
 #pragma unroll
       for (int u = 0; u < NV; ++u)
@@ -333,6 +342,11 @@ pcg_batched_kernel(PcgArgs<T> a) {
     }
   };
   auto dma_chunk_to = [&](int k, T* dst) { dma_rows_to(gP, k, dst); };
+  // Where a matrix's chunk starts inside the stage it was loaded into.
+  auto stage_shift = [&](const T* __restrict__ gM, const T* buf) {
+    return reinterpret_cast<const T*>(reinterpret_cast<const unsigned char*>(buf) +
+                                      (reinterpret_cast<uintptr_t>(gM) & 15u));
+  };
   auto dma_chunk = [&](int k) { dma_chunk_to(k, stage); };
 
   // HYBP: every wave loads pieces q = wave, wave + NW, ... of the problem's
@@ -450,7 +464,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
               for (int c = 0; c < WC; ++c) acc = fma(mS[RPT - 1][c], w[c], acc);
             } else {
-              const T* __restrict__ m = (from_pin ? pinned : stage) + lane * W;
+              const T* __restrict__ m = stage_shift(gP, from_pin ? pinned : stage) + lane * W;
 #pragma unroll 3
               for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
 #pragma unroll
@@ -601,7 +615,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
         dma_rows_to(gS, k, stage);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (valid[k]) {
-          const T* __restrict__ m = stage + lane * W;
+          const T* __restrict__ m = stage_shift(gS, stage) + lane * W;
 #pragma unroll
           for (int c = 0; c < WC; ++c) mS[k][c] = m[c];
         }
@@ -1085,7 +1099,12 @@ bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, siz
   const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
   const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
                         std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
-  const bool hybrid = specialised && vec && kHybridSize<T>(ss) &&
+  // S resident with Pinv streamed also takes matrices aligned to the element
+  // size only (its chunk loads shift, see the kernel), where a 64-row chunk
+  // leaves spare bytes in the stage (3ss elements not a multiple of 16 bytes);
+  // the D-block variants need 16-byte alignment.
+  const bool shiftable = (3 * ss * (int)sizeof(T)) % 16 != 0 && !pinv_diag && !pinv_packed;
+  const bool hybrid = specialised && (vec || shiftable) && kHybridSize<T>(ss) &&
                       std::getenv("GLASS_AMD_PCG_NO_HYBRID") == nullptr;
   pinv_diag = pinv_diag || pinv_packed;
   if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, hybrid, pinv_packed, lds_max, pl,

@@ -170,8 +170,9 @@ int glass_pcg_batched_ex(void* x, const void* S, const void* Pinv,
  * not fit there, S's rows in registers and the D blocks in LDS),
  * GLASS_PLACEMENT_STREAMED[_PREFETCH] (re-read from memory for every
  * matvec) or GLASS_PLACEMENT_S_RESIDENT (S's rows in registers, read once;
- * Pinv re-read for every matvec through the LDS, 16-byte aligned matrices
- * only).  Every placement gives the same bits.  aligned16: whether S and Pinv will be 16-byte aligned.  flags:
+ * Pinv re-read for every matvec through the LDS; matrices aligned to the
+ * element size are enough where a row of 3*state_size elements is not a
+ * multiple of 16 bytes, else they must be 16-byte aligned).  Every placement gives the same bits.  aligned16: whether S and Pinv will be 16-byte aligned.  flags:
  * as glass_pcg_batched_ex (0 for glass_pcg_batched).  Returns a negative
  * GLASS_E* code for shapes the solve rejects.  Enqueues nothing. */
 enum {

@@ -81,8 +81,13 @@ def test_summarize_pmc_calibrates_and_reads_back(tmp_path):
     _counter_csv(tmp_path / "w.csv", "WRITE_SIZE",
                  [(1, neg, 1048576.0), (2, pcg3, 10.0), (3, pcg3, 10.0)])
     out = tmp_path / "traffic.md"
+    # Over all workloads the ss=21 kernel serves two of them: no row.
     bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd f", "cmd w",
                         out=str(out))
+    assert "pcg3" not in bench.read_traffic(str(out))
+    sel = [k for k in bench.KERNEL_OF if k != "pcg3_unaligned"]
+    bench.summarize_pmc(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"), "cmd f", "cmd w",
+                        out=str(out), workloads=sel)
     text = out.read_text()
     # 1 GiB read as 524288 KiB of FETCH_SIZE -> factor 2; writes factor 1.
     assert "x 2.0000" in text and "x 1.0000" in text

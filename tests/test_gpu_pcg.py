@@ -3,6 +3,8 @@ Bars (see gpu_common): iterations within +-2, x within 1e-4 (fp32) / 1e-10
 (fp64) relative L2 of the oracle at the same iteration count, final criterion
 met."""
 
+from dataclasses import replace
+
 import numpy as np
 import pytest
 import torch
@@ -189,8 +191,11 @@ def test_pcg_placement_query_matches_the_workloads(gpu, monkeypatch):
     assert gpu.pcg_batched_placement(14, 32, torch.float32) == gpu.PLACEMENT_RESIDENT
     assert gpu.pcg_batched_placement(21, 64, torch.float32) == gpu.PLACEMENT_S_RESIDENT
     assert gpu.pcg_batched_placement(14, 32, torch.float64) == gpu.PLACEMENT_S_RESIDENT
+    # element-aligned matrices keep S in registers at ss=21 (shifted chunk loads)
     assert gpu.pcg_batched_placement(21, 64, torch.float32, aligned16=False) == \
-        gpu.PLACEMENT_STREAMED
+        gpu.PLACEMENT_S_RESIDENT
+    assert gpu.pcg_batched_placement(21, 64, torch.float32, aligned16=False,
+                                      pinv_block_diagonal=True) == gpu.PLACEMENT_STREAMED
     assert gpu.pcg_batched_placement(21, 64, torch.float32, pinv_block_diagonal=True) == \
         gpu.PLACEMENT_RESIDENT
     # ss=21 kp=64 (21 chunks of 64 rows, 3 per wave): with 8 waves, the LDS
@@ -637,3 +642,58 @@ def test_pcg_s_resident_status_cases(gpu, monkeypatch, ss, kp, dtype, flag):
     assert np.all(it[[0, 4, 5]] == 2) and np.all(st[[0, 4, 5]] == gpu.MAX_ITERS)
     x, it, st, _ = runs[(True, 60, 1e30)]
     assert np.all(it == 0) and np.all(st[[0, 2, 4, 5]] == gpu.CONVERGED)
+
+
+def _shifted_copy(a, elems):
+    """A device copy of array a that starts `elems` elements past a 16-byte
+    boundary (the tensor is a view into a slightly larger buffer)."""
+    t = torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    store = torch.zeros(t.numel() + 4, dtype=t.dtype, device="cuda")
+    view = store[elems:elems + t.numel()].view(t.shape)
+    view.copy_(t)
+    assert view.data_ptr() % 16 == elems * t.element_size() % 16
+    return view
+
+
+@pytest.mark.parametrize("ss,kp,B,dtype,shift_s,shift_p,pinv", [
+    (21, 64, None, np.float32, 1, 2, "tridiagonal"),   # the ss=21 workload, all problems
+    (21, 64, 64, np.float32, 3, 0, "block_jacobi"),
+    (21, 60, 5, np.float32, 2, 1, "tridiagonal"),      # ragged last chunk
+    (21, 41, 3, np.float32, 1, 1, "tridiagonal"),      # per-problem offsets not 16-byte multiples
+    (14, 32, 24, np.float64, 1, 0, "tridiagonal"),     # no spare stage bytes: streamed fallback
+    (14, 32, 96, np.float32, 1, 3, "tridiagonal"),     # resident rows, element loads
+])
+def test_pcg_element_aligned_matrices(gpu, ss, kp, B, dtype, shift_s, shift_p, pinv):
+    """S and Pinv aligned to the element size only (shifted by whole elements
+    from a 16-byte boundary): the S-resident placement loads each chunk from
+    the 16-byte boundary below it and reads the stage at the shift, other
+    placements use element loads; the results equal the aligned call bit
+    for bit and meet the oracle."""
+    if B is None:
+        w = replace(workloads.WORKLOADS[3], pinv=pinv)
+        inp = workloads.generate(w)
+    else:
+        rng = np.random.default_rng(ss * 100 + kp + shift_s)
+        S, D = workloads.random_spd_strips(rng, B, ss, kp, 0.1)
+        P = workloads.block_tridiagonal_pinv(S, D, dtype) if pinv == "tridiagonal" else \
+            workloads.block_jacobi_pinv(D, dtype)
+        inp = {"S": S.astype(dtype), "Pinv": P,
+               "b": rng.standard_normal((B, kp * ss)).astype(dtype),
+               "x0": np.zeros((B, kp * ss), dtype)}
+    B = inp["b"].shape[0]
+    rel = 1e-6 if dtype == np.float32 else 1e-12
+    ref = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0)
+    say("pcg ss=%d kp=%d B=%d %s, S +%d and Pinv +%d elements from 16 bytes"
+        % (ss, kp, B, np.dtype(dtype).name, shift_s, shift_p))
+    S_t, P_t = _shifted_copy(inp["S"], shift_s), _shifted_copy(inp["Pinv"], shift_p)
+    x = torch.from_numpy(inp["x0"]).cuda().clone()
+    it = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    st = torch.full((B,), -1, dtype=torch.int32, device="cuda")
+    rho = torch.zeros((B, 2), dtype=x.dtype, device="cuda")
+    gpu.pcg_batched(x, S_t, P_t, torch.from_numpy(inp["b"]).cuda(), ss, kp, 300, rel, 0.0,
+                    it, st, rho)
+    torch.cuda.synchronize()
+    got = (x.cpu().numpy(), it.cpu().numpy(), st.cpu().numpy(), rho.cpu().numpy())
+    for u, v in zip(ref, got):
+        np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, got, dtype)
