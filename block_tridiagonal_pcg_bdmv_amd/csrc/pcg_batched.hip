@@ -451,8 +451,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
         // Pinv chunk k is pinned in LDS, held in registers (preg waves'
         // chunk 0), or in (or on its way to) the stage.  For the stage: wait
         // for this wave's direct loads, multiply, and once every stage read
-        // has returned, load the next streamed chunk of the sequence (the
-        // first one of the next matvec after the last) into it.
+        // has returned, load the next streamed chunk of this matvec into it.
+        // The first chunk of the next Pinv matvec is loaded by the solve
+        // loop once the stopping test has passed, so a solve that stops
+        // there fetches nothing more.
         const bool from_pin = pin_last && k == RPT - 1;  // wave-uniform
         const bool from_reg = preg && k == 0;             // wave-uniform
         const bool streamed = !no_stream(k);
@@ -475,11 +477,9 @@ pcg_batched_kernel(PcgArgs<T> a) {
           if (streamed) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         if (streamed) {
-          int next = k;  // the next streamed position (at worst k itself)
-          do {
-            next = next + 1 == RPT ? 0 : next + 1;
-          } while (no_stream(next));
-          dma_chunk(next);
+          int next = k + 1;  // the next streamed position of this matvec
+          while (next < RPT && no_stream(next)) ++next;
+          if (next < RPT) dma_chunk(next);
         }
       } else if constexpr (HYBP) {
         // The row's ss values of its D block, times the middle third of the
@@ -623,11 +623,15 @@ pcg_batched_kernel(PcgArgs<T> a) {
       }
     }
   }
-  if constexpr (HYBS) {
-    int first = 0;
-    while (first < RPT && no_stream(first)) ++first;
-    if (first < RPT) dma_chunk(first);
-  }
+  // The first streamed Pinv chunk of a matvec into the stage (HYBS).
+  auto dma_first = [&]() {
+    if constexpr (HYBS) {
+      int first = 0;
+      while (first < RPT && no_stream(first)) ++first;
+      if (first < RPT) dma_chunk(first);
+    }
+  };
+  dma_first();
   if (pin_last) dma_chunk_to(RPT - 1, pinned);
   dma_pinv_whole();
 #pragma unroll
@@ -679,6 +683,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   if (rho_init == T(0) || rho_init < thresh) {
     status = GLASS_PCG_CONVERGED;
   } else {
+    if (a.max_iters > 0) dma_first();  // for the first iteration's z = Pinv r
     for (int it = 0; it < a.max_iters; ++it) {
       matvec(MatS{}, sv, mS, p_pad);  // Sp
       const T pSp = chunk_dot(pr, sv, slotB);
@@ -702,6 +707,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
         status = GLASS_PCG_CONVERGED;
         break;
       }
+      if (it + 1 < a.max_iters) dma_first();  // for the next iteration's z = Pinv r
       const T beta = rz / rho;
 #pragma unroll
       for (int k = 0; k < RPT; ++k) {
@@ -716,8 +722,9 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
   for (int k = 0; k < RPT; ++k)
     if (valid[k]) a.x[prob * n + row[k]] = xr[k];
-  // The last matvec started a load of the next chunk into the stage: let it
-  // land before the workgroup's LDS can pass to another workgroup.
+  // A solve that stopped at a breakdown has a chunk load in flight into the
+  // stage: let it land before the workgroup's LDS can pass to another
+  // workgroup.
   if constexpr (HYB) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tid == 0) {
     if (a.iters) a.iters[prob] = iters;
