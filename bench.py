@@ -700,6 +700,10 @@ def main():
 
     import torch
     import block_tridiagonal_pcg_bdmv_amd as glass
+    # Some rows select a placement through the library's GLASS_AMD_* switches
+    # (pcg3_stream, the several-per-wave rows), which it honours only in a
+    # process that sets this before its first call.
+    os.environ["GLASS_AMD_TUNING"] = "1"
     glass.load()
     torch.cuda.set_device(0)
 

@@ -109,6 +109,18 @@ def _dtype_code(t):
 
 
 def _dev(t, name, numel, dtype=None):
+    """Raw device pointer of ``t`` once it is a contiguous device tensor of
+    ``numel`` elements (and ``dtype``); raises otherwise."""
+    try:
+        if (t.is_cuda and t.is_contiguous() and t.numel() == numel
+                and (dtype is None or t.dtype == dtype)):
+            return t.data_ptr()
+    except AttributeError:
+        raise TypeError("%s must be a torch tensor" % name) from None
+    _dev_fail(t, name, numel, dtype)
+
+
+def _dev_fail(t, name, numel, dtype):
     import torch
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch tensor" % name)
@@ -118,15 +130,20 @@ def _dev(t, name, numel, dtype=None):
         raise ValueError("%s must be contiguous" % name)
     if dtype is not None and t.dtype != dtype:
         raise TypeError("%s must have dtype %s, got %s" % (name, dtype, t.dtype))
-    if t.numel() != numel:
-        raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
-    return ctypes.c_void_p(t.data_ptr())
+    raise ValueError("%s has %d elements, expected %d" % (name, t.numel(), numel))
 
 
 def _stream(stream):
+    """The raw HIP stream: ``stream``'s, or torch's current stream on the
+    current device (read without building a Stream object when torch offers
+    that)."""
     import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+        if raw is not None:
+            return raw(torch.cuda.current_device())
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
 
 
 def _problems(S, ss, kp):

@@ -106,8 +106,16 @@ int allow_dynamic_lds(const void* kernel, size_t bytes) {
   return GLASS_OK;
 }
 
+const char* tuning_getenv(const char* name) {
+  static const bool on = [] {
+    const char* t = std::getenv("GLASS_AMD_TUNING");
+    return t && t[0] == '1' && t[1] == '\0';
+  }();
+  return on ? std::getenv(name) : nullptr;
+}
+
 int env_int(const char* name, int fallback) {
-  const char* s = std::getenv(name);
+  const char* s = tuning_getenv(name);
   if (!s || !*s) return fallback;
   char* end = nullptr;
   long v = std::strtol(s, &end, 10);
@@ -116,7 +124,7 @@ int env_int(const char* name, int fallback) {
 }
 
 int env_flag(const char* name, int fallback) {
-  const char* s = std::getenv(name);
+  const char* s = tuning_getenv(name);
   if (!s) return fallback;
   if (s[0] == '0' && s[1] == '\0') return 0;
   if (s[0] == '1' && s[1] == '\0') return 1;

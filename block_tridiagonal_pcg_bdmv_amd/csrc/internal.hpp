@@ -33,10 +33,16 @@ int current_device_info(DeviceInfo* out);
 int kernel_occupancy(const void* kernel, int threads, size_t lds, int* out);
 int allow_dynamic_lds(const void* kernel, size_t bytes);
 
-// Optional launch-shape override from the environment (tests and tuning
-// sweeps): returns `fallback` when `name` is unset or not a positive integer.
+// Tuning and test switches (GLASS_AMD_* variables) are honoured only in a
+// process that set GLASS_AMD_TUNING=1 before the library's first call;
+// otherwise every switch takes its default, so a user's environment cannot
+// change a placement, and no call reads the environment.
+// tuning_getenv(name): getenv(name) in such a process, else nullptr.
+const char* tuning_getenv(const char* name);
+// Optional launch-shape override (tests and tuning sweeps): returns
+// `fallback` when `name` is unset or not a positive integer.
 int env_int(const char* name, int fallback);
-// A 0/1 switch from the environment: "0" or "1", else `fallback`.
+// A 0/1 switch: "0" or "1", else `fallback`.
 int env_flag(const char* name, int fallback);
 
 // Kernel launchers.  Arguments are already validated by the C ABI.

@@ -857,7 +857,7 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
   // its D blocks held whole in LDS, packed or under the block-diagonal
   // hint): the fewest rows per lane whose workgroup and LDS fit.
   if (hybrid) {
-    const bool pin_ok = std::getenv("GLASS_AMD_PCG_NO_PIN") == nullptr;
+    const bool pin_ok = tuning_getenv("GLASS_AMD_PCG_NO_PIN") == nullptr;
     for (int rpt = 1; rpt <= 3; ++rpt) {
       if (rpt * 3 * ss * (int)sizeof(T) / 4 > 192) break;
       int NW = (nchunks + rpt - 1) / rpt;
@@ -1105,19 +1105,19 @@ bool choose_plan(int ss, int kp, bool vec, bool pinv_diag, bool pinv_packed, siz
                  Plan* pl) {
   const bool specialised = ss == 6 || ss == 12 || ss == 14 || ss == 21;
   const bool prefetch = specialised && vec && kPrefetchFits<T>(ss) &&
-                        std::getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
+                        tuning_getenv("GLASS_AMD_PCG_NO_PREFETCH") == nullptr;
   // S resident with Pinv streamed also takes matrices aligned to the element
   // size only (its chunk loads shift, see the kernel), where a 64-row chunk
   // leaves spare bytes in the stage (3ss elements not a multiple of 16 bytes);
   // the D-block variants need 16-byte alignment.
   const bool shiftable = (3 * ss * (int)sizeof(T)) % 16 != 0 && !pinv_diag && !pinv_packed;
   const bool hybrid = specialised && (vec || shiftable) && kHybridSize<T>(ss) &&
-                      std::getenv("GLASS_AMD_PCG_NO_HYBRID") == nullptr;
+                      tuning_getenv("GLASS_AMD_PCG_NO_HYBRID") == nullptr;
   pinv_diag = pinv_diag || pinv_packed;
   if (!make_plan<T>(ss, kp, specialised, prefetch, pinv_diag, hybrid, pinv_packed, lds_max, pl,
                     specialised && vec))
     return false;
-  if (const char* f = getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && (pl->res || pl->hyb)) {
+  if (const char* f = tuning_getenv("GLASS_AMD_PCG_STREAMED"); f && f[0] == '1' && (pl->res || pl->hyb)) {
     Plan alt;
     if (make_plan<T>(ss, kp, false, prefetch, pinv_packed, false, pinv_packed, lds_max, &alt))
       *pl = alt;

@@ -949,7 +949,7 @@ int launch_grid(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.nb_max = nb_max;
   a.wide = aligned(S, 16) && aligned(P, 16);
   a.spin_limit = kSpinLimit;
-  if (const char* sl = std::getenv("GLASS_AMD_GRID_SPIN_LIMIT"); sl && *sl) {
+  if (const char* sl = tuning_getenv("GLASS_AMD_GRID_SPIN_LIMIT"); sl && *sl) {
     char* end = nullptr;
     const unsigned long v = std::strtoul(sl, &end, 10);
     if (end != sl && *end == '\0' && v <= kSpinLimit) a.spin_limit = (unsigned)v;

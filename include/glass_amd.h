@@ -40,6 +40,10 @@
  *     glass_last_error() then describes the failure (per host thread).
  *   - Calls on one stream run in order; calls on different streams that write
  *     the same memory race, as with any HIP kernel.
+ *   - The library reads no environment variable, except in a process that
+ *     sets GLASS_AMD_TUNING=1 before its first call: there its test and
+ *     tuning switches (GLASS_AMD_* names) can force placements and launch
+ *     shapes.
  */
 #ifndef GLASS_AMD_H
 #define GLASS_AMD_H

@@ -11,6 +11,11 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# The tests drive the library's GLASS_AMD_* placement and launch-shape
+# switches; the library honours them only in a process that set this before
+# its first call.
+os.environ.setdefault("GLASS_AMD_TUNING", "1")
+
 
 def pytest_configure(config):
     config.addinivalue_line(

@@ -697,3 +697,30 @@ def test_pcg_element_aligned_matrices(gpu, ss, kp, B, dtype, shift_s, shift_p, p
     for u, v in zip(ref, got):
         np.testing.assert_array_equal(u, v)
     assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, got, dtype)
+
+
+def test_tuning_switches_need_the_tuning_gate(gpu):
+    """The library's GLASS_AMD_* switches change a placement only in a process
+    that set GLASS_AMD_TUNING=1 before the library's first call; in any other
+    process the same switch is ignored (and no call reads the environment)."""
+    import os
+    import subprocess
+    import sys
+    from conftest import ROOT
+    code = ("import torch, block_tridiagonal_pcg_bdmv_amd as g; g.load(); "
+            "print(g.pcg_batched_placement(21, 64, torch.float32))")
+
+    def placement(tuning):
+        env = dict(os.environ)
+        env["GLASS_AMD_PCG_NO_HYBRID"] = "1"
+        env.pop("GLASS_AMD_TUNING", None)
+        if tuning:
+            env["GLASS_AMD_TUNING"] = "1"
+        say("placement query in a child process, GLASS_AMD_TUNING %s" % ("set" if tuning else "unset"))
+        r = subprocess.run([sys.executable, "-c", code], env=env, cwd=ROOT, capture_output=True,
+                           text=True, timeout=180)
+        assert r.returncode == 0, r.stderr[-2000:]
+        return int(r.stdout.strip().splitlines()[-1])
+
+    assert placement(False) == gpu.PLACEMENT_S_RESIDENT
+    assert placement(True) == gpu.PLACEMENT_STREAMED_PREFETCH
