@@ -143,22 +143,26 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic_bytes_pcg(w, iters: np.ndarray, resident, pinv_diag=False,
-                          pinned_rows=0) -> float:
+                          pass_rows=None) -> float:
     """Bytes one solve must move between HBM and the chip, by the algorithm:
     S and Pinv (n*3ss each; Pinv n*ss when only its D blocks are read) once
     if they stay on chip, else once per pass (the initial S x0 / Pinv r pass
     plus one per iteration); x read, b read, x written (n each); iters
     (4 bytes).  resident: True (both on chip), False (both streamed) or "S"
-    (S on chip, Pinv streamed except pinned_rows of its rows, which stay on
-    chip)."""
+    (S on chip once; Pinv rows as the placement reads them: pass_rows =
+    (rows at pass 0, at odd passes, at even passes >= 2), default every row
+    at every pass)."""
     es = np.dtype(w.dtype).itemsize
     s_bytes = w.n * 3 * w.ss * es
-    p_bytes = w.n * (w.ss if pinv_diag else 3 * w.ss) * es
+    row_b = (w.ss if pinv_diag else 3 * w.ss) * es
+    p_bytes = w.n * row_b
     vec = 3 * w.n * es + 4
-    passes = iters.astype(np.float64) + 1
+    it = iters.astype(np.int64)
+    passes = it.astype(np.float64) + 1
     if resident == "S":
-        p_pin = pinned_rows * (w.ss if pinv_diag else 3 * w.ss) * es
-        return float(np.sum(s_bytes + p_pin + passes * (p_bytes - p_pin) + vec))
+        r0, r_odd, r_even = pass_rows if pass_rows is not None else (w.n, w.n, w.n)
+        rows = r0 + ((it + 1) // 2) * r_odd + (it // 2) * r_even
+        return float(np.sum(s_bytes + rows.astype(np.float64) * row_b + vec))
     if resident:
         passes = np.ones_like(passes)
     return float(np.sum(passes * (s_bytes + p_bytes) + vec))
@@ -471,10 +475,10 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic,
         pinv_diagonal_blocks=packed)
     resident = grid or placement in (glass.PLACEMENT_RESIDENT, glass.PLACEMENT_SEVERAL_PER_WAVE) \
         or ("S" if placement == glass.PLACEMENT_S_RESIDENT else False)
-    pinned = glass.pcg_batched_pinned_rows(
-        w.ss, w.kp, S.dtype, aligned16=key not in UNALIGNED, pinv_block_diagonal=pd,
-        pinv_diagonal_blocks=packed) if resident == "S" else 0
-    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed, pinned_rows=pinned)
+    pass_rows = tuple(glass.pcg_batched_pinv_pass_rows(
+        w.ss, w.kp, S.dtype, p, aligned16=key not in UNALIGNED, pinv_block_diagonal=pd,
+        pinv_diagonal_blocks=packed) for p in (0, 1, 2)) if resident == "S" else None
+    nbytes = algorithmic_bytes_pcg(w, it, resident, pinv_diag=pd or packed, pass_rows=pass_rows)
     compulsory = compulsory_bytes_pcg(w, B, pinv_diag=pd or packed)
     served_by = "hbm" if resident is True else "hbm+infinity-cache"
     for k in range(min(10, len(xs))):

@@ -26,6 +26,7 @@ __all__ = [
     "pcg_batched_placement", "pcg_batched_pinned_rows", "PLACEMENT_RESIDENT",
     "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT", "PLACEMENT_SEVERAL_PER_WAVE", "stream_read",
+    "pcg_batched_pinv_pass_rows",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +76,7 @@ def load():
             "glass_bdsv_workspace_bytes": ([I, I, I, I], Z),
             "glass_pcg_batched_placement": ([I, I, I, I, U], I),
             "glass_pcg_batched_pinned_rows": ([I, I, I, I, U], I),
+            "glass_pcg_batched_pinv_pass_rows": ([I, I, I, I, U, I], I),
             "glass_pcg_grid_workspace_bytes": ([I, I, I], Z),
             "glass_pcg_grid": ([P, P, P, P, I, I, I, D, D, P, P, Z, I, P], I),
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
@@ -245,6 +247,24 @@ def pcg_batched_placement(state_size: int, knot_points: int, dtype, aligned16=Tr
                                                if pinv_diagonal_blocks else 0))
     if rc < 0:
         _check(rc, "glass_pcg_batched_placement")
+    return rc
+
+
+def pcg_batched_pinv_pass_rows(state_size: int, knot_points: int, dtype, pass_index: int,
+                               aligned16=True, pinv_block_diagonal=False,
+                               pinv_diagonal_blocks=False) -> int:
+    """Pinv rows per problem that matvec pass ``pass_index`` of pcg_batched
+    reads from memory on the current device (pass 0: z = Pinv r0, with the
+    rows kept on chip for the whole solve; pass p >= 1: iteration p).  Raises
+    for shapes the solve rejects."""
+    import torch
+    code = GLASS_F32 if dtype == torch.float32 else GLASS_F64
+    rc = load().glass_pcg_batched_pinv_pass_rows(
+        int(state_size), int(knot_points), code, 1 if aligned16 else 0,
+        (PCG_PINV_BLOCK_DIAGONAL if pinv_block_diagonal else 0)
+        | (PCG_PINV_DIAGONAL_BLOCKS if pinv_diagonal_blocks else 0), int(pass_index))
+    if rc < 0:
+        _check(rc, "glass_pcg_batched_pinv_pass_rows")
     return rc
 
 

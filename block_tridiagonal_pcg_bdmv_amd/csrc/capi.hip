@@ -245,6 +245,18 @@ int glass_pcg_batched_pinned_rows(int state_size, int knot_points, glass_dtype d
                                         (flags & GLASS_PCG_PINV_DIAGONAL_BLOCKS) != 0);
 }
 
+int glass_pcg_batched_pinv_pass_rows(int state_size, int knot_points, glass_dtype dtype,
+                                     int aligned16, unsigned flags, int pass) {
+  if (int rc = check_common(dtype, state_size, knot_points, 1)) return rc;
+  if (flags & ~kPcgFlags) return fail(GLASS_EINVAL, "unknown pcg flags");
+  if (pass < 0) return fail(GLASS_EINVAL, "pass must be >= 0");
+  if ((long long)knot_points * state_size > 8192)
+    return fail(GLASS_EUNSUPPORTED, "knot_points*state_size above 8192 (use glass_pcg_grid)");
+  return glass::pcg_batched_pinv_pass_rows(dtype, state_size, knot_points, aligned16 != 0,
+                                           (flags & kPinvDiag) != 0,
+                                           (flags & GLASS_PCG_PINV_DIAGONAL_BLOCKS) != 0, pass);
+}
+
 size_t glass_bdsv_workspace_bytes(int state_size, int knot_points, int n_problems,
                                   glass_dtype dtype) {
   if (dtype != GLASS_F32 && dtype != GLASS_F64) return 0;
@@ -384,6 +396,6 @@ const char* glass_status_string(int status) {
 
 const char* glass_last_error(void) { return glass::last_error_text(); }
 
-int glass_version(void) { return 300; }
+int glass_version(void) { return 400; }
 
 }  // extern "C"

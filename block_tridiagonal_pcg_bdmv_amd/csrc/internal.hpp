@@ -67,6 +67,8 @@ int launch_pcg_multi(glass_dtype dt, void* x, const void* S, const void* Pinv, c
 int pcg_batched_placement(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
                           bool pinv_packed);
 // Pinv rows the S-resident placement keeps pinned in LDS (0 otherwise).
+int pcg_batched_pinv_pass_rows(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
+                               bool pinv_packed, int pass);
 int pcg_batched_pinned_rows(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
                             bool pinv_packed);
 

@@ -209,6 +209,8 @@ pcg_batched_kernel(PcgArgs<T> a) {
   auto no_stream = [&](int k) {
     return (pin_last && k == RPT - 1) || (preg && (k == 0 || (wave + k * NW) * 64 >= n));
   };
+  // HYBS: positions whose chunk exists and goes through the stage.
+  auto streams = [&](int k) { return !no_stream(k) && (wave + k * NW) * 64 < n; };
   // HYBP: the problem's packed Pinv D blocks, [n][ss], after the head.
   T* pinv_lds = reinterpret_cast<T*>(smem_raw + head);
 
@@ -424,9 +426,14 @@ pcg_batched_kernel(PcgArgs<T> a) {
   };
 
   // out[k] = (M * vpad)[row k]: one lane, one row, serial 3*ss contraction.
-  // MI selects the matrix: 0 = S, 1 = Pinv.
-  auto matvec = [&](auto mi_tag, T (&out)[RPT], auto& mreg, const T* __restrict__ vpad) {
+  // MI selects the matrix: 0 = S, 1 = Pinv.  REV walks the wave's chunk
+  // positions from the last to the first (each row's result does not depend
+  // on the order; HYBS uses it to start a pass with the chunk the previous
+  // pass left in the stage).
+  auto matvec = [&](auto mi_tag, T (&out)[RPT], auto& mreg, const T* __restrict__ vpad,
+                    auto rev_tag) {
     constexpr int MI = decltype(mi_tag)::value;
+    constexpr bool REV = decltype(rev_tag)::value;
     const T* __restrict__ gM = MI == 0 ? gS : gP;
     // Streamed Pinv as packed D blocks: rows of ss values, multiplied with
     // the middle third of the window (the terms and order of a D-only row).
@@ -434,7 +441,8 @@ pcg_batched_kernel(PcgArgs<T> a) {
     const bool mpacked = MI == 1 && (PFM ? PFP : packed);
     constexpr bool REG = MI == 0 ? SRES : RES;  // this matrix's rows in registers
 #pragma unroll
-    for (int k = 0; k < RPT; ++k) {
+    for (int j = 0; j < RPT; ++j) {
+      const int k = REV ? RPT - 1 - j : j;
       T acc = T(0);
       if constexpr (REG) {
         if (valid[k]) {
@@ -451,13 +459,14 @@ pcg_batched_kernel(PcgArgs<T> a) {
         // Pinv chunk k is pinned in LDS, held in registers (preg waves'
         // chunk 0), or in (or on its way to) the stage.  For the stage: wait
         // for this wave's direct loads, multiply, and once every stage read
-        // has returned, load the next streamed chunk of this matvec into it.
-        // The first chunk of the next Pinv matvec is loaded by the solve
-        // loop once the stopping test has passed, so a solve that stops
-        // there fetches nothing more.
+        // has returned, load the next streamed chunk of this matvec (in its
+        // walking order) into it.  Passes alternate direction, so each pass
+        // after the first starts with the chunk the previous one left in
+        // the stage: it is not loaded again, and no load is in flight
+        // between passes (a solve that stops fetches nothing more).
         const bool from_pin = pin_last && k == RPT - 1;  // wave-uniform
         const bool from_reg = preg && k == 0;             // wave-uniform
-        const bool streamed = !no_stream(k);
+        const bool streamed = streams(k);
         if (streamed) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         if (chunk_r0(k) < n) {  // wave-uniform
           if (valid[k]) {
@@ -477,9 +486,15 @@ pcg_batched_kernel(PcgArgs<T> a) {
           if (streamed) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
         if (streamed) {
-          int next = k + 1;  // the next streamed position of this matvec
-          while (next < RPT && no_stream(next)) ++next;
-          if (next < RPT) dma_chunk(next);
+          int next = -1;  // the next streamed position of this matvec
+          if constexpr (REV) {
+            for (int q = k - 1; q >= 0 && next < 0; --q)
+              if (streams(q)) next = q;
+          } else {
+            for (int q = k + 1; q < RPT && next < 0; ++q)
+              if (streams(q)) next = q;
+          }
+          if (next >= 0) dma_chunk(next);
         }
       } else if constexpr (HYBP) {
         // The row's ss values of its D block, times the middle third of the
@@ -548,6 +563,8 @@ pcg_batched_kernel(PcgArgs<T> a) {
   };
   using MatS = std::integral_constant<int, 0>;
   using MatP = std::integral_constant<int, 1>;
+  using Fwd = std::integral_constant<bool, false>;
+  using Rev = std::integral_constant<bool, HYBS>;  // reverse order only where it pays
 
   // Dot product of two row-distributed vectors, independent of the launch
   // shape: each 64-row chunk's products go through the fixed wave64 tree
@@ -624,14 +641,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
     }
   }
   // The first streamed Pinv chunk of a matvec into the stage (HYBS).
-  auto dma_first = [&]() {
-    if constexpr (HYBS) {
-      int first = 0;
-      while (first < RPT && no_stream(first)) ++first;
-      if (first < RPT) dma_chunk(first);
-    }
-  };
-  dma_first();
+  // The first streamed Pinv chunk of the first pass into the stage (HYBS).
+  if constexpr (HYBS) {
+    int first = 0;
+    while (first < RPT && !streams(first)) ++first;
+    if (first < RPT) dma_chunk(first);
+  }
   if (pin_last) dma_chunk_to(RPT - 1, pinned);
   dma_pinv_whole();
 #pragma unroll
@@ -646,7 +661,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   block_sync();
 
   T sv[RPT];
-  matvec(MatS{}, sv, mS, p_pad);  // S x0
+  matvec(MatS{}, sv, mS, p_pad, Fwd{});  // S x0
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     rr[k] = valid[k] ? tmp[k] - sv[k] : T(0);
@@ -667,7 +682,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     if (pin_last) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
   block_sync();
-  matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
+  matvec(MatP{}, sv, mP, r_pad, Fwd{});  // z = Pinv r (pass 0)
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     pr[k] = sv[k];
@@ -683,9 +698,8 @@ pcg_batched_kernel(PcgArgs<T> a) {
   if (rho_init == T(0) || rho_init < thresh) {
     status = GLASS_PCG_CONVERGED;
   } else {
-    if (a.max_iters > 0) dma_first();  // for the first iteration's z = Pinv r
     for (int it = 0; it < a.max_iters; ++it) {
-      matvec(MatS{}, sv, mS, p_pad);  // Sp
+      matvec(MatS{}, sv, mS, p_pad, Fwd{});  // Sp
       const T pSp = chunk_dot(pr, sv, slotB);
       if (!(pSp > T(0)) || !is_finite_val(pSp)) {
         status = GLASS_PCG_BREAKDOWN;
@@ -700,14 +714,15 @@ pcg_batched_kernel(PcgArgs<T> a) {
       }
       iters = it + 1;
       block_sync();
-      matvec(MatP{}, sv, mP, r_pad);  // z = Pinv r
+      // z = Pinv r (pass it + 1: odd passes walk the chunks backwards)
+      if (HYBS && (it & 1) == 0) matvec(MatP{}, sv, mP, r_pad, Rev{});
+      else matvec(MatP{}, sv, mP, r_pad, Fwd{});
       const T rz = chunk_dot(rr, sv, slotA);
       rho_last = rz;
       if (fabs(rz) < thresh) {
         status = GLASS_PCG_CONVERGED;
         break;
       }
-      if (it + 1 < a.max_iters) dma_first();  // for the next iteration's z = Pinv r
       const T beta = rz / rho;
 #pragma unroll
       for (int k = 0; k < RPT; ++k) {
@@ -722,9 +737,9 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
   for (int k = 0; k < RPT; ++k)
     if (valid[k]) a.x[prob * n + row[k]] = xr[k];
-  // A solve that stopped at a breakdown has a chunk load in flight into the
-  // stage: let it land before the workgroup's LDS can pass to another
-  // workgroup.
+  // Direct loads into LDS must land before the workgroup's LDS can pass to
+  // another workgroup.  None is in flight here (the last chunk of a pass
+  // starts no load); the wait makes sure.
   if constexpr (HYB) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (tid == 0) {
     if (a.iters) a.iters[prob] = iters;
@@ -1224,7 +1239,63 @@ int pinned_rows_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_
   return rows;
 }
 
+// Pinv rows (per problem) that matvec pass `pass` reads from memory: the
+// plan's chunk walk as the kernel does it (pass 0 forward and the pinned
+// rows once; then alternate directions, each pass starting with the chunk
+// the previous one left in the wave's stage).
+template <typename T>
+int pass_rows_typed(int ss, int kp, bool aligned16, bool pinv_diag, bool pinv_packed, int pass) {
+  constexpr glass_dtype dt = sizeof(T) == 4 ? GLASS_F32 : GLASS_F64;
+  const long long n = (long long)kp * ss, es = (long long)sizeof(T);
+  if (use_multi(dt, ss, kp, pinv_packed)) return pass == 0 ? (int)n : 0;
+  DeviceInfo dev;
+  if (int rc = current_device_info(&dev)) return rc;
+  const bool vec = aligned16 && (n * 3 * ss * es) % 16 == 0 &&
+                   (!pinv_packed || (n * ss * es) % 16 == 0);
+  Plan pl;
+  if (!choose_plan<T>(ss, kp, vec, pinv_diag, pinv_packed, dev.max_lds_per_block, &pl))
+    return fail(GLASS_EUNSUPPORTED, "pcg: problem too large for one workgroup (rows or LDS)");
+  if (!pl.hyb) return pl.res ? (pass == 0 ? (int)n : 0) : (int)n;
+  if (pl.pd) return pass == 0 ? (int)n : 0;  // D blocks in LDS, read once
+  long long rows = 0;
+  for (int w = 0; w < pl.NW; ++w) {
+    auto chunk_rows = [&](int k) -> long long {
+      const long long r0 = (long long)(w + k * pl.NW) * 64;
+      return r0 < n ? std::min<long long>(64, n - r0) : 0;
+    };
+    const bool pin_last = w < pl.npin;
+    const bool preg = pl.regpin && pl.RPT >= 2 && chunk_rows(pl.RPT - 1) == 0 && chunk_rows(0) > 0;
+    auto streams = [&](int k) {
+      const bool off = (pin_last && k == pl.RPT - 1) || (preg && k == 0);
+      return !off && chunk_rows(k) > 0;
+    };
+    int first = -1, last = -1;
+    long long streamed = 0;
+    for (int k = 0; k < pl.RPT; ++k)
+      if (streams(k)) {
+        if (first < 0) first = k;
+        last = k;
+        streamed += chunk_rows(k);
+      }
+    if (pass == 0) {
+      rows += streamed;
+      if (pin_last) rows += chunk_rows(pl.RPT - 1);
+      if (preg) rows += chunk_rows(0);
+    } else if (first >= 0) {
+      rows += streamed - chunk_rows((pass & 1) ? last : first);
+    }
+  }
+  return (int)rows;
+}
+
 }  // namespace
+
+int pcg_batched_pinv_pass_rows(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
+                               bool pinv_packed, int pass) {
+  return dt == GLASS_F32
+             ? pass_rows_typed<float>(ss, kp, aligned16, pinv_diag, pinv_packed, pass)
+             : pass_rows_typed<double>(ss, kp, aligned16, pinv_diag, pinv_packed, pass);
+}
 
 int pcg_batched_pinned_rows(glass_dtype dt, int ss, int kp, bool aligned16, bool pinv_diag,
                             bool pinv_packed) {

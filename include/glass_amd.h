@@ -195,13 +195,29 @@ int glass_pcg_batched_placement(int state_size, int knot_points,
                                 glass_dtype dtype, int aligned16, unsigned flags);
 
 /* In GLASS_PLACEMENT_S_RESIDENT, the number of Pinv strip rows (per problem)
- * that stay in LDS for the whole solve: the LDS left over after the
- * per-wave stages holds the last chunk of 64 rows of some waves, read from
- * memory once; the other rows are read once per matvec.  0 for the other
- * placements.  Arguments, errors and side effects as
- * glass_pcg_batched_placement (it enqueues nothing). */
+ * that stay on chip for the whole solve: the LDS left over after the
+ * per-wave stages holds the last chunk of 64 rows of some waves, and waves
+ * with a register row to spare hold their first chunk there; these are read
+ * from memory once.  0 for the other placements.  Arguments, errors and side
+ * effects as glass_pcg_batched_placement (it enqueues nothing). */
 int glass_pcg_batched_pinned_rows(int state_size, int knot_points,
                                   glass_dtype dtype, int aligned16, unsigned flags);
+
+/* The number of Pinv strip rows (per problem) that matvec pass `pass` reads
+ * from memory on the current device: pass 0 is z = Pinv r0 and also counts
+ * the rows kept on chip for the whole solve; pass p >= 1 is iteration p's
+ * z = Pinv r.  In GLASS_PLACEMENT_S_RESIDENT the other rows stream through
+ * one LDS stage per wave, in 64-row chunks; passes walk each wave's chunks in
+ * alternating directions, so a pass after the first starts with the chunk
+ * the previous pass left in the stage and does not read it again (the count
+ * then alternates between odd and even passes when a chunk is short).
+ * Resident placements: knot_points*state_size rows at pass 0, 0 after;
+ * streamed placements: knot_points*state_size at every pass.  pass < 0 is
+ * GLASS_EINVAL; otherwise arguments, errors and side effects as
+ * glass_pcg_batched_placement (it enqueues nothing). */
+int glass_pcg_batched_pinv_pass_rows(int state_size, int knot_points,
+                                     glass_dtype dtype, int aligned16, unsigned flags,
+                                     int pass);
 
 /*
  * One PCG solve (same steps and outputs as glass_pcg_batched with
@@ -343,7 +359,7 @@ const char* glass_status_string(int status);
 const char* glass_last_error(void);
 /* Library ABI version (major*10000 + minor*100 + patch).  0.2.0 added
  * glass_pcg_batched_pinned_rows and GLASS_PLACEMENT_S_RESIDENT; 0.3.0 added
- * glass_pcg_grid_noalloc. */
+ * glass_pcg_grid_noalloc; 0.4.0 added glass_pcg_batched_pinv_pass_rows. */
 int glass_version(void);
 
 #ifdef __cplusplus

@@ -63,6 +63,9 @@ int main() {
   expect(glass_pcg_batched_placement(64, 200, GLASS_F32, 1, 0), GLASS_EUNSUPPORTED,
          "placement rows");
   expect(glass_pcg_batched_pinned_rows(6, 32, GLASS_F32, 1, 4u), GLASS_EINVAL, "pinned flags");
+  expect(glass_pcg_batched_pinv_pass_rows(6, 32, GLASS_F32, 1, 4u, 0), GLASS_EINVAL, "pass rows flags");
+  expect(glass_pcg_batched_pinv_pass_rows(6, 32, GLASS_F32, 1, 0u, -1), GLASS_EINVAL, "pass rows pass");
+  expect(glass_pcg_batched_pinv_pass_rows(6, 32, (glass_dtype)7, 1, 0u, 0), GLASS_EINVAL, "pass rows dtype");
   // grid
   const size_t ws = glass_pcg_grid_workspace_bytes(12, 8192, GLASS_F64);
   if (ws == 0) {

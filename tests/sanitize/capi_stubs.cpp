@@ -17,6 +17,7 @@ int launch_pcg_batched(glass_dtype, void*, const void*, const void*, const void*
 }
 int pcg_batched_placement(glass_dtype, int, int, bool, bool, bool) { return GLASS_EHIP; }
 int pcg_batched_pinned_rows(glass_dtype, int, int, bool, bool, bool) { return GLASS_EHIP; }
+int pcg_batched_pinv_pass_rows(glass_dtype, int, int, bool, bool, bool, int) { return GLASS_EHIP; }
 size_t bdsv_workspace_bytes(int ss, int kp, long long n_problems, glass_dtype dt) {
   const size_t es = dt == GLASS_F32 ? 4 : 8;
   return ((size_t)n_problems * kp * ss * (ss + 1) * es + 255) / 256 * 256;

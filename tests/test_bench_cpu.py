@@ -31,9 +31,14 @@ def test_pcg_bytes_resident_and_streamed():
     # S on chip (144 B once), Pinv (144 B) once per pass
     assert bench.algorithmic_bytes_pcg(w, it, resident="S") == \
         (144 + 5 * 144 + 76) + (144 + 1 * 144 + 76)
-    # two of Pinv's 6 rows (2 * 6 * 4 = 48 B) pinned on chip: read once
-    assert bench.algorithmic_bytes_pcg(w, it, resident="S", pinned_rows=2) == \
-        (144 + 48 + 5 * 96 + 76) + (144 + 48 + 1 * 96 + 76)
+    # Pinv rows as the placement reads them (24 B each): all 6 at pass 0,
+    # 4 at odd passes and 3 at even ones; 4 iterations are passes 1-4 (two
+    # odd, two even), none after the first for the solve that stops at 0.
+    assert bench.algorithmic_bytes_pcg(w, it, resident="S", pass_rows=(6, 4, 3)) == \
+        (144 + (6 + 2 * 4 + 2 * 3) * 24 + 76) + (144 + 6 * 24 + 76)
+    it3 = np.array([3])  # passes 1, 2, 3: two odd, one even
+    assert bench.algorithmic_bytes_pcg(w, it3, resident="S", pass_rows=(6, 4, 3)) == \
+        144 + (6 + 2 * 4 + 3) * 24 + 76
 
 
 def test_bdmv_bytes():

@@ -139,6 +139,11 @@ def test_placement_query_argument_errors(lib):
     assert lib.glass_pcg_batched_pinned_rows(6, 32, 5, 1, 0) == EINVAL
     assert lib.glass_pcg_batched_pinned_rows(64, 200, 0, 1, 0) == EUNSUPPORTED
     assert lib.glass_pcg_batched_pinned_rows(6, 32, 0, 1, 4) == EINVAL
+    assert lib.glass_pcg_batched_pinv_pass_rows(0, 32, 0, 1, 0, 0) == EINVAL
+    assert lib.glass_pcg_batched_pinv_pass_rows(6, 32, 5, 1, 0, 0) == EINVAL
+    assert lib.glass_pcg_batched_pinv_pass_rows(64, 200, 0, 1, 0, 0) == EUNSUPPORTED
+    assert lib.glass_pcg_batched_pinv_pass_rows(6, 32, 0, 1, 4, 0) == EINVAL
+    assert lib.glass_pcg_batched_pinv_pass_rows(6, 32, 0, 1, 0, -1) == EINVAL
 
 
 def test_pcg_ex_flag_errors(lib):

@@ -724,3 +724,25 @@ def test_tuning_switches_need_the_tuning_gate(gpu):
 
     assert placement(False) == gpu.PLACEMENT_S_RESIDENT
     assert placement(True) == gpu.PLACEMENT_STREAMED_PREFETCH
+
+
+def test_pinv_pass_rows_follow_the_chunk_walk(gpu, monkeypatch):
+    """Pinv rows each matvec pass reads from memory.  The ss=21 kp=64
+    S-resident solve: all 1344 rows at pass 0 (256 of them then stay on
+    chip), after that its 17 streamed chunks less the one each of its 8 waves
+    carries over in its stage, 9 chunks (576 rows).  The fp64 ss=14 solve in
+    the same placement has one chunk per wave, so after pass 0 it reads
+    nothing.  Resident: pass 0 only; streamed: every row every pass."""
+    f32, f64 = torch.float32, torch.float64
+    q = gpu.pcg_batched_pinv_pass_rows
+    assert gpu.pcg_batched_placement(21, 64, f32) == gpu.PLACEMENT_S_RESIDENT
+    assert (q(21, 64, f32, 0), q(21, 64, f32, 1), q(21, 64, f32, 2), q(21, 64, f32, 7)) == \
+        (1344, 576, 576, 576)
+    assert gpu.pcg_batched_placement(14, 32, f64) == gpu.PLACEMENT_S_RESIDENT
+    assert (q(14, 32, f64, 0), q(14, 32, f64, 1), q(14, 32, f64, 2)) == (448, 0, 0)
+    assert gpu.pcg_batched_placement(14, 32, f32) == gpu.PLACEMENT_RESIDENT
+    assert (q(14, 32, f32, 0), q(14, 32, f32, 3)) == (448, 0)
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_PIN", "1")
+    assert q(21, 64, f32, 0) == 1344 and q(21, 64, f32, 1) == q(21, 64, f32, 2) < 1344
+    monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
+    assert (q(21, 64, f32, 0), q(21, 64, f32, 1)) == (1344, 1344)
