@@ -108,6 +108,8 @@ struct PcgArgs {
   int ppacked;      // Pinv is packed D blocks, [kp*ss][ss] per problem (read
                     // by kStream; the other modes fix it at compile time)
   unsigned lds_bytes;  // dynamic LDS of the launch (debug fill)
+  int resd_s_stage;    // RESD: S rows also arrive through the stage, before Pinv's
+                       // (coalesced; one exposed round trip)
 };
 
 // Placements of the matrices (see the header).
@@ -287,7 +289,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
         for (int c = 0; c < WCP; ++c) mP[k][c] = T(0);
       }
-      if (valid[k] && !(HYBS && kSViaLds)) {
+      if (valid[k] && !(HYBS && kSViaLds) && !(RESD && a.resd_s_stage)) {
         const long long off = (long long)row[k] * WC;
         // The D part starts ss elements into the row: at (3*row + 1) times
         // its own byte size, so the widths load_row_regs picks stay aligned.
@@ -608,20 +610,35 @@ pcg_batched_kernel(PcgArgs<T> a) {
     // This wave's Pinv rows (one chunk: RPT == 1) into its stage, issued
     // after x0 and b so that waiting for those does not wait for them.  The
     // stage holds exactly the chunk; lanes past its last 16-byte vector are
-    // masked off.
+    // masked off.  With resd_s_stage the wave's S rows come the same way
+    // first, and each lane copies its row out before the Pinv load reuses
+    // the stage.
     const int r0 = chunk_r0(0);
     const int cvec = (min(64, n - r0) * W * (int)sizeof(T) + 15) / 16;
-    const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(gP + (long long)r0 * W, (n - r0) * W * (int)sizeof(T));
     unsigned char* st = reinterpret_cast<unsigned char*>(stage);
     constexpr int NVC = (64 * WC * (int)sizeof(T) + 1023) / 1024;
+    auto dma_rows = [&](const T* __restrict__ gM) {
+      const __amdgpu_buffer_rsrc_t rs =
+          make_rsrc(gM + (long long)r0 * W, (n - r0) * W * (int)sizeof(T));
 #pragma unroll
-    for (int u = 0; u < NVC; ++u) {
-      if (lane + u * kWave < cvec)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
-            (lane + u * kWave) * 16, 0, 0, 0);
+      for (int u = 0; u < NVC; ++u) {
+        if (lane + u * kWave < cvec)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
+              (lane + u * kWave) * 16, 0, 0, 0);
+      }
+    };
+    if (a.resd_s_stage) {
+      dma_rows(gS);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (valid[0]) {
+        const T* __restrict__ m = stage + lane * W;
+#pragma unroll
+        for (int c = 0; c < WC; ++c) mS[0][c] = m[c];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
+    dma_rows(gP);
   }
   if constexpr (HYBS && kSViaLds) {
     // S chunks through the stage: coalesced direct loads, then each lane
@@ -1187,6 +1204,11 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   a.npin = pl.npin;
   a.regpin = pl.regpin ? 1 : 0;
   a.ppacked = pinv_packed ? 1 : 0;
+  // Rows of 128 bytes or more: one load instruction of a lane's own S row
+  // touches as many cache lines as the wave has lanes, so the coalesced
+  // staging wins (ss=14 fp32: 168-byte rows); shorter rows load directly.
+  a.resd_s_stage =
+      env_flag("GLASS_AMD_PCG_RESD_S_STAGE", 3 * ss * (int)sizeof(T) >= 128 ? 1 : 0);
   switch (ss) {
     case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
     case 12: return launch_ss<T, 12>(a, n_problems, pl, st);

@@ -1,8 +1,10 @@
 """Resident rows with the Pinv rows brought in through each wave's LDS stage
-by direct loads (while the S rows load straight into registers): the same
-values in the same registers and the same steps in the same order as the
-plain resident load (GLASS_AMD_PCG_RES_DMA=0), so bit-identical outputs,
-and the oracle bars of gpu_common."""
+by direct loads, and the S rows either straight into registers or through
+the same stage first (GLASS_AMD_PCG_RESD_S_STAGE; by default for rows of
+128 bytes or more): the same values in the same registers and the same
+steps in the same order as the plain resident load
+(GLASS_AMD_PCG_RES_DMA=0), so bit-identical outputs, and the oracle bars of
+gpu_common."""
 
 from dataclasses import replace
 
@@ -23,6 +25,12 @@ def both(gpu, monkeypatch, inp, ss, kp, max_iters, rel, abs_tol):
     got = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
     for u, v in zip(ref, got):
         np.testing.assert_array_equal(u, v)
+    for s_stage in ("0", "1"):
+        monkeypatch.setenv("GLASS_AMD_PCG_RESD_S_STAGE", s_stage)
+        alt = pcg_gpu(gpu, inp, ss, kp, max_iters, rel, abs_tol)
+        for u, v in zip(ref, alt):
+            np.testing.assert_array_equal(u, v)
+    monkeypatch.delenv("GLASS_AMD_PCG_RESD_S_STAGE")
     return got
 
 
