@@ -291,3 +291,42 @@ def test_long_grid_solve(gpu, pinv, variant):
     its = assert_pcg_parity(inp, 12, 2048, 2000, 1e-20, 0.0, res, np.float64)
     say("  iterations %d" % its[0])
     assert its[0] >= 15
+
+
+def test_s_resident_random_shapes_match_streamed(gpu, monkeypatch):
+    """Seeded random shapes in the S-resident placement (ss = 12, 14, 21;
+    fp32 and fp64; kp up to the placement's limit, so ragged last chunks,
+    pinned and register-held chunks and odd/even carried-chunk patterns all
+    occur; both preconditioners; zero and random x0): bit for bit the
+    streamed placement's results, and the oracle bar on the first cases."""
+    rng = np.random.default_rng(20261203)
+    shapes = [(21, np.float32, 73), (14, np.float64, 56), (12, np.float64, 82)]
+    seen = 0
+    for case in range(24):
+        ss, dtype, kmax = shapes[case % 3]
+        kp = int(rng.integers(1, kmax + 1))
+        B = int(rng.integers(1, 97))
+        tdt = torch.float32 if dtype == np.float32 else torch.float64
+        monkeypatch.delenv("GLASS_AMD_PCG_NO_HYBRID", raising=False)
+        assert gpu.pcg_batched_placement(ss, kp, tdt) == gpu.PLACEMENT_S_RESIDENT, (ss, kp)
+        r2 = np.random.default_rng(int(rng.integers(0, 1 << 30)))
+        S, D = workloads.random_spd_strips(r2, B, ss, kp, 0.1)
+        P = workloads.block_tridiagonal_pinv(S, D, dtype) if case % 2 else \
+            workloads.block_jacobi_pinv(D, dtype)
+        inp = {"S": S.astype(dtype), "Pinv": P,
+               "b": r2.standard_normal((B, kp * ss)).astype(dtype),
+               "x0": (r2.standard_normal((B, kp * ss)) if case % 4 == 3
+                      else np.zeros((B, kp * ss))).astype(dtype)}
+        rel = 1e-6 if dtype == np.float32 else 1e-12
+        say("S-resident random shape %d: ss=%d kp=%d B=%d %s, Pinv rows per pass %s" % (
+            case, ss, kp, B, np.dtype(dtype).name,
+            [gpu.pcg_batched_pinv_pass_rows(ss, kp, tdt, p) for p in (0, 1, 2)]))
+        got = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0)
+        monkeypatch.setenv("GLASS_AMD_PCG_NO_HYBRID", "1")
+        ref = pcg_gpu(gpu, inp, ss, kp, 300, rel, 0.0)
+        for u, v in zip(got, ref):
+            np.testing.assert_array_equal(u, v)
+        if case < 6:
+            assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, got, dtype)
+        seen += 1
+    assert seen == 24
