@@ -110,6 +110,8 @@ struct PcgArgs {
   unsigned lds_bytes;  // dynamic LDS of the launch (debug fill)
   int resd_s_stage;    // RESD: S rows also arrive through the stage, before Pinv's
                        // (coalesced; one exposed round trip)
+  int preg_stage;      // HYBS: preg waves' Pinv chunk 0 arrives through the stage
+                       // after their S chunks (coalesced), not row by row
 };
 
 // Placements of the matrices (see the header).
@@ -308,7 +310,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   }
   if constexpr (HYBS) {
     // preg: chunk 0's Pinv rows into the registers of the absent last chunk.
-    if (preg && valid[0]) {
+    if (preg && valid[0] && !(kSViaLds && a.preg_stage)) {
       if (vec) load_row_regs<T, WC, true>(mS[RPT - 1], gP + (long long)row[0] * WC);
       else load_row_regs<T, WC, false>(mS[RPT - 1], gP + (long long)row[0] * WC);
     }
@@ -656,8 +658,17 @@ pcg_batched_kernel(PcgArgs<T> a) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
     }
+    if (preg && a.preg_stage) {  // chunk 0 of Pinv the same way, into its registers
+      dma_rows_to(gP, 0, stage);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (valid[0]) {
+        const T* __restrict__ m = stage_shift(gP, stage) + lane * W;
+#pragma unroll
+        for (int c = 0; c < WC; ++c) mS[RPT - 1][c] = m[c];
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
   }
-  // The first streamed Pinv chunk of a matvec into the stage (HYBS).
   // The first streamed Pinv chunk of the first pass into the stage (HYBS).
   if constexpr (HYBS) {
     int first = 0;
@@ -1209,6 +1220,7 @@ int launch_typed(T* x, const T* S, const T* P, const T* b, int ss, int kp,
   // staging wins (ss=14 fp32: 168-byte rows); shorter rows load directly.
   a.resd_s_stage =
       env_flag("GLASS_AMD_PCG_RESD_S_STAGE", 3 * ss * (int)sizeof(T) >= 128 ? 1 : 0);
+  a.preg_stage = env_flag("GLASS_AMD_PCG_PREG_STAGE", 1);
   switch (ss) {
     case 6: return launch_ss<T, 6>(a, n_problems, pl, st);
     case 12: return launch_ss<T, 12>(a, n_problems, pl, st);

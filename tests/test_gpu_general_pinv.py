@@ -330,3 +330,19 @@ def test_s_resident_random_shapes_match_streamed(gpu, monkeypatch):
             assert_pcg_parity(inp, ss, kp, 300, rel, 0.0, got, dtype)
         seen += 1
     assert seen == 24
+
+
+def test_register_held_pinv_chunk_staged_or_direct(gpu, monkeypatch):
+    """The waves that keep Pinv's chunk 0 in registers load it through their
+    LDS stage after their S chunks (default) or row by row
+    (GLASS_AMD_PCG_PREG_STAGE=0): the same values in the same registers, so
+    the ss=21 kp=64 workload gives the same bits either way."""
+    w = replace(workloads.WORKLOADS[3], pinv="tridiagonal")
+    inp = workloads.generate(w, n_problems=256)
+    say("ss=21 kp=64 register-held Pinv chunk: staged vs row by row")
+    got = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    monkeypatch.setenv("GLASS_AMD_PCG_PREG_STAGE", "0")
+    ref = pcg_gpu(gpu, inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol)
+    for u, v in zip(got, ref):
+        np.testing.assert_array_equal(u, v)
+    assert_pcg_parity(inp, w.ss, w.kp, w.max_iters, w.rel_tol, w.abs_tol, got, np.float32)
