@@ -128,8 +128,35 @@ def workload_of(key):
     return replace(w, **VARIANT_OF[key]) if key in VARIANT_OF else w
 
 
+def code_without_comments(text: str) -> str:
+    """C/C++ source with // and /* */ comments removed (string and character
+    literals kept as they are), so that edits of comments alone do not
+    change the hash below."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def kernel_source_hash() -> str:
-    """sha256 over the HIP sources and the C ABI header (sorted by name)."""
+    """sha256 over the code of the HIP sources and the C ABI header (sorted by
+    name, comments removed)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "block_tridiagonal_pcg_bdmv_amd", "csrc")
     files = sorted(os.path.join(csrc, f) for f in os.listdir(csrc)
@@ -137,8 +164,8 @@ def kernel_source_hash() -> str:
     files.append(os.path.join(ROOT, "include", "glass_amd.h"))
     for f in files:
         h.update(os.path.basename(f).encode())
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(code_without_comments(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -24,21 +24,26 @@
 //   every placement (number of waves, rows per lane, resident or streamed).
 //   Two slot arrays alternate so one barrier per dot suffices.
 // * matrices: RESIDENT -- each lane holds its S row and Pinv row in VGPRs,
-//   loaded once straight from memory with every load of both rows in flight
-//   (the widest loads the row alignment allows);
+//   loaded once: straight from memory with every load of both rows in
+//   flight (the widest loads the row alignment allows), or (RESD) through
+//   the wave's LDS stage by coalesced direct loads -- the Pinv rows, and the
+//   S rows first when rows are 128 bytes or longer;
 //   STREAMED -- every matvec re-stages the wave's 64-row chunk of S or
 //   Pinv HBM/L2 -> LDS (coalesced 16-byte loads) and each lane multiplies its
-//   row from there.  With PREFETCH, the wave's next two chunks in the fixed
-//   sequence (chunks of S, then of Pinv, then of S, ...) are loaded into
-//   registers ahead of use, so they stay in flight across the multiply, the
-//   dots and the workgroup barriers (matrix loads never depend on the
-//   vectors);
+//   row from there.  With PREFETCH, the wave's next chunk (two with
+//   GLASS_AMD_RING_DEPTH=2) in the fixed sequence (chunks of S, then of
+//   Pinv, then of S, ...) is loaded into registers ahead of use, so it stays
+//   in flight across the multiply, the dots and the workgroup barriers
+//   (matrix loads never depend on the vectors);
 //   S RESIDENT (HYBRID) -- when S and Pinv rows do not fit the registers
 //   together: each lane holds its S rows in VGPRs for the whole solve, and
 //   Pinv goes memory -> LDS with direct buffer -> LDS loads, which hold no
-//   registers in flight.  A general Pinv streams through a per-wave stage
-//   one chunk ahead (some chunks pinned on chip: in LDS left over after the
-//   stages, or in the S registers of waves without a last chunk); a
+//   registers in flight.  A general Pinv streams through a per-wave stage a
+//   chunk at a time, each pass walking the wave's chunks in the opposite
+//   direction to the pass before, so a pass after the first starts with the
+//   chunk the previous one left in the stage and does not load it again
+//   (some chunks pinned on chip for the whole solve: in LDS left over after
+//   the stages, or in the S registers of waves without a last chunk); a
 //   block-Jacobi Pinv's D blocks are loaded whole into LDS once.
 // Barriers per iteration: 4 (p^T Sp, r publish, r^T z, p publish).
 //

@@ -124,3 +124,14 @@ def test_alu_roofline_uses_the_unpacked_fp32_peak():
     r = bench.roofline_alu(78.6e9, 1e9, 1.0, None, np.float32)
     assert r["peak"] == pytest.approx(78.6) and r["frac"] == pytest.approx(1.0)
     assert r["frac_of_packed_peak"] == pytest.approx(78.6 / 157.3)
+
+
+def test_code_without_comments():
+    src = 'int a = 1; // note\n/* block\n comment */ const char* s = "// not a comment";\nchar c = \'/\'; /**/x'
+    got = bench.code_without_comments(src)
+    assert "note" not in got and "block" not in got
+    assert '"// not a comment"' in got and "'/'" in got
+    assert got.replace(" ", "").replace("\n", "") == 'inta=1;constchar*s="//notacomment";charc=\'/\';x'
+    # comments alone do not change the code text; code does
+    assert bench.code_without_comments("x = 1; // a\n") == bench.code_without_comments("x = 1; // b\n")
+    assert bench.code_without_comments("x = 1;\n") != bench.code_without_comments("x = 2;\n")
