@@ -668,6 +668,27 @@ def measured_read_gbs(torch, glass, nbytes=1 << 30, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
+def measured_lds_gbs(torch, glass, rounds=2048, reps=10):
+    """The device's LDS read rate: glass_lds_read (16-byte reads by every
+    thread of 8 workgroups per compute unit; median of 10), in GB/s.  The
+    LDS-side fractions of the placements that stream through LDS are priced
+    against it.  The per-workgroup checksum is verified on the first word."""
+    dev = torch.device("cuda:0")
+    sink = torch.zeros(4096, dtype=torch.int32, device=dev)
+    wg = glass.lds_read(sink, rounds)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        glass.lds_read(sink, rounds)
+        b.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
+    words = sink[:wg].cpu().numpy()
+    assert np.all(words == words[0])
+    return wg * 256 * rounds * 8 * 16 / (ms * 1e-3) / 1e9
+
+
 def torch_copy_gbs(torch, nbytes=1 << 30, reps=10):
     """Device-to-device torch copy of 1 GiB (read + write bytes per second),
     reported for context."""
@@ -764,6 +785,7 @@ def main():
     if args.calibration_copy:
         calibration_copy(torch)
     read_gbs = measured_read_gbs(torch, glass)
+    lds_gbs = measured_lds_gbs(torch, glass)
     copy_gbs = torch_copy_gbs(torch)
     for r in res.values():
         rl = r["roofline"]
@@ -789,6 +811,7 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
         "measured_read_gbs": read_gbs,
+        "measured_lds_gbs": lds_gbs,
         "torch_copy_gbs": copy_gbs,
         "workloads": res,
     }

@@ -26,7 +26,7 @@ __all__ = [
     "pcg_batched_placement", "pcg_batched_pinned_rows", "PLACEMENT_RESIDENT",
     "PLACEMENT_STREAMED_PREFETCH",
     "PLACEMENT_STREAMED", "PLACEMENT_S_RESIDENT", "PLACEMENT_SEVERAL_PER_WAVE", "stream_read",
-    "pcg_batched_pinv_pass_rows",
+    "pcg_batched_pinv_pass_rows", "lds_read",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +82,7 @@ def load():
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
             "glass_pcg_grid_noalloc": ([P, P, P, P, I, I, I, D, D, P, P, P, I, U, P], I),
             "glass_stream_read": ([P, Z, P, Z, P], I),
+            "glass_lds_read": ([P, Z, I, ctypes.POINTER(ctypes.c_int), P], I),
             "glass_status_string": ([I], ctypes.c_char_p),
             "glass_last_error": ([], ctypes.c_char_p),
             "glass_version": ([], I),
@@ -354,6 +355,19 @@ def pcg_grid_noalloc(x, S, Pinv, b, state_size: int, knot_points: int, max_iters
                                        | (GRID_SINGLE_REDUCTION if single_reduction else 0),
                                        _stream(stream))
     _check(rc, "glass_pcg_grid_noalloc")
+
+
+def lds_read(sink, rounds: int, stream=None) -> int:
+    """Measurement aid (glass_lds_read): every workgroup launched fills 32 KB
+    of LDS and its threads read it back ``rounds`` * 8 times as 16-byte
+    vectors; ``sink`` (int32 device tensor, zeroed by the caller) receives one
+    XOR per workgroup.  Returns the number of workgroups launched."""
+    import torch
+    sk = _dev(sink, "sink", sink.numel(), torch.int32)
+    wg = ctypes.c_int(0)
+    rc = load().glass_lds_read(sk, sink.numel(), int(rounds), ctypes.byref(wg), _stream(stream))
+    _check(rc, "glass_lds_read")
+    return wg.value
 
 
 def stream_read(src, sink, stream=None):

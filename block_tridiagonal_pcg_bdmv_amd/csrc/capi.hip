@@ -383,6 +383,16 @@ int glass_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sin
   return glass::launch_stream_read(src, nbytes, sink, sink_words, (hipStream_t)hip_stream);
 }
 
+int glass_lds_read(unsigned* sink, size_t sink_words, int rounds, int* workgroups_out,
+                   void* hip_stream) {
+  if (!sink || !workgroups_out) return fail(GLASS_EINVAL, "LDS read: NULL pointer");
+  if (!glass::aligned(sink, 4) || sink_words == 0)
+    return fail(GLASS_EINVAL, "LDS read: sink must be 4-byte aligned with at least one word");
+  if (rounds < 1 || rounds > (1 << 20)) return fail(GLASS_EINVAL, "LDS read: rounds must be 1 .. 2^20");
+  return glass::launch_lds_read(sink, sink_words, rounds, workgroups_out,
+                                (hipStream_t)hip_stream);
+}
+
 const char* glass_status_string(int status) {
   switch (status) {
     case GLASS_OK: return "ok";
@@ -396,6 +406,6 @@ const char* glass_status_string(int status) {
 
 const char* glass_last_error(void) { return glass::last_error_text(); }
 
-int glass_version(void) { return 400; }
+int glass_version(void) { return 500; }
 
 }  // extern "C"

@@ -43,7 +43,59 @@ stream_read_kernel(const vec16_t* __restrict__ src, long long nvec, unsigned* __
   }
 }
 
+// LDS read-rate probe (a measurement aid): each workgroup of 256 threads fills
+// a 32 KB LDS buffer with word i = i * 0x9E3779B1, then every thread reads
+// 16-byte vectors k = (t + 256 u + 8 r) mod 2048 for r < rounds, u < 8, and
+// folds their words into an XOR; sink[w] = the XOR over the workgroup's
+// threads.  The rate of the call is the LDS's 16-byte read rate.
+constexpr int kLdsProbeVecs = 2048;  // 32 KB of 16-byte vectors
+
+__global__ void __launch_bounds__(kProbeThreads)
+lds_read_kernel(unsigned* __restrict__ sink, int rounds) {
+  __shared__ vec16_t buf[kLdsProbeVecs];
+  __shared__ unsigned red[kProbeThreads];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kLdsProbeVecs; i += kProbeThreads) {
+    const unsigned w = (unsigned)i * 4u;
+    buf[i] = vec16_t{__uint_as_float(w * 0x9E3779B1u), __uint_as_float((w + 1u) * 0x9E3779B1u),
+                     __uint_as_float((w + 2u) * 0x9E3779B1u),
+                     __uint_as_float((w + 3u) * 0x9E3779B1u)};
+  }
+  __syncthreads();
+  unsigned acc = 0u;
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const vec16_t v = buf[(tid + u * kProbeThreads + r * 8) & (kLdsProbeVecs - 1)];
+      acc ^= __float_as_uint(v[0]) ^ __float_as_uint(v[1]) ^ __float_as_uint(v[2]) ^
+             __float_as_uint(v[3]);
+    }
+  }
+  red[tid] = acc;
+  __syncthreads();
+  if (tid == 0) {
+    unsigned x = 0u;
+    for (int k = 0; k < kProbeThreads; ++k) x ^= red[k];
+    sink[blockIdx.x] = x;
+  }
+}
+
 }  // namespace
+
+int launch_lds_read(unsigned* sink, size_t sink_words, int rounds, int* workgroups,
+                    hipStream_t stream) {
+  DeviceInfo dev;
+  if (int rc = current_device_info(&dev)) return rc;
+  // Eight workgroups per compute unit at most, never more than the sink holds.
+  long long grid = std::min<long long>(8LL * dev.cu_count, (long long)sink_words);
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, stream, sink,
+                     rounds);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail_hip(e, "LDS read probe launch");
+  *workgroups = (int)grid;
+  return GLASS_OK;
+}
 
 int launch_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sink_words,
                        hipStream_t stream) {

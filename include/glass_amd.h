@@ -353,13 +353,28 @@ int glass_bdsv_batched(void* x, const void* S, const void* b, int state_size,
 int glass_stream_read(const void* src, size_t nbytes, unsigned* sink,
                       size_t sink_words, void* hip_stream);
 
+/*
+ * Measurement aid, not a step of the solve: the LDS read rate.  Launches up
+ * to sink_words workgroups (8 per compute unit at most) of 256 threads; each
+ * fills a 32 KB LDS buffer whose 32-bit word i is i * 0x9E3779B1 (mod 2^32),
+ * then every thread t reads the 16-byte vectors (t + 256 u + 8 r) mod 2048
+ * for r < rounds and u < 8 and folds their words into an XOR; sink[w] is the
+ * XOR over workgroup w's threads (words past the workgroups launched are
+ * left untouched).  *workgroups_out (host memory) receives the number of
+ * workgroups launched, so the call reads workgroups * 256 * rounds * 8 * 16
+ * bytes from LDS.  rounds: 1 .. 2^20.
+ */
+int glass_lds_read(unsigned* sink, size_t sink_words, int rounds, int* workgroups_out,
+                   void* hip_stream);
+
 /* Static text for a GLASS_* return code. */
 const char* glass_status_string(int status);
 /* Text describing the last failing call on this host thread ("" if none). */
 const char* glass_last_error(void);
 /* Library ABI version (major*10000 + minor*100 + patch).  0.2.0 added
  * glass_pcg_batched_pinned_rows and GLASS_PLACEMENT_S_RESIDENT; 0.3.0 added
- * glass_pcg_grid_noalloc; 0.4.0 added glass_pcg_batched_pinv_pass_rows. */
+ * glass_pcg_grid_noalloc; 0.4.0 added glass_pcg_batched_pinv_pass_rows; 0.5.0 added
+ * glass_lds_read. */
 int glass_version(void);
 
 #ifdef __cplusplus

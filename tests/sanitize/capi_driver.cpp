@@ -104,6 +104,10 @@ int main() {
   unsigned sink = 0;
   expect(glass_stream_read(F, 24, &sink, 1, nullptr), GLASS_EINVAL, "stream read size");
   expect(glass_stream_read(nullptr, 32, &sink, 1, nullptr), GLASS_EINVAL, "stream read src");
+  int wg = 0;
+  expect(glass_lds_read(&sink, 1, 0, &wg, nullptr), GLASS_EINVAL, "lds read rounds");
+  expect(glass_lds_read(&sink, 0, 4, &wg, nullptr), GLASS_EINVAL, "lds read sink words");
+  expect(glass_lds_read(&sink, 1, 4, nullptr, nullptr), GLASS_EINVAL, "lds read wg out");
   // status text
   for (int code = -6; code <= 2; ++code)
     if (!glass_status_string(code) || std::strlen(glass_status_string(code)) == 0) ++failures;

@@ -1,7 +1,9 @@
 """The streaming-read probe (a measurement aid of the benchmark) reads every
 byte it is given: the XOR of its per-workgroup words equals the XOR of all
 32-bit words of the buffer, for sizes that fill several rounds of the grid,
-one partial round and a single 16-byte vector."""
+one partial round and a single 16-byte vector.  The LDS read probe's
+per-workgroup XOR equals the one computed here from its documented fill and
+read pattern."""
 
 import numpy as np
 import pytest
@@ -23,6 +25,38 @@ def test_stream_read_checksum(gpu, nwords):
     torch.cuda.synchronize()
     got = np.bitwise_xor.reduce(sink.cpu().numpy())
     assert got == np.bitwise_xor.reduce(host)
+
+
+def lds_probe_expected(rounds):
+    """XOR of the words a 256-thread workgroup of the LDS probe reads: word i
+    of the buffer is i * 0x9E3779B1 (mod 2^32); thread t reads 16-byte vector
+    (t + 256 u + 8 r) mod 2048 for u < 8, r < rounds."""
+    words = (np.arange(4 * 2048, dtype=np.uint64) * 0x9E3779B1) & 0xFFFFFFFF
+    vec = np.bitwise_xor.reduce(words.reshape(2048, 4), axis=1)
+    t = np.arange(256)[:, None, None]
+    u = np.arange(8)[None, :, None]
+    r = np.arange(rounds)[None, None, :]
+    idx = (t + 256 * u + 8 * r) % 2048
+    return int(np.bitwise_xor.reduce(vec[idx].ravel()))
+
+
+@pytest.mark.parametrize("rounds,sink_words", [(1, 4096), (3, 5), (257, 4096)])
+def test_lds_read_checksum(gpu, rounds, sink_words):
+    sink = torch.zeros(sink_words, dtype=torch.int32, device="cuda")
+    say("lds read rounds=%d sink=%d" % (rounds, sink_words))
+    wg = gpu.lds_read(sink, rounds)
+    torch.cuda.synchronize()
+    assert 1 <= wg <= sink_words
+    got = sink.cpu().numpy().view(np.uint32)
+    assert np.all(got[:wg] == np.uint32(lds_probe_expected(rounds)))
+    assert np.all(got[wg:] == 0)
+
+
+def test_lds_read_rejects_bad_rounds(gpu):
+    sink = torch.zeros(8, dtype=torch.int32, device="cuda")
+    with pytest.raises(gpu.GlassError) as ei:
+        gpu.lds_read(sink, 0)
+    assert ei.value.code == -1
 
 
 def test_stream_read_rejects_bad_sizes(gpu):
