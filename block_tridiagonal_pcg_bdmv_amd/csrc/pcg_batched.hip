@@ -16,7 +16,9 @@
 //   x, r, p (and the transient z, S p) live in registers.
 // * only p and r must be seen by other lanes (the 3*ss matvec window), so
 //   they are the two padded vectors kept in LDS; the page's other work
-//   vectors stay in registers.
+//   vectors stay in registers.  Where both matrices stay on chip, each block
+//   of ss entries takes a whole number of 16-byte vectors in LDS, so a
+//   window is read with 16-byte loads.
 // * dots: each 64-row chunk's products -> wave64 DPP tree -> one LDS slot per
 //   chunk -> every thread adds the slots in chunk order.  alpha, beta and the
 //   stopping decision are therefore computed identically (same bits) by every
@@ -119,6 +121,20 @@ struct PcgArgs {
                        // after their S chunks (coalesced), not row by row
 };
 
+// Block stride of the padded vectors in LDS: ss rounded up to whole 16-byte
+// vectors, so every window starts 16-byte aligned and its reads can be
+// 16-byte LDS loads (twice the delivery rate of 4- and 8-byte ones).  The
+// tail of each block is never read.  The placements that hold both
+// matrices on chip (resident, and S resident with Pinv's D blocks in LDS)
+// use it; the streamed ones keep blocks of ss (they measured no faster
+// padded, and the plain streamed placement, the fallback for the largest
+// problems, needs the least LDS).
+template <typename T>
+__host__ __device__ constexpr int vec_block(int ss, bool padded = true) {
+  return padded ? (ss + (int)(16 / sizeof(T)) - 1) / (int)(16 / sizeof(T)) * (int)(16 / sizeof(T))
+                : ss;
+}
+
 // Placements of the matrices (see the header).
 enum Mode {
   kResident = 0,
@@ -177,7 +193,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
   const int W = 3 * ss;
   const int kp = a.kp;
   const int n = kp * ss;
-  const int pad_len = (kp + 2) * ss;
+  // p and r in LDS as kp + 2 blocks of ssp elements (a zero block at each
+  // end, ss entries used per block).
+  constexpr bool PADV = RES || HYBP;
+  constexpr int SSP = SS > 0 ? vec_block<T>(SS, PADV) : 0;
+  const int ssp = SS > 0 ? SSP : vec_block<T>(ss, PADV);
+  const int pad_len = (kp + 2) * ssp;
   const int NT = blockDim.x;
   const int NW = NT >> 6;
   const int tid = threadIdx.x;
@@ -224,15 +245,23 @@ pcg_batched_kernel(PcgArgs<T> a) {
   T* pinv_lds = reinterpret_cast<T*>(smem_raw + head);
 
   // Row bookkeeping.
-  int row[RPT], wstart[RPT];
+  int row[RPT], wstart[RPT], vix[RPT];
   bool valid[RPT];
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     row[k] = (wave + k * NW) * 64 + lane;
     valid[k] = row[k] < n;
     const int br = valid[k] ? row[k] / ss : 0;
-    wstart[k] = br * ss;  // window start in a padded vector
+    wstart[k] = br * ssp;                         // window start in a padded vector
+    vix[k] = (br + 1) * ssp + (row[k] - br * ss);  // the row's own entry
   }
+  // Window entry c (0 <= c < 3*ss) of a padded vector window w: block c / ss,
+  // entry c % ss.  The window start is 16-byte aligned.
+  auto win = [&](const T* __restrict__ w, int c) -> T {
+    const T* __restrict__ wa = w;
+    if constexpr (PADV) wa = static_cast<const T*>(__builtin_assume_aligned(w, 16));
+    return SS > 0 ? wa[(c / SS) * SSP + c % SS] : wa[(c / ss) * ssp + c % ss];
+  };
 
   // Chunk k of this wave: rows [r0, r0 + nrows) of a matrix, which are one
   // contiguous range of count = nrows * W elements.
@@ -458,10 +487,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
           const T* __restrict__ w = vpad + wstart[k];
           if constexpr (PD && MI == 1) {
 #pragma unroll
-            for (int c = 0; c < WCP; ++c) acc = fma(mreg[k][c], w[SS + c], acc);
+            for (int c = 0; c < WCP; ++c) acc = fma(mreg[k][c], win(w, SS + c), acc);
           } else {
 #pragma unroll
-            for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], w[c], acc);
+            for (int c = 0; c < WC; ++c) acc = fma(mreg[k][c], win(w, c), acc);
           }
         }
       } else if constexpr (HYBS) {
@@ -482,13 +511,13 @@ pcg_batched_kernel(PcgArgs<T> a) {
             const T* __restrict__ w = vpad + wstart[k];
             if (from_reg) {
 #pragma unroll
-              for (int c = 0; c < WC; ++c) acc = fma(mS[RPT - 1][c], w[c], acc);
+              for (int c = 0; c < WC; ++c) acc = fma(mS[RPT - 1][c], win(w, c), acc);
             } else {
               const T* __restrict__ m = stage_shift(gP, from_pin ? pinned : stage) + lane * W;
 #pragma unroll 3
               for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
 #pragma unroll
-                for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], w[c], acc);
+                for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], win(w, c), acc);
               }
             }
           }
@@ -510,9 +539,9 @@ pcg_batched_kernel(PcgArgs<T> a) {
         // window (the terms and order of a D-only row).
         if (valid[k]) {
           const T* __restrict__ m = pinv_lds + row[k] * SS;
-          const T* __restrict__ w = vpad + wstart[k] + SS;
+          const T* __restrict__ w = vpad + wstart[k];
 #pragma unroll
-          for (int c = 0; c < SS; ++c) acc = fma(m[c], w[c], acc);
+          for (int c = 0; c < SS; ++c) acc = fma(m[c], win(w, SS + c), acc);
         }
       } else {
         const int r0 = chunk_r0(k);
@@ -543,12 +572,13 @@ pcg_batched_kernel(PcgArgs<T> a) {
           wave_lds_sync();
           if (valid[k] && mpacked) {
             const T* __restrict__ m = stage + lane * ss;
-            const T* __restrict__ w = vpad + wstart[k] + ss;
+            const T* __restrict__ w = vpad + wstart[k];
             if constexpr (SS > 0) {
 #pragma unroll
-              for (int c = 0; c < SS; ++c) acc = fma(m[c], w[c], acc);
+              for (int c = 0; c < SS; ++c) acc = fma(m[c], win(w, SS + c), acc);
             } else {
-              for (int c = 0; c < ss; ++c) acc = fma(m[c], w[c], acc);
+              const T* __restrict__ wd = w + ssp;
+              for (int c = 0; c < ss; ++c) acc = fma(m[c], wd[c], acc);
             }
           } else if (valid[k]) {
             const T* __restrict__ m = stage + lane * W;
@@ -558,10 +588,13 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll 3
               for (int c0 = 0; c0 < 3 * SS; c0 += SS) {
 #pragma unroll
-                for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], w[c], acc);
+                for (int c = c0; c < c0 + SS; ++c) acc = fma(m[c], win(w, c), acc);
               }
             } else {
-              for (int c = 0; c < W; ++c) acc = fma(m[c], w[c], acc);
+              // Three blocks of ss entries, in the order of the row.
+              for (int b3 = 0; b3 < 3; ++b3)
+                for (int c = 0; c < ss; ++c)
+                  acc = fma(m[b3 * ss + c], w[b3 * ssp + c], acc);
             }
           }
           wave_lds_sync();
@@ -684,12 +717,12 @@ pcg_batched_kernel(PcgArgs<T> a) {
   dma_pinv_whole();
 #pragma unroll
   for (int k = 0; k < RPT; ++k)
-    if (valid[k]) p_pad[ss + row[k]] = xr[k];
-  for (int e = tid; e < ss; e += NT) {
+    if (valid[k]) p_pad[vix[k]] = xr[k];
+  for (int e = tid; e < ssp; e += NT) {
     p_pad[e] = T(0);
-    p_pad[(kp + 1) * ss + e] = T(0);
+    p_pad[(kp + 1) * ssp + e] = T(0);
     r_pad[e] = T(0);
-    r_pad[(kp + 1) * ss + e] = T(0);
+    r_pad[(kp + 1) * ssp + e] = T(0);
   }
   block_sync();
 
@@ -698,7 +731,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     rr[k] = valid[k] ? tmp[k] - sv[k] : T(0);
-    if (valid[k]) r_pad[ss + row[k]] = rr[k];
+    if (valid[k]) r_pad[vix[k]] = rr[k];
   }
   // D blocks, or pinned chunks, landed
   if constexpr (HYBP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -719,7 +752,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
   for (int k = 0; k < RPT; ++k) {
     pr[k] = sv[k];
-    if (valid[k]) p_pad[ss + row[k]] = pr[k];  // p = z (x0 reads are done)
+    if (valid[k]) p_pad[vix[k]] = pr[k];  // p = z (x0 reads are done)
   }
   T rho = chunk_dot(rr, sv, slotA);  // also publishes p_pad
   const T rho0 = rho;
@@ -743,7 +776,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
       for (int k = 0; k < RPT; ++k) {
         xr[k] = fma(alpha, pr[k], xr[k]);
         rr[k] = fma(-alpha, sv[k], rr[k]);
-        if (valid[k]) r_pad[ss + row[k]] = rr[k];
+        if (valid[k]) r_pad[vix[k]] = rr[k];
       }
       iters = it + 1;
       block_sync();
@@ -760,7 +793,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
 #pragma unroll
       for (int k = 0; k < RPT; ++k) {
         pr[k] = fma(beta, pr[k], sv[k]);
-        if (valid[k]) p_pad[ss + row[k]] = pr[k];
+        if (valid[k]) p_pad[vix[k]] = pr[k];
       }
       rho = rz;
       block_sync();
@@ -805,9 +838,11 @@ struct Plan {
 };
 
 template <typename T>
-size_t lds_bytes(int ss, int kp, int NW, int stage_elems) {
+size_t lds_bytes(int ss, int kp, int NW, int stage_elems, bool padded = true) {
   const size_t nchunks = ((size_t)kp * ss + 63) / 64;
-  const size_t head = ((size_t)(2 * (kp + 2) * ss + 2 * nchunks) * sizeof(T) + 15) & ~(size_t)15;
+  const size_t head =
+      ((size_t)(2 * (kp + 2) * vec_block<T>(ss, padded) + 2 * nchunks) * sizeof(T) + 15) &
+      ~(size_t)15;
   return head + (size_t)NW * stage_elems * sizeof(T);
 }
 
@@ -915,7 +950,7 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       // hold a Pinv chunk; take it when that pins more chunks in all (LDS
       // slots below plus those registers).
       auto pins = [&](int nw) {
-        const size_t used = lds_bytes<T>(ss, kp, nw, prefetch_stage_elems<T>(ss));
+        const size_t used = lds_bytes<T>(ss, kp, nw, prefetch_stage_elems<T>(ss), false);
         if (used > lds_max) return -1;
         const size_t slot = (size_t)prefetch_stage_elems<T>(ss) * sizeof(T);
         int have_last = 0, reg = 0;
@@ -933,7 +968,7 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       const size_t dbytes = ((size_t)n * ss * sizeof(T) + 1023) & ~(size_t)1023;
       const int stage = pinv_diag ? 0 : prefetch_stage_elems<T>(ss);
       const size_t lds = pinv_diag ? lds_bytes<T>(ss, kp, NW, 0) + dbytes
-                                   : lds_bytes<T>(ss, kp, NW, stage);
+                                   : lds_bytes<T>(ss, kp, NW, stage, false);
       if (lds > lds_max) continue;
       Plan p;
       p.NW = NW;
@@ -972,7 +1007,7 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       const int NW = (nchunks + rpt - 1) / rpt;
       if (NW * 64 > max_threads_for(rpt, mode)) continue;
       const int stage = pf ? prefetch_stage_elems<T>(ss) : 64 * W;
-      const size_t lds = lds_bytes<T>(ss, kp, NW, stage);
+      const size_t lds = lds_bytes<T>(ss, kp, NW, stage, false);
       if (lds > lds_max) continue;
       const int waste = NW * rpt - nchunks;
       if (!found || waste < best_waste || (waste == best_waste && NW > best.NW)) {
