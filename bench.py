@@ -668,19 +668,20 @@ def measured_read_gbs(torch, glass, nbytes=1 << 30, reps=10):
     return nbytes / (ms * 1e-3) / 1e9
 
 
-def measured_lds_gbs(torch, glass, rounds=2048, reps=10):
-    """The device's LDS read rate: glass_lds_read (16-byte reads by every
-    thread of 8 workgroups per compute unit; median of 10), in GB/s.  The
-    LDS-side fractions of the placements that stream through LDS are priced
-    against it.  The per-workgroup checksum is verified on the first word."""
+def measured_lds_gbs(torch, glass, rounds=2048, reps=10, width=16):
+    """The device's LDS read rate: glass_lds_read (loads of ``width`` bytes
+    per lane by every thread of 8 workgroups per compute unit; median of 10),
+    in GB/s.  The LDS-side fractions of the placements that stream through
+    LDS are priced against the 16-byte rate.  Every workgroup's checksum must
+    agree."""
     dev = torch.device("cuda:0")
     sink = torch.zeros(4096, dtype=torch.int32, device=dev)
-    wg = glass.lds_read(sink, rounds)
+    wg = glass.lds_read(sink, rounds, width)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for a, b in ev:
         a.record()
-        glass.lds_read(sink, rounds)
+        glass.lds_read(sink, rounds, width)
         b.record()
     torch.cuda.synchronize()
     ms = float(np.median([a.elapsed_time(b) for a, b in ev]))
@@ -785,7 +786,7 @@ def main():
     if args.calibration_copy:
         calibration_copy(torch)
     read_gbs = measured_read_gbs(torch, glass)
-    lds_gbs = measured_lds_gbs(torch, glass)
+    lds_gbs = {w: measured_lds_gbs(torch, glass, width=w) for w in (16, 8, 4)}
     copy_gbs = torch_copy_gbs(torch)
     for r in res.values():
         rl = r["roofline"]
@@ -811,7 +812,8 @@ def main():
         "roofline": head["roofline"],
         "cpu_baseline": head.get("cpu_baseline"),
         "measured_read_gbs": read_gbs,
-        "measured_lds_gbs": lds_gbs,
+        "measured_lds_gbs": lds_gbs[16],
+        "measured_lds_gbs_by_load_width": {"%d B" % w: v for w, v in lds_gbs.items()},
         "torch_copy_gbs": copy_gbs,
         "workloads": res,
     }

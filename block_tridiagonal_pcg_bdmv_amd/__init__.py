@@ -82,7 +82,7 @@ def load():
             "glass_pcg_grid_ex": ([P, P, P, P, I, I, I, D, D, P, P, P, P, Z, I, U, P], I),
             "glass_pcg_grid_noalloc": ([P, P, P, P, I, I, I, D, D, P, P, P, I, U, P], I),
             "glass_stream_read": ([P, Z, P, Z, P], I),
-            "glass_lds_read": ([P, Z, I, ctypes.POINTER(ctypes.c_int), P], I),
+            "glass_lds_read": ([P, Z, I, I, ctypes.POINTER(ctypes.c_int), P], I),
             "glass_status_string": ([I], ctypes.c_char_p),
             "glass_last_error": ([], ctypes.c_char_p),
             "glass_version": ([], I),
@@ -357,15 +357,17 @@ def pcg_grid_noalloc(x, S, Pinv, b, state_size: int, knot_points: int, max_iters
     _check(rc, "glass_pcg_grid_noalloc")
 
 
-def lds_read(sink, rounds: int, stream=None) -> int:
+def lds_read(sink, rounds: int, bytes_per_load: int = 16, stream=None) -> int:
     """Measurement aid (glass_lds_read): every workgroup launched fills 32 KB
     of LDS and its threads read it back ``rounds`` * 8 times as 16-byte
-    vectors; ``sink`` (int32 device tensor, zeroed by the caller) receives one
-    XOR per workgroup.  Returns the number of workgroups launched."""
+    vectors, each with loads of ``bytes_per_load`` (4, 8 or 16) bytes per lane;
+    ``sink`` (int32 device tensor, zeroed by the caller) receives one XOR per
+    workgroup.  Returns the number of workgroups launched."""
     import torch
     sk = _dev(sink, "sink", sink.numel(), torch.int32)
     wg = ctypes.c_int(0)
-    rc = load().glass_lds_read(sk, sink.numel(), int(rounds), ctypes.byref(wg), _stream(stream))
+    rc = load().glass_lds_read(sk, sink.numel(), int(rounds), int(bytes_per_load),
+                               ctypes.byref(wg), _stream(stream))
     _check(rc, "glass_lds_read")
     return wg.value
 

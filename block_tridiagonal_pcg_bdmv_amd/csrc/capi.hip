@@ -383,13 +383,15 @@ int glass_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sin
   return glass::launch_stream_read(src, nbytes, sink, sink_words, (hipStream_t)hip_stream);
 }
 
-int glass_lds_read(unsigned* sink, size_t sink_words, int rounds, int* workgroups_out,
-                   void* hip_stream) {
+int glass_lds_read(unsigned* sink, size_t sink_words, int rounds, int bytes_per_load,
+                   int* workgroups_out, void* hip_stream) {
   if (!sink || !workgroups_out) return fail(GLASS_EINVAL, "LDS read: NULL pointer");
   if (!glass::aligned(sink, 4) || sink_words == 0)
     return fail(GLASS_EINVAL, "LDS read: sink must be 4-byte aligned with at least one word");
   if (rounds < 1 || rounds > (1 << 20)) return fail(GLASS_EINVAL, "LDS read: rounds must be 1 .. 2^20");
-  return glass::launch_lds_read(sink, sink_words, rounds, workgroups_out,
+  if (bytes_per_load != 4 && bytes_per_load != 8 && bytes_per_load != 16)
+    return fail(GLASS_EINVAL, "LDS read: bytes_per_load must be 4, 8 or 16");
+  return glass::launch_lds_read(sink, sink_words, rounds, bytes_per_load, workgroups_out,
                                 (hipStream_t)hip_stream);
 }
 

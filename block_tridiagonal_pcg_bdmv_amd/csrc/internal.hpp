@@ -86,7 +86,7 @@ int launch_pcg_grid(glass_dtype dt, void* x, const void* S, const void* Pinv,
                     bool exclusive, bool single, bool keep, hipStream_t stream);
 
 // Streaming-read probe (measurement aid); arguments validated by the C ABI.
-int launch_lds_read(unsigned* sink, size_t sink_words, int rounds, int* workgroups,
+int launch_lds_read(unsigned* sink, size_t sink_words, int rounds, int width, int* workgroups,
                     hipStream_t stream);
 int launch_stream_read(const void* src, size_t nbytes, unsigned* sink, size_t sink_words,
                        hipStream_t stream);

@@ -47,9 +47,13 @@ stream_read_kernel(const vec16_t* __restrict__ src, long long nvec, unsigned* __
 // a 32 KB LDS buffer with word i = i * 0x9E3779B1, then every thread reads
 // 16-byte vectors k = (t + 256 u + 8 r) mod 2048 for r < rounds, u < 8, and
 // folds their words into an XOR; sink[w] = the XOR over the workgroup's
-// threads.  The rate of the call is the LDS's 16-byte read rate.
+// threads.  WIDTH is the bytes one LDS load instruction reads per lane: 16
+// (one ds_read_b128 per vector), 8 or 4 (two ds_read_b64 or four ds_read_b32,
+// kept apart by volatile accesses).  The rate of the call is the LDS's read
+// rate at that width.
 constexpr int kLdsProbeVecs = 2048;  // 32 KB of 16-byte vectors
 
+template <int WIDTH>
 __global__ void __launch_bounds__(kProbeThreads)
 lds_read_kernel(unsigned* __restrict__ sink, int rounds) {
   __shared__ vec16_t buf[kLdsProbeVecs];
@@ -66,9 +70,21 @@ lds_read_kernel(unsigned* __restrict__ sink, int rounds) {
   for (int r = 0; r < rounds; ++r) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const vec16_t v = buf[(tid + u * kProbeThreads + r * 8) & (kLdsProbeVecs - 1)];
-      acc ^= __float_as_uint(v[0]) ^ __float_as_uint(v[1]) ^ __float_as_uint(v[2]) ^
-             __float_as_uint(v[3]);
+      const int k = (tid + u * kProbeThreads + r * 8) & (kLdsProbeVecs - 1);
+      if constexpr (WIDTH == 16) {
+        const vec16_t v = buf[k];
+        acc ^= __float_as_uint(v[0]) ^ __float_as_uint(v[1]) ^ __float_as_uint(v[2]) ^
+               __float_as_uint(v[3]);
+      } else if constexpr (WIDTH == 8) {
+        typedef __attribute__((address_space(3))) const volatile unsigned long long lds_u64;
+        const lds_u64* q = (const lds_u64*)(&buf[k]);
+        const unsigned long long a0 = q[0], a1 = q[1];
+        acc ^= (unsigned)a0 ^ (unsigned)(a0 >> 32) ^ (unsigned)a1 ^ (unsigned)(a1 >> 32);
+      } else {
+        typedef __attribute__((address_space(3))) const volatile unsigned lds_u32;
+        const lds_u32* q = (const lds_u32*)(&buf[k]);
+        acc ^= q[0] ^ q[1] ^ q[2] ^ q[3];
+      }
     }
   }
   red[tid] = acc;
@@ -82,15 +98,15 @@ lds_read_kernel(unsigned* __restrict__ sink, int rounds) {
 
 }  // namespace
 
-int launch_lds_read(unsigned* sink, size_t sink_words, int rounds, int* workgroups,
+int launch_lds_read(unsigned* sink, size_t sink_words, int rounds, int width, int* workgroups,
                     hipStream_t stream) {
   DeviceInfo dev;
   if (int rc = current_device_info(&dev)) return rc;
   // Eight workgroups per compute unit at most, never more than the sink holds.
   long long grid = std::min<long long>(8LL * dev.cu_count, (long long)sink_words);
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)grid), dim3(kProbeThreads), 0, stream, sink,
-                     rounds);
+  auto kern = width == 16 ? lds_read_kernel<16> : width == 8 ? lds_read_kernel<8> : lds_read_kernel<4>;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kProbeThreads), 0, stream, sink, rounds);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail_hip(e, "LDS read probe launch");
   *workgroups = (int)grid;

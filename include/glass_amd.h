@@ -360,12 +360,14 @@ int glass_stream_read(const void* src, size_t nbytes, unsigned* sink,
  * then every thread t reads the 16-byte vectors (t + 256 u + 8 r) mod 2048
  * for r < rounds and u < 8 and folds their words into an XOR; sink[w] is the
  * XOR over workgroup w's threads (words past the workgroups launched are
- * left untouched).  *workgroups_out (host memory) receives the number of
- * workgroups launched, so the call reads workgroups * 256 * rounds * 8 * 16
- * bytes from LDS.  rounds: 1 .. 2^20.
+ * left untouched).  bytes_per_load (4, 8 or 16) is what one LDS load
+ * instruction reads per lane: each vector is read with one 16-byte load, two
+ * 8-byte or four 4-byte ones; the XOR is the same.  *workgroups_out (host
+ * memory) receives the number of workgroups launched, so the call reads
+ * workgroups * 256 * rounds * 8 * 16 bytes from LDS.  rounds: 1 .. 2^20.
  */
-int glass_lds_read(unsigned* sink, size_t sink_words, int rounds, int* workgroups_out,
-                   void* hip_stream);
+int glass_lds_read(unsigned* sink, size_t sink_words, int rounds, int bytes_per_load,
+                   int* workgroups_out, void* hip_stream);
 
 /* Static text for a GLASS_* return code. */
 const char* glass_status_string(int status);

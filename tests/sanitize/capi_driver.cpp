@@ -105,9 +105,10 @@ int main() {
   expect(glass_stream_read(F, 24, &sink, 1, nullptr), GLASS_EINVAL, "stream read size");
   expect(glass_stream_read(nullptr, 32, &sink, 1, nullptr), GLASS_EINVAL, "stream read src");
   int wg = 0;
-  expect(glass_lds_read(&sink, 1, 0, &wg, nullptr), GLASS_EINVAL, "lds read rounds");
-  expect(glass_lds_read(&sink, 0, 4, &wg, nullptr), GLASS_EINVAL, "lds read sink words");
-  expect(glass_lds_read(&sink, 1, 4, nullptr, nullptr), GLASS_EINVAL, "lds read wg out");
+  expect(glass_lds_read(&sink, 1, 0, 16, &wg, nullptr), GLASS_EINVAL, "lds read rounds");
+  expect(glass_lds_read(&sink, 0, 4, 16, &wg, nullptr), GLASS_EINVAL, "lds read sink words");
+  expect(glass_lds_read(&sink, 1, 4, 16, nullptr, nullptr), GLASS_EINVAL, "lds read wg out");
+  expect(glass_lds_read(&sink, 1, 4, 12, &wg, nullptr), GLASS_EINVAL, "lds read width");
   // status text
   for (int code = -6; code <= 2; ++code)
     if (!glass_status_string(code) || std::strlen(glass_status_string(code)) == 0) ++failures;

@@ -36,6 +36,6 @@ int launch_pcg_grid(glass_dtype, void*, const void*, const void*, const void*, i
                     hipStream_t) {
   return GLASS_EHIP;
 }
-int launch_lds_read(unsigned*, size_t, int, int*, hipStream_t) { return GLASS_EHIP; }
+int launch_lds_read(unsigned*, size_t, int, int, int*, hipStream_t) { return GLASS_EHIP; }
 int launch_stream_read(const void*, size_t, unsigned*, size_t, hipStream_t) { return GLASS_EHIP; }
 }  // namespace glass

@@ -40,11 +40,13 @@ def lds_probe_expected(rounds):
     return int(np.bitwise_xor.reduce(vec[idx].ravel()))
 
 
-@pytest.mark.parametrize("rounds,sink_words", [(1, 4096), (3, 5), (257, 4096)])
-def test_lds_read_checksum(gpu, rounds, sink_words):
+@pytest.mark.parametrize("rounds,sink_words,width", [(1, 4096, 16), (3, 5, 16), (257, 4096, 16),
+                                                    (3, 5, 8), (257, 4096, 8), (3, 5, 4),
+                                                    (257, 4096, 4)])
+def test_lds_read_checksum(gpu, rounds, sink_words, width):
     sink = torch.zeros(sink_words, dtype=torch.int32, device="cuda")
-    say("lds read rounds=%d sink=%d" % (rounds, sink_words))
-    wg = gpu.lds_read(sink, rounds)
+    say("lds read rounds=%d sink=%d width=%d" % (rounds, sink_words, width))
+    wg = gpu.lds_read(sink, rounds, width)
     torch.cuda.synchronize()
     assert 1 <= wg <= sink_words
     got = sink.cpu().numpy().view(np.uint32)
@@ -52,11 +54,12 @@ def test_lds_read_checksum(gpu, rounds, sink_words):
     assert np.all(got[wg:] == 0)
 
 
-def test_lds_read_rejects_bad_rounds(gpu):
+def test_lds_read_rejects_bad_arguments(gpu):
     sink = torch.zeros(8, dtype=torch.int32, device="cuda")
-    with pytest.raises(gpu.GlassError) as ei:
-        gpu.lds_read(sink, 0)
-    assert ei.value.code == -1
+    for rounds, width in ((0, 16), (4, 12)):
+        with pytest.raises(gpu.GlassError) as ei:
+            gpu.lds_read(sink, rounds, width)
+        assert ei.value.code == -1
 
 
 def test_stream_read_rejects_bad_sizes(gpu):
