@@ -75,6 +75,27 @@ __device__ __forceinline__ T wave_sum(T v) {
   return read_lane(v, 0) + read_lane(v, 32);
 }
 
+// s = ((slots[0] + slots[1]) + slots[2]) + ... + slots[n-1], n >= 1, the
+// plain left-to-right sum, in every lane with the same bits: lane j loads
+// slot j (and j + 64, ... for more than 64 slots; lanes past the end re-load
+// the last slot), so one LDS round trip brings them all, and the additions
+// then take the slots from the lanes one by one in order.  All 64 lanes of
+// the wave must be active.
+template <typename T>
+__device__ __forceinline__ T sum_slots_in_order(const T* slots, int n) {
+  const int lane = threadIdx.x & 63;
+  T v = slots[min(lane, n - 1)];
+  T s = read_lane(v, 0);
+  const int n0 = min(n, 64);
+  for (int c = 1; c < n0; ++c) s = s + read_lane(v, c);
+  for (int base = 64; base < n; base += 64) {
+    const T w = slots[min(base + lane, n - 1)];
+    const int m = min(n - base, 64);
+    for (int c = 0; c < m; ++c) s = s + read_lane(w, c);
+  }
+  return s;
+}
+
 // Workgroup-wide sum; every thread of the block must call it.  `slots` is an
 // LDS array of one entry per wave that no other live block_sum is using (the
 // callers alternate two arrays; a barrier separates reads of one use from

@@ -624,9 +624,18 @@ pcg_batched_kernel(PcgArgs<T> a) {
       }
     }
     block_sync();
-    T s = slots[0];
-    for (int c = 1; c < nchunks; ++c) s = s + slots[c];
-    return s;
+    // Resident placements: all slots in one LDS round trip, added from the
+    // lanes in order.  The others keep the slot-by-slot loop, which measured
+    // faster there (the S-resident kernels are 4-9 % slower with the lane
+    // form, for reasons not found); both add the same values in the same
+    // order, so the bits agree.
+    if constexpr (RES) {
+      return sum_slots_in_order(slots, nchunks);
+    } else {
+      T s = slots[0];
+      for (int c = 1; c < nchunks; ++c) s = s + slots[c];
+      return s;
+    }
   };
 
   // Initial state: p_pad temporarily holds x0 (the vector S multiplies).
