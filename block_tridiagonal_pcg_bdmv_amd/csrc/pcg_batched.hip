@@ -626,9 +626,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
     block_sync();
     // Resident placements: all slots in one LDS round trip, added from the
     // lanes in order.  The others keep the slot-by-slot loop, which measured
-    // faster there (the S-resident kernels are 4-9 % slower with the lane
-    // form, for reasons not found); both add the same values in the same
-    // order, so the bits agree.
+    // faster there: the S-resident kernels hold 3*ss S values per lane, and
+    // the lane form's extra live values left their stage matvec fewer
+    // registers for LDS reads in flight (4-9 % slower).  Both add the same
+    // values in the same order, so the bits agree.
     if constexpr (RES) {
       return sum_slots_in_order(slots, nchunks);
     } else {
