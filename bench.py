@@ -16,7 +16,8 @@ starts from its own copy of x0 = 0 (prepared before the timed region), so no
 step starts from an already-converged x.
 
 Roofline: ``achieved`` = algorithmic bytes per launch / mean launch duration
-(HIP events around each launch on the stream the library launches on).
+(HIP events before the first and after the last timed launch, on the stream
+the library launches on, divided by the number of launches).
 ``traffic`` = HBM bytes per launch of the workload's kernel measured by the
 rocprofv3 FETCH_SIZE / WRITE_SIZE counters and calibrated against a copy of
 known size; it is read from ``profiles/hbm_traffic.md`` and reported only
@@ -342,14 +343,26 @@ def summarize_pmc(fetch_csv, write_csv, fetch_cmd, write_cmd, out=TRAFFIC_FILE, 
 
 class Timer:
     """HIP events on the stream the library launches on (torch's current
-    stream): per-launch durations inside the timed region."""
+    stream), one before the first and one after the last of the timed
+    launches: the average launch duration over the timed region, the short
+    gaps between back-to-back launches included.  No events go between the
+    launches: on the headline solve a pair around every launch added about
+    8 us per step to the wall time and lengthened the launches themselves
+    (450 against 442 us)."""
 
     def __init__(self, torch, steps):
-        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(steps)]
+        self.steps = steps
+        self.a = torch.cuda.Event(enable_timing=True)
+        self.b = torch.cuda.Event(enable_timing=True)
 
-    def launch_ms(self):
-        return [a.elapsed_time(b) for a, b in self.ev]
+    def start(self):
+        self.a.record()
+
+    def stop(self):
+        self.b.record()
+
+    def avg_ms(self):
+        return self.a.elapsed_time(self.b) / self.steps
 
 
 def isolated_ms(torch, fn, reps=10):
@@ -485,16 +498,15 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic,
     torch.cuda.synchronize()
     tm = Timer(torch, steps)
     t0 = time.perf_counter()
+    tm.start()
     for k in range(steps):
-        tm.ev[k][0].record()
         run(xs[k])
-        tm.ev[k][1].record()
+    tm.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = tm.launch_ms()
     it = iters.cpu().numpy()
     st = status.cpu().numpy()
-    avg_ms = float(np.mean(launch_ms))
+    avg_ms = tm.avg_ms()
     # S and Pinv count once if they stay on chip (the grid solve and the
     # batched resident placement), else once per pass.
     placement = None if grid else glass.pcg_batched_placement(
@@ -516,7 +528,6 @@ def bench_pcg(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic,
         "kernel": KERNEL_OF[key], "dtype": np.dtype(w.dtype).name, "state_size": w.ss,
         "knot_points": w.kp, "n_problems": B, "solves_per_s": B * steps / wall,
         "ms_per_step": wall * 1e3 / steps, "kernel_ms_avg": avg_ms,
-        "kernel_ms_min": float(np.min(launch_ms)),
         "kernel_ms_isolated": iso,
         "iterations": {str(k): int(v) for k, v in zip(*np.unique(it, return_counts=True))},
         # every timed solve must have converged (a breakdown or a grid
@@ -560,21 +571,20 @@ def bench_bdmv(torch, glass, steps, warmup, cpu_budget, with_cpu, traffic):
     torch.cuda.synchronize()
     tm = Timer(torch, steps)
     t0 = time.perf_counter()
+    tm.start()
     for k in range(steps):
-        tm.ev[k][0].record()
         glass.bdmv_batched(y, S, v, w.ss, w.kp)
-        tm.ev[k][1].record()
+    tm.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = tm.launch_ms()
-    avg_ms = float(np.mean(launch_ms))
+    avg_ms = tm.avg_ms()
     nbytes = algorithmic_bytes_bdmv(w, w.n_problems)
     iso = isolated_ms(torch, lambda k: glass.bdmv_batched(y, S, v, w.ss, w.kp))
     out = {
         "workload": w.name, "kind": "bdmv", "kernel": KERNEL_OF["bdmv1"], "dtype": "float32",
         "state_size": w.ss, "knot_points": w.kp, "n_problems": w.n_problems,
         "gb_per_s": nbytes / (wall / steps) / 1e9, "ms_per_step": wall * 1e3 / steps,
-        "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
+        "kernel_ms_avg": avg_ms,
         "kernel_ms_isolated": iso,
         "roofline": roofline(nbytes, avg_ms, traffic.get("bdmv1")),
     }
@@ -608,14 +618,13 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
     torch.cuda.synchronize()
     tm = Timer(torch, steps)
     t0 = time.perf_counter()
+    tm.start()
     for k in range(steps):
-        tm.ev[k][0].record()
         glass.bdsv_batched(x, S, b, w.ss, w.kp, status, workspace=ws)
-        tm.ev[k][1].record()
+    tm.stop()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = tm.launch_ms()
-    avg_ms = float(np.mean(launch_ms))
+    avg_ms = tm.avg_ms()
     iso = isolated_ms(torch, lambda k: glass.bdsv_batched(x, S, b, w.ss, w.kp, status,
                                                          workspace=ws))
     es = np.dtype(w.dtype).itemsize
@@ -627,7 +636,7 @@ def bench_bdsv(torch, glass, key, steps, warmup, cpu_budget, with_cpu, traffic):
         "workload": "bdsv_ss14_kp32_b4096_f32", "kind": "bdsv", "kernel": KERNEL_OF[key],
         "dtype": np.dtype(w.dtype).name, "state_size": w.ss, "knot_points": w.kp,
         "n_problems": B, "solves_per_s": B * steps / wall, "ms_per_step": wall * 1e3 / steps,
-        "kernel_ms_avg": avg_ms, "kernel_ms_min": float(np.min(launch_ms)),
+        "kernel_ms_avg": avg_ms,
         "kernel_ms_isolated": iso,
         "not_spd": int((status.cpu().numpy() != 0).sum()),
         "roofline": roofline_alu(B * algorithmic_flops_bdsv(w), nbytes, avg_ms, traffic.get(key),
