@@ -131,7 +131,8 @@ def workload_of(key):
 
 def code_without_comments(text: str) -> str:
     """C/C++ source with // and /* */ comments removed (string and character
-    literals kept as they are), so that edits of comments alone do not
+    literals kept as they are) and blank lines and trailing blanks dropped,
+    so that edits of comments alone, however many lines they take, do not
     change the hash below."""
     out, i, n = [], 0, len(text)
     while i < n:
@@ -152,7 +153,7 @@ def code_without_comments(text: str) -> str:
         else:
             out.append(c)
             i += 1
-    return "".join(out)
+    return "\n".join(line.rstrip() for line in "".join(out).splitlines() if line.strip())
 
 
 def kernel_source_hash() -> str:

@@ -134,4 +134,7 @@ def test_code_without_comments():
     assert got.replace(" ", "").replace("\n", "") == 'inta=1;constchar*s="//notacomment";charc=\'/\';x'
     # comments alone do not change the code text; code does
     assert bench.code_without_comments("x = 1; // a\n") == bench.code_without_comments("x = 1; // b\n")
+    # a comment that takes more lines does not change it either
+    assert (bench.code_without_comments("x = 1;\n// a\ny = 2;\n") ==
+            bench.code_without_comments("x = 1;\n// a\n// b\n\ny = 2;   \n"))
     assert bench.code_without_comments("x = 1;\n") != bench.code_without_comments("x = 2;\n")
