@@ -454,6 +454,48 @@ def test_pcg_pinv_packed_diagonal_blocks_workloads(gpu, monkeypatch):
             np.testing.assert_array_equal(u, v)
 
 
+def test_resident_random_shapes_match_streamed(gpu, monkeypatch):
+    """Seeded random shapes in the resident placements, whose p and r blocks
+    sit in LDS padded to whole 16-byte vectors (ss=6 in blocks of 8, ss=14
+    in blocks of 16) and whose dots load the chunk slots in one round trip:
+    kp from 1 up to the placement's limit (ragged last chunks, 1 to 16
+    waves), both preconditioners, zero and random x0, one and two rows per
+    lane.  Bit for bit the streamed placement (blocks of ss, slot-by-slot
+    dot), and the oracle bar on the first cases."""
+    rng = np.random.default_rng(20261204)
+    shapes = [(6, 170), (14, 73)]
+    # the smallest systems would go to the several-per-wave placement
+    monkeypatch.setenv("GLASS_AMD_PCG_MULTI", "0")
+    for case in range(16):
+        ss, kmax = shapes[case % 2]
+        kp = int(rng.integers(1, kmax + 1))
+        B = int(rng.integers(1, 70))
+        rpt = "2" if case % 4 == 2 else None
+        monkeypatch.delenv("GLASS_AMD_PCG_STREAMED", raising=False)
+        if rpt:
+            monkeypatch.setenv("GLASS_AMD_PCG_RES_RPT", rpt)
+        else:
+            monkeypatch.delenv("GLASS_AMD_PCG_RES_RPT", raising=False)
+        assert gpu.pcg_batched_placement(ss, kp, torch.float32) == gpu.PLACEMENT_RESIDENT, (ss, kp)
+        r2 = np.random.default_rng(int(rng.integers(0, 1 << 30)))
+        S, D = workloads.random_spd_strips(r2, B, ss, kp, 0.2)
+        P = workloads.block_tridiagonal_pinv(S, D, np.float32) if case % 3 == 1 else \
+            workloads.block_jacobi_pinv(D, np.float32)
+        inp = {"S": S.astype(np.float32), "Pinv": P,
+               "b": r2.standard_normal((B, kp * ss)).astype(np.float32),
+               "x0": (r2.standard_normal((B, kp * ss)) if case % 4 == 3
+                      else np.zeros((B, kp * ss))).astype(np.float32)}
+        say("resident random shape %d: ss=%d kp=%d B=%d rows/lane=%s" % (case, ss, kp, B, rpt or "1"))
+        got = pcg_gpu(gpu, inp, ss, kp, 300, 1e-6, 0.0)
+        monkeypatch.delenv("GLASS_AMD_PCG_RES_RPT", raising=False)
+        monkeypatch.setenv("GLASS_AMD_PCG_STREAMED", "1")
+        ref = pcg_gpu(gpu, inp, ss, kp, 300, 1e-6, 0.0)
+        for u, v in zip(got, ref):
+            np.testing.assert_array_equal(u, v)
+        if case < 4:
+            assert_pcg_parity(inp, ss, kp, 300, 1e-6, 0.0, got, np.float32)
+
+
 @pytest.mark.parametrize("rpt", ["2", "3", "4"])
 def test_pcg_resident_rows_per_lane_bit_identical(gpu, monkeypatch, rpt):
     """Resident rows at 2, 3 and 4 rows per lane (GLASS_AMD_PCG_RES_RPT; for
