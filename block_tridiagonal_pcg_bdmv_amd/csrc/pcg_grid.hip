@@ -311,12 +311,11 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
   }
   __syncthreads();
   if (wave == 0) {
+    // The workgroup's partials, its waves' sums added in wave order (all
+    // slots in one LDS round trip).
     T part[NV];
 #pragma unroll
-    for (int q = 0; q < NV; ++q) {
-      part[q] = wsl[q * NW];
-      for (int w = 1; w < NW; ++w) part[q] = part[q] + wsl[q * NW + w];
-    }
+    for (int q = 0; q < NV; ++q) part[q] = sum_slots_in_order(wsl + q * NW, NW);
     u64* slots = xc.part + (size_t)(bar & 1u) * xc.G * NV * WD;
     const size_t epar = (bar & 1u) ? xc.edge_parity : 0;
     const u64* left = xc.left ? xc.left + epar : nullptr;
