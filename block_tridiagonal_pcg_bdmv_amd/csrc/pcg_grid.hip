@@ -443,6 +443,10 @@ pcg_grid_kernel(GridArgs<T> a) {
   const bool own = valid && br >= A && br < B;
   const long long grow = (long long)br * ss + i;
   const int wstart = (e < next ? e / ss : 0) * ss;  // window start in p_loc/r_loc
+  // A whole number of 16-byte vectors per block: say so, so the window reads
+  // can be 16-byte LDS loads.
+  if constexpr (SS > 0 && (SS * sizeof(T)) % 16 == 0)
+    __builtin_assume((wstart & (int)(16 / sizeof(T) - 1)) == 0);
 
   // z of a block-row outside [A, B) (A-2, A-1, B or B+1), as received from
   // its owner in the last r^T z dot (0 off the chain).
@@ -501,6 +505,9 @@ pcg_grid_kernel(GridArgs<T> a) {
     T acc = T(0);
     const T* __restrict__ w = vloc + wstart;
     if constexpr (RES) {
+      // Blocks of whole 16-byte vectors start every window 16-byte aligned
+      // (the vectors are (nb + 4) blocks each from an aligned base), so
+      // the window is read with 16-byte LDS loads.
 #pragma unroll
       for (int c = 0; c < WC; ++c) acc = fma(mreg[c], w[c], acc);
     } else {
@@ -650,6 +657,8 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
   const bool own = valid && br >= A && br < B;
   const long long grow = (long long)br * ss + i;
   const int wstart = (e < next ? e / ss : 0) * ss;
+  if constexpr (SS > 0 && (SS * sizeof(T)) % 16 == 0)
+    __builtin_assume((wstart & (int)(16 / sizeof(T) - 1)) == 0);
 
   auto ghost = [&](int gbr, int gi) -> T {
     return gbr < A ? ghost_lds[(gbr - (A - 2)) * ss + gi] : ghost_lds[2 * ss + (gbr - B) * ss + gi];
@@ -710,6 +719,9 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
     T acc = T(0);
     const T* __restrict__ w = vloc + wstart;
     if constexpr (RES) {
+      // Blocks of whole 16-byte vectors start every window 16-byte aligned
+      // (the vectors are (nb + 4) blocks each from an aligned base), so
+      // the window is read with 16-byte LDS loads.
 #pragma unroll
       for (int c = 0; c < WC; ++c) acc = fma(mreg[c], w[c], acc);
     } else {
