@@ -254,6 +254,10 @@ pcg_batched_kernel(PcgArgs<T> a) {
     const int br = valid[k] ? row[k] / ss : 0;
     wstart[k] = br * ssp;                         // window start in a padded vector
     vix[k] = (br + 1) * ssp + (row[k] - br * ss);  // the row's own entry
+    // Blocks of whole 16-byte vectors: every window starts 16-byte aligned
+    // (said here because the compiler rewrites br * ssp as row - row % ss).
+    if constexpr (SS > 0 && (SSP * sizeof(T)) % 16 == 0)
+      __builtin_assume((wstart[k] & (int)(16 / sizeof(T) - 1)) == 0);
   }
   // Window entry c (0 <= c < 3*ss) of a padded vector window w: block c / ss,
   // entry c % ss.  The window start is 16-byte aligned.
