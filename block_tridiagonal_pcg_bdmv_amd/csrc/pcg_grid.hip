@@ -505,9 +505,9 @@ pcg_grid_kernel(GridArgs<T> a) {
     T acc = T(0);
     const T* __restrict__ w = vloc + wstart;
     if constexpr (RES) {
-      // Blocks of whole 16-byte vectors start every window 16-byte aligned
-      // (the vectors are (nb + 4) blocks each from an aligned base), so
-      // the window is read with 16-byte LDS loads.
+      // Where a block is a whole number of 16-byte vectors (see wstart),
+      // every window starts 16-byte aligned (each vector is nb_max + 4
+      // blocks from an aligned base) and is read with 16-byte LDS loads.
 #pragma unroll
       for (int c = 0; c < WC; ++c) acc = fma(mreg[c], w[c], acc);
     } else {
@@ -719,9 +719,9 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
     T acc = T(0);
     const T* __restrict__ w = vloc + wstart;
     if constexpr (RES) {
-      // Blocks of whole 16-byte vectors start every window 16-byte aligned
-      // (the vectors are (nb + 4) blocks each from an aligned base), so
-      // the window is read with 16-byte LDS loads.
+      // Where a block is a whole number of 16-byte vectors (see wstart),
+      // every window starts 16-byte aligned (each vector is nb_max + 4
+      // blocks from an aligned base) and is read with 16-byte LDS loads.
 #pragma unroll
       for (int c = 0; c < WC; ++c) acc = fma(mreg[c], w[c], acc);
     } else {
