@@ -42,8 +42,9 @@ def frac_array(vals):
 
 @pytest.fixture(scope="session")
 def gpu():
-    """The HIP library on cuda:0.  Skips where there is no GPU; on a GPU machine a
-    missing or unloadable library is an error, never a silent fallback."""
+    """The HIP library on cuda:0.  Skips where there is no GPU; where there is
+    one, a missing or unloadable library is an error, never a silent
+    fallback."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU in this environment")
