@@ -51,11 +51,13 @@ def test_grid_full_chain_fp64(gpu, variant):
 @pytest.mark.parametrize("ss,kp,dtype", [(12, 64, np.float64), (6, 300, np.float32),
                                          (14, 97, np.float32), (21, 40, np.float32),
                                          (5, 33, np.float64), (3, 4, np.float64),
-                                         (12, 5000, np.float32)])
+                                         (12, 5000, np.float32), (6, 300, np.float64),
+                                         (14, 97, np.float64)])
 def test_grid_matches_oracle_and_batched(gpu, ss, kp, dtype, variant):
     """Specialised and runtime state sizes, partitions of uneven length, the
     minimum chain (kp = 4).  Also cross-checked with the batched solve of the
-    same single problem."""
+    same single problem.  fp64 at ss = 6, 12, 14 and fp32 at ss = 12 have
+    blocks of whole 16-byte vectors, read with 16-byte LDS loads."""
     rng = np.random.default_rng(ss * 7 + kp)
     S, D = workloads.random_spd_strips(rng, 1, ss, kp, 0.1, dtype)
     inp = {"S": S, "Pinv": workloads.block_jacobi_pinv(D, dtype),
