@@ -16,9 +16,9 @@
 //   x, r, p (and the transient z, S p) live in registers.
 // * only p and r must be seen by other lanes (the 3*ss matvec window), so
 //   they are the two padded vectors kept in LDS; the page's other work
-//   vectors stay in registers.  Where both matrices stay on chip, each block
-//   of ss entries takes a whole number of 16-byte vectors in LDS, so a
-//   window is read with 16-byte loads.
+//   vectors stay in registers.  Where S (or both matrices) stays on chip,
+//   each block of ss entries takes a whole number of 16-byte vectors in LDS,
+//   so a window is read with 16-byte loads.
 // * dots: each 64-row chunk's products -> wave64 DPP tree -> one LDS slot per
 //   chunk -> every thread adds the slots in chunk order.  alpha, beta and the
 //   stopping decision are therefore computed identically (same bits) by every
@@ -124,11 +124,10 @@ struct PcgArgs {
 // Block stride of the padded vectors in LDS: ss rounded up to whole 16-byte
 // vectors, so every window starts 16-byte aligned and its reads can be
 // 16-byte LDS loads (twice the delivery rate of 4- and 8-byte ones).  The
-// tail of each block is never read.  The placements that hold both
-// matrices on chip (resident, and S resident with Pinv's D blocks in LDS)
-// use it; the streamed ones keep blocks of ss (they measured no faster
-// padded, and the plain streamed placement, the fallback for the largest
-// problems, needs the least LDS).
+// tail of each block is never read.  The placements that hold S (or both
+// matrices) on chip use it; the streamed ones keep blocks of ss (they
+// measured no faster padded, and the plain streamed placement, the
+// fallback for the largest problems, needs the least LDS).
 template <typename T>
 __host__ __device__ constexpr int vec_block(int ss, bool padded = true) {
   return padded ? (ss + (int)(16 / sizeof(T)) - 1) / (int)(16 / sizeof(T)) * (int)(16 / sizeof(T))
@@ -195,7 +194,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
   const int n = kp * ss;
   // p and r in LDS as kp + 2 blocks of ssp elements (a zero block at each
   // end, ss entries used per block).
-  constexpr bool PADV = RES || HYBP;
+  constexpr bool PADV = RES || HYBP || HYBS;
   constexpr int SSP = SS > 0 ? vec_block<T>(SS, PADV) : 0;
   const int ssp = SS > 0 ? SSP : vec_block<T>(ss, PADV);
   const int pad_len = (kp + 2) * ssp;
@@ -378,11 +377,16 @@ pcg_batched_kernel(PcgArgs<T> a) {
       const int nbytes = has ? min(64, n - r0) * W * (int)sizeof(T) + shift : 0;
       const __amdgpu_buffer_rsrc_t rs = make_rsrc(has ? src - shift : src, nbytes);
       unsigned char* st = reinterpret_cast<unsigned char*>(dst);
+      // The lane's byte offset, made opaque here so that the offsets of the
+      // NV loads are formed at each call instead of being kept in NV
+      // registers for the whole solve.
+      int vbase = lane * 16;
+      asm volatile("" : "+v"(vbase));
 #pragma unroll
       for (int u = 0; u < NV; ++u)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
-            (lane + u * kWave) * 16, 0, 0, 0);
+            vbase + u * kWave * 16, 0, 0, 0);
     }
   };
   auto dma_chunk_to = [&](int k, T* dst) { dma_rows_to(gP, k, dst); };
@@ -632,7 +636,7 @@ pcg_batched_kernel(PcgArgs<T> a) {
     // lanes in order.  The others keep the slot-by-slot loop, which measured
     // faster there: the S-resident kernels hold 3*ss S values per lane, and
     // the lane form's extra live values left their stage matvec fewer
-    // registers for LDS reads in flight (4-9 % slower).  Both add the same
+    // registers for LDS reads in flight (1-4 % slower).  Both add the same
     // values in the same order, so the bits agree.
     if constexpr (RES) {
       return sum_slots_in_order(slots, nchunks);
@@ -964,7 +968,7 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       // hold a Pinv chunk; take it when that pins more chunks in all (LDS
       // slots below plus those registers).
       auto pins = [&](int nw) {
-        const size_t used = lds_bytes<T>(ss, kp, nw, prefetch_stage_elems<T>(ss), false);
+        const size_t used = lds_bytes<T>(ss, kp, nw, prefetch_stage_elems<T>(ss), true);
         if (used > lds_max) return -1;
         const size_t slot = (size_t)prefetch_stage_elems<T>(ss) * sizeof(T);
         int have_last = 0, reg = 0;
@@ -982,7 +986,7 @@ bool make_plan(int ss, int kp, bool res_available, bool prefetch, bool pinv_diag
       const size_t dbytes = ((size_t)n * ss * sizeof(T) + 1023) & ~(size_t)1023;
       const int stage = pinv_diag ? 0 : prefetch_stage_elems<T>(ss);
       const size_t lds = pinv_diag ? lds_bytes<T>(ss, kp, NW, 0) + dbytes
-                                   : lds_bytes<T>(ss, kp, NW, stage, false);
+                                   : lds_bytes<T>(ss, kp, NW, stage, true);
       if (lds > lds_max) continue;
       Plan p;
       p.NW = NW;
