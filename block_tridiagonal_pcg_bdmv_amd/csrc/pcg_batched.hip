@@ -221,6 +221,9 @@ pcg_batched_kernel(PcgArgs<T> a) {
   T* slotA = r_pad + pad_len;  // [nchunks] per-chunk dot partials
   T* slotB = slotA + nchunks;
   const size_t head = ((size_t)(2 * pad_len + 2 * nchunks) * sizeof(T) + 15) & ~(size_t)15;
+  // Every stage holds a whole number of 64-row blocks (the host sizes it as
+  // 64 rows of a fixed width), so every stage starts as aligned as the head.
+  __builtin_assume(a.stage_elems % 64 == 0);
   T* stage = reinterpret_cast<T*>(smem_raw + head) + (size_t)wave * a.stage_elems;
   // HYBS: a wave below a.npin holds its last chunk (k = RPT-1) of Pinv in a
   // pinned slot after the NW stages, loaded once; only its other chunks
