@@ -31,6 +31,12 @@
 //   stopping decisions.  One store and about one load round trip per dot,
 //   against the five dependent round trips of a counter-based two-level
 //   barrier (measured 2.2 us against 4.4 us per barrier at 256 workgroups).
+// * Partial copies.  Each partial is stored into kPartCopies copies of the
+//   partial array, and a workgroup polls copy blockIdx % kPartCopies: the
+//   workgroups of one XCD share a copy, so each line is polled by G/8
+//   workgroups instead of G.  The same values are added in the same order
+//   whichever copy is read.  Measured at 256 workgroups: fp64 chain 81-82 ->
+//   73 us, fp32 47-48 -> 43.5 us (16 or more copies were slower than 8).
 // * Reuse rules.  Partials and edge values alternate between two buffers by
 //   barrier parity: a workgroup writes the buffers of barrier n+2 only after
 //   it has seen every partial of barrier n+1, and each of those was stored
@@ -86,7 +92,7 @@ struct GridArgs {
   T rel_tol;
   T abs_tol;
   unsigned int* flags;       // [0]: a poll timed out (zeroed before the launch)
-  unsigned long long* part;  // [2][G][kDotValues][kTagWords<T>] tagged partials, by barrier parity
+  unsigned long long* part;  // [kPartCopies][2][G][kDotValues][kTagWords<T>] tagged partials, by barrier parity
   unsigned long long* edges; // [2][G][4*ss][kTagWords<T>] tagged edge values (block-rows
                              // A, A+1, B-2, B-1), by barrier parity
   int G;
@@ -108,6 +114,10 @@ constexpr int kTagWords = (int)sizeof(T) / 4;
 // reduces two).
 constexpr int kDotValues = 2;
 
+// Copies of the partial array (see "Partial copies" at the top of the file).
+constexpr int kPartCopies = 8;
+static_assert(kPartCopies <= 64, "one wave stores every copy");
+
 struct WorkspaceLayout {
   size_t flags, part, edges, total;
 };
@@ -120,7 +130,7 @@ WorkspaceLayout layout_for(size_t G, int ss, size_t elem) {
   WorkspaceLayout w;
   w.flags = 0;
   w.part = 256;
-  w.edges = w.part + round256(2 * G * kDotValues * words * sizeof(u64));
+  w.edges = w.part + round256((size_t)kPartCopies * 2 * G * kDotValues * words * sizeof(u64));
   w.total = w.edges + round256(2 * G * 4 * (size_t)ss * words * sizeof(u64));
   return w;
 }
@@ -275,7 +285,7 @@ constexpr int kSumBatch = 4;
 // Where a workgroup's exchange buffers are (edge pointers for parity 0; the
 // parity-1 buffers follow at edge_parity words).
 struct GridXchg {
-  u64* part;         // [2][G][kDotValues][kTagWords]
+  u64* part;         // [kPartCopies][2][G][kDotValues][kTagWords]
   u64* my_edges;     // this workgroup's [4*ss][kTagWords]
   const u64* left;   // left neighbour's edges, or null (first partition)
   const u64* right;  // right neighbour's edges, or null (last partition)
@@ -284,6 +294,7 @@ struct GridXchg {
   unsigned spin_limit;
   unsigned tag_base;
   int G, g;
+  int copy;  // the partial copy this workgroup polls
 };
 
 // Grid-wide sums of NV per-thread values v[0..NV); every thread of every
@@ -316,17 +327,22 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
     T part[NV];
 #pragma unroll
     for (int q = 0; q < NV; ++q) part[q] = sum_slots_in_order(wsl + q * NW, NW);
-    u64* slots = xc.part + (size_t)(bar & 1u) * xc.G * NV * WD;
+    // Partial array of copy c for this barrier's parity.
+    auto slots_of = [&](int c) {
+      return xc.part + ((size_t)c * 2 + (bar & 1u)) * xc.G * NV * WD;
+    };
     const size_t epar = (bar & 1u) ? xc.edge_parity : 0;
     const u64* left = xc.left ? xc.left + epar : nullptr;
     const u64* right = xc.right ? xc.right + epar : nullptr;
     if (edge_lds)
       for (int j = lane; j < n_edge; j += kWave)
         put_tagged(xc.my_edges + epar + j * WD, edge_lds[j], tag);
-    if (lane == 0) {
+    if (lane < kPartCopies) {  // lane c stores into copy c
+      u64* mine = slots_of(lane) + xc.g * NV * WD;
 #pragma unroll
-      for (int q = 0; q < NV; ++q) put_tagged(slots + (xc.g * NV + q) * WD, part[q], tag);
+      for (int q = 0; q < NV; ++q) put_tagged(mine + q * WD, part[q], tag);
     }
+    const u64* slots = slots_of(xc.copy);
 
     // Neighbour edges: loaded now, checked after the partials, so both
     // share one round trip when the neighbours are on time.
@@ -473,6 +489,7 @@ pcg_grid_kernel(GridArgs<T> a) {
   xc.flags = a.flags;
   xc.G = G;
   xc.g = g;
+  xc.copy = bid % kPartCopies;
   unsigned int barriers = 0;
   auto dot = [&](T v, bool with_edges) {
     ++barriers;
@@ -688,6 +705,7 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
   xc.flags = a.flags;
   xc.G = G;
   xc.g = g;
+  xc.copy = bid % kPartCopies;
   unsigned int barriers = 0;
   auto dot2 = [&](T v0, T v1, T (&out)[2]) {
     ++barriers;
@@ -841,7 +859,7 @@ int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
       n2 = 0;
     } else {  // the words this grid reads: both partial buffers and the edges
       w1 = a.part;
-      n1 = 2LL * a.G * kDotValues * kTagWords<T>;
+      n1 = (long long)kPartCopies * 2 * a.G * kDotValues * kTagWords<T>;
       n2 = 2LL * a.G * 4 * a.ss * kTagWords<T>;
     }
     const long long most = std::max(n1, n2);
