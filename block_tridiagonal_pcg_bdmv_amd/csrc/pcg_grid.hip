@@ -37,6 +37,9 @@
 //   workgroups instead of G.  The same values are added in the same order
 //   whichever copy is read.  Measured at 256 workgroups: fp64 chain 81-82 ->
 //   73 us, fp32 47-48 -> 43.5 us (16 or more copies were slower than 8).
+//   Each partial also has a slot of its own of kSlotBytes, so two
+//   workgroups at most store into one 128-byte line (fp64 chain a further
+//   72.7 -> 68.5 us).
 // * Reuse rules.  Partials and edge values alternate between two buffers by
 //   barrier parity: a workgroup writes the buffers of barrier n+2 only after
 //   it has seen every partial of barrier n+1, and each of those was stored
@@ -92,7 +95,7 @@ struct GridArgs {
   T rel_tol;
   T abs_tol;
   unsigned int* flags;       // [0]: a poll timed out (zeroed before the launch)
-  unsigned long long* part;  // [kPartCopies][2][G][kDotValues][kTagWords<T>] tagged partials, by barrier parity
+  unsigned long long* part;  // [kPartCopies][2][G][kSlotWords] tagged partials, by barrier parity
   unsigned long long* edges; // [2][G][4*ss][kTagWords<T>] tagged edge values (block-rows
                              // A, A+1, B-2, B-1), by barrier parity
   int G;
@@ -117,6 +120,10 @@ constexpr int kDotValues = 2;
 // Copies of the partial array (see "Partial copies" at the top of the file).
 constexpr int kPartCopies = 8;
 static_assert(kPartCopies <= 64, "one wave stores every copy");
+// Bytes of one workgroup's slot in a partial array (its NV values, padded).
+constexpr int kSlotBytes = 64;
+static_assert(kDotValues * 2 * 8 <= kSlotBytes, "a slot holds every value of a dot");
+constexpr int kSlotWords = kSlotBytes / 8;
 
 struct WorkspaceLayout {
   size_t flags, part, edges, total;
@@ -130,7 +137,7 @@ WorkspaceLayout layout_for(size_t G, int ss, size_t elem) {
   WorkspaceLayout w;
   w.flags = 0;
   w.part = 256;
-  w.edges = w.part + round256((size_t)kPartCopies * 2 * G * kDotValues * words * sizeof(u64));
+  w.edges = w.part + round256((size_t)kPartCopies * 2 * G * kSlotBytes);
   w.total = w.edges + round256(2 * G * 4 * (size_t)ss * words * sizeof(u64));
   return w;
 }
@@ -285,7 +292,7 @@ constexpr int kSumBatch = 4;
 // Where a workgroup's exchange buffers are (edge pointers for parity 0; the
 // parity-1 buffers follow at edge_parity words).
 struct GridXchg {
-  u64* part;         // [kPartCopies][2][G][kDotValues][kTagWords]
+  u64* part;         // [kPartCopies][2][G][kSlotWords]
   u64* my_edges;     // this workgroup's [4*ss][kTagWords]
   const u64* left;   // left neighbour's edges, or null (first partition)
   const u64* right;  // right neighbour's edges, or null (last partition)
@@ -329,7 +336,7 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
     for (int q = 0; q < NV; ++q) part[q] = sum_slots_in_order(wsl + q * NW, NW);
     // Partial array of copy c for this barrier's parity.
     auto slots_of = [&](int c) {
-      return xc.part + ((size_t)c * 2 + (bar & 1u)) * xc.G * NV * WD;
+      return xc.part + ((size_t)c * 2 + (bar & 1u)) * xc.G * kSlotWords;
     };
     const size_t epar = (bar & 1u) ? xc.edge_parity : 0;
     const u64* left = xc.left ? xc.left + epar : nullptr;
@@ -338,7 +345,7 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
       for (int j = lane; j < n_edge; j += kWave)
         put_tagged(xc.my_edges + epar + j * WD, edge_lds[j], tag);
     if (lane < kPartCopies) {  // lane c stores into copy c
-      u64* mine = slots_of(lane) + xc.g * NV * WD;
+      u64* mine = slots_of(lane) + xc.g * kSlotWords;
 #pragma unroll
       for (int q = 0; q < NV; ++q) put_tagged(mine + q * WD, part[q], tag);
     }
@@ -377,7 +384,7 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
 #pragma unroll
           for (int q = 0; q < NV; ++q) {
             val[k][q] = T(0);
-            if (j < xc.G) ok &= get_tagged(slots + (j * NV + q) * WD, tag, val[k][q]);
+            if (j < xc.G) ok &= get_tagged(slots + j * kSlotWords + q * WD, tag, val[k][q]);
           }
         }
         if (__all(ok)) break;
@@ -859,7 +866,7 @@ int launch_grid_typed(GridArgs<T> a, int NT, size_t lds, const DeviceInfo& dev,
       n2 = 0;
     } else {  // the words this grid reads: both partial buffers and the edges
       w1 = a.part;
-      n1 = (long long)kPartCopies * 2 * a.G * kDotValues * kTagWords<T>;
+      n1 = (long long)kPartCopies * 2 * a.G * kSlotWords;
       n2 = 2LL * a.G * 4 * a.ss * kTagWords<T>;
     }
     const long long most = std::max(n1, n2);

@@ -291,9 +291,9 @@ int glass_pcg_grid_ex(void* x, const void* S, const void* Pinv, const void* b,
  * clearing kernel is launched.  The exchange area lives in a static device array of
  * GLASS_PCG_GRID_NOALLOC_SCRATCH_BYTES bytes that the library holds on each
  * device it runs on until the process ends; the call itself allocates and
- * frees nothing.  It needs 256 + 8*2*G*2*w*8 + 2*G*4*state_size*w*8 bytes
+ * frees nothing.  It needs 256 + 8*2*G*64 + 2*G*4*state_size*w*8 bytes
  * (G = workgroups of the grid, usually one per compute unit; w = 1 for
- * GLASS_F32, 2 for GLASS_F64), about 0.5 MB for a 256-workgroup fp64 grid
+ * GLASS_F32, 2 for GLASS_F64), about 0.66 MB for a 256-workgroup fp64 grid
  * at state_size 12; a shape that needs more returns GLASS_EUNSUPPORTED with
  * nothing launched.  Every call on one device shares that device's array:
  * calls ordered on one stream are safe, calls that overlap in time (other

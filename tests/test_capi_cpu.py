@@ -90,9 +90,9 @@ def test_pcg_argument_errors(lib):
 
 def test_grid_argument_errors_and_workspace_size(lib):
     ws = lib.glass_pcg_grid_workspace_bytes(12, 8192, 1)
-    # Flag block, 8 copies of the tagged partials [2][G][2 values][2 words],
+    # Flag block, 8 copies of the tagged partials [2][G] in 64-byte slots,
     # tagged edges [2][G][4 ss][2 words]; G = kp/2 capped at 2048.
-    assert ws == 256 + 8 * 2 * 2048 * 2 * 2 * 8 + 2 * 2048 * 4 * 12 * 2 * 8
+    assert ws == 256 + 8 * 2 * 2048 * 64 + 2 * 2048 * 4 * 12 * 2 * 8
     assert lib.glass_pcg_grid_workspace_bytes(12, 3, 1) == 0
     assert lib.glass_pcg_grid_workspace_bytes(0, 100, 1) == 0
 
