@@ -40,6 +40,10 @@
 //   Each partial also has a slot of its own of kSlotBytes, so two
 //   workgroups at most store into one 128-byte line (fp64 chain a further
 //   72.7 -> 68.5 us).
+// * Staggered polls.  Wave 0 keeps two poll rounds of the partials in
+//   flight, half a round trip apart, and checks them alternately (where the
+//   second set of words fits in registers): fp32 chain 42.7 -> 38.7 us,
+//   fp64 73.8 -> 72.0 us.
 // * Reuse rules.  Partials and edge values alternate between two buffers by
 //   barrier parity: a workgroup writes the buffers of barrier n+2 only after
 //   it has seen every partial of barrier n+1, and each of those was stored
@@ -288,6 +292,18 @@ __device__ __forceinline__ bool keep_polling(unsigned& spins, unsigned int* flag
 
 // Partials one lane loads per poll round.
 constexpr int kSumBatch = 4;
+// Sleep units (64 clocks) between the two poll rounds of a grid dot.
+constexpr int kPollStagger = 20;
+
+// The value of kTagWords<T> exchange words read raw (see put_tagged).
+template <typename T>
+__device__ __forceinline__ T tagged_value(const u64 (&w)[kTagWords<T>]) {
+  if constexpr (sizeof(T) == 4) {
+    return __uint_as_float((unsigned)w[0]);
+  } else {
+    return __longlong_as_double((long long)((w[1] << 32) | (w[0] & 0xffffffffull)));
+  }
+}
 
 // Where a workgroup's exchange buffers are (edge pointers for parity 0; the
 // parity-1 buffers follow at edge_parity words).
@@ -312,7 +328,7 @@ struct GridXchg {
 // block-rows A-2, A-1 and [2ss, 4ss) of B, B+1 (zero off the chain).  GP
 // bounds the ghost values per lane (GP*64 >= n_edge).  Contains two
 // __syncthreads().
-template <typename T, int GP, int NV>
+template <typename T, int GP, int NV, bool STAGGER>
 __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const T* edge_lds,
                                            T* ghost_lds, int n_edge, const GridXchg& xc,
                                            unsigned bar, T* wsl, T* bcast, int NW, int wave,
@@ -373,6 +389,63 @@ __device__ __forceinline__ void grid_dot_n(const T (&v)[NV], T (&out)[NV], const
     T sum[NV];
 #pragma unroll
     for (int q = 0; q < NV; ++q) sum[q] = T(0);
+    if constexpr (STAGGER) {
+      // Two poll rounds in flight, started kPollStagger sleep units (64
+      // clocks each) apart and re-issued alternately: a partial that lands
+      // just after one round's load is seen by the other round about half a
+      // round trip later instead of a whole one.  The same words are added
+      // in the same order.  The caller picks it where the second set of
+      // words does not make its kernel spill.
+      for (int base = 0; base < xc.G; base += kSumBatch * kWave) {
+        u64 wa[kSumBatch][NV][WD], wb[kSumBatch][NV][WD];
+        auto issue = [&](u64 (&w)[kSumBatch][NV][WD]) {
+#pragma unroll
+          for (int k = 0; k < kSumBatch; ++k) {
+            const int j = base + lane + k * kWave;
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+#pragma unroll
+              for (int d = 0; d < WD; ++d)  // entries past G read as current
+                w[k][q][d] = j < xc.G ? load_word(slots + j * kSlotWords + q * WD + d)
+                                      : ((u64)tag << 32);
+          }
+        };
+        auto ready = [&](const u64 (&w)[kSumBatch][NV][WD]) {
+          bool ok = true;
+#pragma unroll
+          for (int k = 0; k < kSumBatch; ++k)
+#pragma unroll
+            for (int q = 0; q < NV; ++q)
+#pragma unroll
+              for (int d = 0; d < WD; ++d) ok &= (unsigned)(w[k][q][d] >> 32) == tag;
+          return __all(ok);
+        };
+        auto add = [&](const u64 (&w)[kSumBatch][NV][WD]) {
+#pragma unroll
+          for (int k = 0; k < kSumBatch; ++k)
+            if (base + lane + k * kWave < xc.G) {
+#pragma unroll
+              for (int q = 0; q < NV; ++q) sum[q] = sum[q] + tagged_value<T>(w[k][q]);
+            }
+        };
+        unsigned spins = 0;
+        issue(wa);
+        __builtin_amdgcn_s_sleep(kPollStagger);
+        issue(wb);
+        for (;;) {
+          if (ready(wa) || !keep_polling(spins, xc.flags, lane, xc.spin_limit, xc.tag_base)) {
+            add(wa);
+            break;
+          }
+          issue(wa);
+          if (ready(wb) || !keep_polling(spins, xc.flags, lane, xc.spin_limit, xc.tag_base)) {
+            add(wb);
+            break;
+          }
+          issue(wb);
+        }
+      }
+    } else
     for (int base = 0; base < xc.G; base += kSumBatch * kWave) {
       T val[kSumBatch][NV];
       unsigned spins = 0;
@@ -501,8 +574,8 @@ pcg_grid_kernel(GridArgs<T> a) {
   auto dot = [&](T v, bool with_edges) {
     ++barriers;
     T in[1] = {v}, out[1];
-    grid_dot_n<T, GP, 1>(in, out, with_edges ? edge_lds : (const T*)nullptr, ghost_lds, n_edge,
-                         xc, barriers, wsl, bcast, NW, wave, lane);
+    grid_dot_n<T, GP, 1, true>(in, out, with_edges ? edge_lds : (const T*)nullptr, ghost_lds,
+                               n_edge, xc, barriers, wsl, bcast, NW, wave, lane);
     return out[0];
   };
 
@@ -717,8 +790,11 @@ pcg_grid_cg1_kernel(GridArgs<T> a) {
   auto dot2 = [&](T v0, T v1, T (&out)[2]) {
     ++barriers;
     T in[2] = {v0, v1};
-    grid_dot_n<T, GP, 2>(in, out, edge_lds, ghost_lds, n_edge, xc, barriers, wsl, bcast, NW,
-                         wave, lane);
+    // Staggered polls: fp32 up to state size 14 (fp64, and larger states,
+    // would spill the second set of words).
+    constexpr bool kStagger = sizeof(T) == 4 && (SS > 0 && SS <= 14);
+    grid_dot_n<T, GP, 2, kStagger>(in, out, edge_lds, ghost_lds, n_edge, xc, barriers, wsl,
+                                   bcast, NW, wave, lane);
   };
 
   // S and Pinv rows of every valid extended row.
