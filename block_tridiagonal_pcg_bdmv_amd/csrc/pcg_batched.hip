@@ -385,11 +385,22 @@ pcg_batched_kernel(PcgArgs<T> a) {
       // registers for the whole solve.
       int vbase = lane * 16;
       asm volatile("" : "+v"(vbase));
+      // S is read once: in fp64 its loads are non-temporal (cache-policy
+      // bit 1), which measured 414 -> 401 us on the fp64 ss=14 solve; in
+      // fp32 the same slowed the ss=21 solve (440 -> 466 us).
+      if (sizeof(T) == 8 && gM == gS) {
 #pragma unroll
-      for (int u = 0; u < NV; ++u)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
-            vbase + u * kWave * 16, 0, 0, 0);
+        for (int u = 0; u < NV; ++u)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
+              vbase + u * kWave * 16, 0, 0, 2);
+      } else {
+#pragma unroll
+        for (int u = 0; u < NV; ++u)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(st + u * kWave * 16), 16,
+              vbase + u * kWave * 16, 0, 0, 0);
+      }
     }
   };
   auto dma_chunk_to = [&](int k, T* dst) { dma_rows_to(gP, k, dst); };
